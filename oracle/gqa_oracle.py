@@ -1,0 +1,231 @@
+"""fp64 CPU oracle: causal grouped-query attention with RoPE (base 1e6).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import or run this module.  The library never calls it, and it
+shares no code with the GPU path: the only thing both sides use is the seeded
+input generator in ``synthetic/``.
+
+It is the plain definition, written out in float64 with NumPy, in the order
+the pages state it, with no tiling, fusion or reordering.
+
+Sources (web pages on the Qwen2 decoder, cited by title/host and section):
+  [evo]  "从 Qwen 1 到 Qwen 2 架构演进到底改了什么" (nxmr.cn)
+  [ip]   "Qwen2架构解析：GQA与MoE技术在大模型中的创新应用" (intelliparadigm.com)
+  [csdn] Qwen2 technical-report walkthrough (aicoding.csdn.net)
+  [kn]   "Qwen2 / Qwen3 的实测配置差异与三个坑" (docs.keinmal.top)
+
+Readings taken where the pages are silent or disagree:
+  * RoPE rotates dimension j together with dimension j + d/2 ("half-split"
+    pairing); the pages only say "each dimension pair".
+  * The frequency exponent uses the head size d (the rotation happens inside
+    each head's d_k dims, [csdn] §4.1.3 step 3; Q and K share one table,
+    [kn] pitfall 3); [ip] §2.3 writes d_model there, read as a slip.
+  * Masked scores are -inf (exact zero weight) ([csdn] §4.1.3 step 4 allows
+    "-inf or a very large negative number").
+  * Prefill: query i and key j both sit at position (offset + index); key j
+    is visible to query i iff pos(j) <= pos(i).
+  * Decode: the cache holds keys that are already rotated; the new query is
+    rotated at its own position inside; every cached row < kv_len is visible.
+
+Every function here is pinned by tests that do not re-type its formulas:
+closed forms of the rotation, SDPA from PyTorch in fp64, the pages' group
+example, brute-force loops, and the invariants the pages state.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ROPE_THETA = 1.0e6   # Qwen2's RoPE base: [evo] §2.3/§3.2, [csdn] §5.2, [kn] config table
+
+
+# ---------------------------------------------------------------- RoPE ----
+
+def inv_freq(d: int, theta: float = ROPE_THETA) -> np.ndarray:
+    """omega_j = theta^(-2j/d), j = 0 .. d/2-1 ([ip] §2.3 angle m*base^(-2i/d);
+    [csdn] §5.2: the base generates the inverse frequencies)."""
+    if d % 2:
+        raise ValueError("RoPE needs an even head size")
+    j = np.arange(d // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -2.0 * j / d)
+
+
+def rope(x: np.ndarray, positions, theta: float = ROPE_THETA) -> np.ndarray:
+    """Rotate every row of x[..., L, h, d] at its position ([csdn] §3.5.2 and
+    §4.1.3 step 3: rotate Q and K per position and per dimension pair; the
+    shape is unchanged).  ``positions`` has shape [L] (or broadcasts to
+    x.shape[:-2]).  Pair (j, j + d/2) turns by the angle pos * omega_j."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    pos = np.asarray(positions, dtype=np.float64)
+    ang = pos[..., None] * inv_freq(d, theta)          # [..., L, d/2]
+    c = np.cos(ang)[..., None, :]                      # broadcast over heads
+    s = np.sin(ang)[..., None, :]
+    x1 = x[..., :half]
+    x2 = x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# ---------------------------------------------------------- grouping ------
+
+def group_size(h_q: int, h_kv: int) -> int:
+    """g = h_q / h_kv ([csdn] §4.1.2); h_q must be a multiple of h_kv."""
+    if h_kv < 1 or h_q < 1 or h_q % h_kv:
+        raise ValueError(f"h_q={h_q} is not a positive multiple of h_kv={h_kv}")
+    return h_q // h_kv
+
+
+def kv_group(t: int, h_q: int, h_kv: int) -> int:
+    """0-based KV group of query head t: u = floor(t / g), the 0-based form of
+    [csdn] §4.1.2 / [evo] §2.2 u = floor((t-1)/g) + 1."""
+    return t // group_size(h_q, h_kv)
+
+
+# ---------------------------------------------------------- attention -----
+
+def visible(q_pos, k_pos) -> np.ndarray:
+    """Causal mask [Lq, Lk]: key j may be seen by query i iff pos_j <= pos_i
+    ([csdn] §4.1.3 step 4: positions j > i are masked)."""
+    return np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+
+
+def softmax_rows(s: np.ndarray, vis: np.ndarray) -> np.ndarray:
+    """Row softmax of scores with masked entries at -inf (exact zero weight).
+    Subtracts the row max first; every row must see at least one key."""
+    s = np.where(vis, s, -np.inf)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def head_weights(q_rot: np.ndarray, k_rot: np.ndarray, scale: float,
+                 vis: np.ndarray) -> np.ndarray:
+    """A = softmax(Q' K'^T * scale + M) for one query head and its KV group
+    ([csdn] §3.5.2 S_ij = Q'[i].K'[j]/sqrt(d_k); §4.1.3 step 4)."""
+    return softmax_rows((q_rot @ k_rot.T) * scale, vis)
+
+
+def attend(q_rot, k_rot, v, scale, vis) -> np.ndarray:
+    """head = A V ([csdn] §4.1.3 step 4)."""
+    return head_weights(q_rot, k_rot, scale, vis) @ np.asarray(v, np.float64)
+
+
+def prefill(q, k, v, theta: float = ROPE_THETA, scale: float | None = None,
+            causal: bool = True, pos0: int = 0) -> np.ndarray:
+    """Causal GQA prefill.  q [B, L, h_q, d], k/v [B, L, h_kv, d] (pre-RoPE);
+    rows sit at positions pos0 .. pos0+L-1.  Returns O [B, L, h_q, d] fp64
+    (the per-head outputs side by side, i.e. the concat layout of [csdn]
+    §4.1.3 step 5, before W_O).
+
+    Steps as in [csdn] §4.1.3: 3) rotate Q and K; 4) per query head t with
+    its group u: scores, causal mask, softmax, times V^(u)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, L, h_q, d = q.shape
+    h_kv = k.shape[2]
+    group_size(h_q, h_kv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    pos = np.arange(pos0, pos0 + L)
+    qr = rope(q, pos, theta)
+    kr = rope(k, pos, theta)
+    vis = visible(pos, pos) if causal else np.ones((L, L), bool)
+    out = np.empty((B, L, h_q, d), np.float64)
+    for b in range(B):
+        for t in range(h_q):
+            u = kv_group(t, h_q, h_kv)
+            out[b, :, t, :] = attend(qr[b, :, t, :], kr[b, :, u, :],
+                                     v[b, :, u, :], scale, vis)
+    return out
+
+
+def prefill_rows(q, k, v, rows, theta: float = ROPE_THETA,
+                 scale: float | None = None) -> np.ndarray:
+    """The same causal prefill, evaluated one output row at a time for a list
+    of (b, i, t) triples; returns [len(rows), d].  Row i only needs keys
+    0..i, so this serves as the oracle for sampled rows of large inputs."""
+    d = q.shape[-1]
+    h_q, h_kv = q.shape[2], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.empty((len(rows), d), np.float64)
+    for n, (b, i, t) in enumerate(rows):
+        u = kv_group(t, h_q, h_kv)
+        qr = rope(np.asarray(q[b, i:i + 1, t:t + 1, :], np.float64), [i], theta)[:, 0, :]
+        kr = rope(np.asarray(k[b, :i + 1, u:u + 1, :], np.float64),
+                  np.arange(i + 1), theta)[:, 0, :]
+        out[n] = attend(qr, kr, v[b, :i + 1, u, :], scale,
+                        visible([i], np.arange(i + 1)))[0]
+    return out
+
+
+def decode(q, k_cache, v_cache, kv_len: int, q_pos: int,
+           theta: float = ROPE_THETA, scale: float | None = None) -> np.ndarray:
+    """One new query token per sequence.  q [B, h_q, d] (pre-RoPE, rotated
+    here at q_pos); k_cache/v_cache [B, cap, h_kv, d] hold rotated keys and
+    values; rows 0..kv_len-1 are attended ([csdn] §4.1.3: the cache keeps only
+    the h_kv groups' K, V, appended each step).  Returns O [B, h_q, d]."""
+    q = np.asarray(q, np.float64)
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    if not 1 <= kv_len <= k_cache.shape[1]:
+        raise ValueError("kv_len out of range")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qr = rope(q[:, None, :, :], [q_pos], theta)[:, 0]
+    out = np.empty((B, h_q, d), np.float64)
+    vis = np.ones((1, kv_len), bool)   # every cached row precedes the query
+    for b in range(B):
+        kb = np.asarray(k_cache[b, :kv_len], np.float64)
+        vb = np.asarray(v_cache[b, :kv_len], np.float64)
+        for t in range(h_q):
+            u = kv_group(t, h_q, h_kv)
+            out[b, t] = attend(qr[b, t][None, :], kb[:, u, :], vb[:, u, :],
+                               scale, vis)[0]
+    return out
+
+
+# ------------------------------------------------------- brute force ------
+
+def prefill_brute(q, k, v, theta: float = ROPE_THETA, scale: float | None = None,
+                  pos0: int = 0):
+    """Scalar-loop causal GQA prefill for tiny inputs (nested Python lists or
+    arrays).  Written independently of the vectorised functions above: it
+    uses math.cos/sin and plain loops only."""
+    B, L, h_q, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    h_kv = len(k[0][0])
+    g = h_q // h_kv
+    half = d // 2
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    def rot(vec, p):
+        outv = [0.0] * d
+        for j in range(half):
+            a = p * theta ** (-2.0 * j / d)
+            c, s = math.cos(a), math.sin(a)
+            outv[j] = vec[j] * c - vec[j + half] * s
+            outv[j + half] = vec[j + half] * c + vec[j] * s
+        return outv
+
+    out = [[[[0.0] * d for _ in range(h_q)] for _ in range(L)] for _ in range(B)]
+    for b in range(B):
+        for t in range(h_q):
+            u = t // g
+            kr = [rot([float(x) for x in k[b][j][u]], pos0 + j) for j in range(L)]
+            for i in range(L):
+                qi = rot([float(x) for x in q[b][i][t]], pos0 + i)
+                sc = []
+                for j in range(i + 1):
+                    sc.append(sum(qi[e] * kr[j][e] for e in range(d)) * scale)
+                mx = max(sc)
+                w = [math.exp(s - mx) for s in sc]
+                tot = sum(w)
+                for e in range(d):
+                    out[b][i][t][e] = sum(w[j] * float(v[b][j][u][e])
+                                          for j in range(i + 1)) / tot
+    return np.array(out, dtype=np.float64)

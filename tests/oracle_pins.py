@@ -1,0 +1,287 @@
+"""Pins for the fp64 oracle: checks that tie it to something other than itself.
+
+Each ``pin_*`` takes the oracle module (or a deliberately broken copy of it,
+see test_oracle_mutants.py) and raises AssertionError on a mismatch.  The
+pins come from the pages' worked example, closed forms of a plane rotation,
+PyTorch's SDPA in float64 (a library routine the GQA case reduces to),
+brute-force loops and the invariants the pages state.
+"""
+
+from __future__ import annotations
+
+import cmath
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def close(a, b, tol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ------------------------------------------------------------------ RoPE --
+
+def pin_inv_freq_closed_form(orc):
+    """omega_0 = 1 and omega_{d/4} = theta^(-1/2) = 1e-3 for theta = 1e6; the
+    ratio of neighbours is theta^(-2/d) (geometric ladder over d/2 pairs)."""
+    for d in (4, 8, 64, 128):
+        w = orc.inv_freq(d, 1.0e6)
+        assert w.shape == (d // 2,), "inv_freq length"
+        close(w[0], 1.0, 0.0, "omega_0")
+        close(w[d // 4], 1.0e-3, 1e-18, f"omega_(d/4) d={d}")
+        close(w[1:] / w[:-1], np.full(d // 2 - 1, 10.0 ** (-12.0 / d)), 1e-14,
+              f"omega ratio d={d}")
+    close(orc.inv_freq(2, 1.0e6), [1.0], 0.0, "d=2")
+
+
+def pin_rope_d2_is_plane_rotation(orc):
+    """d = 2: one pair with omega = 1, so position m turns (a, b) by m radians,
+    i.e. multiplies a + ib by e^{im}."""
+    rng = _rng(1)
+    for m in (0, 1, 2, 7, 1000, 32767, 32768):
+        a, b = _rand(rng, 2)
+        z = complex(a, b) * cmath.exp(1j * m)
+        out = orc.rope(np.array([[[[a, b]]]]), [m], 1.0e6)[0, 0, 0]
+        close(out, [z.real, z.imag], 1e-12, f"plane rotation m={m}")
+
+
+def pin_rope_half_split_pairing(orc):
+    """Dimension j pairs with j + d/2: a unit vector on dim j rotated at m has
+    its only non-zeros on dims j (cos) and j + d/2 (sin of m*theta^(-2j/d))."""
+    d = 8
+    for j in range(d // 2):
+        e = np.zeros((1, 1, 1, d))
+        e[..., j] = 1.0
+        m = 3
+        ang = m * 1.0e6 ** (-2.0 * j / d)
+        want = np.zeros(d)
+        want[j] = math.cos(ang)
+        want[j + d // 2] = math.sin(ang)
+        close(orc.rope(e, [m], 1.0e6)[0, 0, 0], want, 1e-14, f"pair of dim {j}")
+
+
+def pin_rope_norm(orc):
+    """Rotation leaves every row's length unchanged (pages: RoPE keeps the
+    vector length and only changes phases)."""
+    rng = _rng(2)
+    x = _rand(rng, 2, 5, 3, 128)
+    pos = np.array([0, 1, 4095, 32767, 32768])
+    r = orc.rope(x, pos, 1.0e6)
+    close(np.linalg.norm(r, axis=-1), np.linalg.norm(x, axis=-1), 1e-12, "norms")
+
+
+def pin_rope_relative(orc):
+    """q'_m . k'_n depends only on m - n (pages: S_ij reflects i - j)."""
+    rng = _rng(3)
+    q = _rand(rng, 1, 1, 1, 64)
+    k = _rand(rng, 1, 1, 1, 64)
+    for m, n, c in ((5, 2, 100), (4096, 0, 28000), (32767, 1, 1), (9, 9, 32000)):
+        a = np.sum(orc.rope(q, [m])[0, 0, 0] * orc.rope(k, [n])[0, 0, 0])
+        b = np.sum(orc.rope(q, [m + c])[0, 0, 0] * orc.rope(k, [n + c])[0, 0, 0])
+        close(a, b, 1e-10, f"relative m={m} n={n} c={c}")
+
+
+def pin_rope_group_law(orc):
+    """R(0) = I and R(n) R(m) = R(m + n)."""
+    rng = _rng(4)
+    x = _rand(rng, 1, 3, 2, 16)
+    close(orc.rope(x, [0, 0, 0]), x, 0.0, "R(0)")
+    m = np.array([1, 50, 20000])
+    n = np.array([7, 3, 12767])
+    close(orc.rope(orc.rope(x, m), n), orc.rope(x, m + n), 1e-10, "R(n)R(m)")
+
+
+# ------------------------------------------------------------- grouping --
+
+def pin_group_example(orc):
+    """The pages' Qwen2-7B example: heads 1-7 read group 1, heads 8-14 group 2.
+    V of group u is the constant u+1 everywhere, so output head t must equal
+    the 1-based group the table lists for it."""
+    rows = read_table("group_mapping_qwen2_7b.txt")
+    h_q = int(rows[0][1])
+    h_kv = int(rows[1][1])
+    table = [(int(a), int(b)) for a, b in rows[2:]]
+    rng = _rng(5)
+    L, d = 4, 8
+    q = _rand(rng, 1, L, h_q, d)
+    k = _rand(rng, 1, L, h_kv, d)
+    v = np.empty((1, L, h_kv, d))
+    for u in range(h_kv):
+        v[:, :, u, :] = u + 1
+    o = orc.prefill(q, k, v)
+    for t1, u1 in table:
+        close(o[0, :, t1 - 1, :], np.full((L, d), float(u1)), 1e-12,
+              f"head {t1} -> group {u1}")
+
+
+def pin_repeat_interleave(orc):
+    """GQA equals MHA after expanding K/V with repeat_interleave along heads
+    (docs.keinmal.top pitfall 2), and differs from tiling the groups."""
+    rng = _rng(6)
+    B, L, h_q, h_kv, d = 2, 7, 6, 2, 8
+    g = h_q // h_kv
+    q = _rand(rng, B, L, h_q, d)
+    k = _rand(rng, B, L, h_kv, d)
+    v = _rand(rng, B, L, h_kv, d)
+    o = orc.prefill(q, k, v)
+    o_rep = orc.prefill(q, np.repeat(k, g, axis=2), np.repeat(v, g, axis=2))
+    close(o, o_rep, 1e-12, "GQA vs repeat_interleave MHA")
+    o_tile = orc.prefill(q, np.tile(k, (1, 1, g, 1)), np.tile(v, (1, 1, g, 1)))
+    assert np.max(np.abs(o - o_tile)) > 1e-3, "GQA must differ from tiled repeat"
+
+
+def pin_sdpa(orc):
+    """With the rotation applied, the oracle equals PyTorch's SDPA in float64
+    (causal, enable_gqa, default scale 1/sqrt(d)) for MHA (g = 1), MQA
+    (h_kv = 1) and GQA (g = 7, the Qwen2 ratio)."""
+    rng = _rng(7)
+    F = torch.nn.functional
+    for (B, L, h_q, h_kv, d) in ((1, 9, 4, 4, 8), (2, 11, 4, 1, 16),
+                                 (1, 13, 14, 2, 64), (1, 5, 28, 4, 128)):
+        q = _rand(rng, B, L, h_q, d)
+        k = _rand(rng, B, L, h_kv, d)
+        v = _rand(rng, B, L, h_kv, d)
+        pos = np.arange(L)
+        qt = torch.from_numpy(orc.rope(q, pos)).permute(0, 2, 1, 3)
+        kt = torch.from_numpy(orc.rope(k, pos)).permute(0, 2, 1, 3)
+        vt = torch.from_numpy(v).permute(0, 2, 1, 3)
+        for causal in (True, False):
+            ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=causal,
+                                                 enable_gqa=(h_q != h_kv))
+            o = orc.prefill(q, k, v, causal=causal)
+            close(o, ref.permute(0, 2, 1, 3).numpy(), 1e-12,
+                  f"SDPA B{B} L{L} {h_q}/{h_kv} d{d} causal={causal}")
+
+
+def pin_brute(orc):
+    """Scalar-loop definition vs the vectorised oracle on tiny inputs."""
+    rng = _rng(8)
+    for (B, L, h_q, h_kv, d, pos0) in ((1, 6, 4, 2, 8, 0), (1, 5, 3, 1, 4, 11),
+                                       (2, 4, 2, 2, 2, 0)):
+        q = _rand(rng, B, L, h_q, d)
+        k = _rand(rng, B, L, h_kv, d)
+        v = _rand(rng, B, L, h_kv, d)
+        close(orc.prefill(q, k, v, pos0=pos0),
+              orc.prefill_brute(q.tolist(), k.tolist(), v.tolist(), pos0=pos0),
+              1e-12, f"brute B{B} L{L} {h_q}/{h_kv} d{d}")
+
+
+# -------------------------------------------------------- softmax/causal --
+
+def pin_softmax_causal(orc):
+    """Rows of A sum to 1, weights above the diagonal are exactly 0, row 0 of
+    every head is V[0] of its group, and equal rotated keys give the running
+    mean of V (closed form A_ij = 1/(i+1))."""
+    rng = _rng(9)
+    L, d = 10, 16
+    qr = _rand(rng, L, d)
+    kr = _rand(rng, L, d)
+    v = _rand(rng, L, d)
+    vis = orc.visible(np.arange(L), np.arange(L))
+    A = orc.head_weights(qr, kr, 0.25, vis)
+    close(A.sum(axis=1), np.ones(L), 1e-14, "row sums")
+    assert np.all(A[np.triu_indices(L, 1)] == 0.0), "future weight not zero"
+    assert np.all(A[np.tril_indices(L)] > 0.0), "visible weight not positive"
+    o = orc.attend(qr, kr, v, 0.25, vis)
+    close(o[0], v[0], 1e-15, "row 0 = V[0]")
+    keq = np.repeat(_rand(rng, 1, d), L, axis=0)
+    o = orc.attend(qr, keq, v, 0.25, vis)
+    close(o, np.cumsum(v, axis=0) / np.arange(1, L + 1)[:, None], 1e-13,
+          "equal keys -> prefix mean")
+
+
+def pin_future_invariance(orc):
+    """Output row i does not change when K/V rows after i change."""
+    rng = _rng(10)
+    B, L, h_q, h_kv, d = 1, 12, 4, 2, 8
+    q = _rand(rng, B, L, h_q, d)
+    k = _rand(rng, B, L, h_kv, d)
+    v = _rand(rng, B, L, h_kv, d)
+    o = orc.prefill(q, k, v)
+    i = 5
+    k2, v2 = k.copy(), v.copy()
+    k2[:, i + 1:] = _rand(rng, B, L - i - 1, h_kv, d) * 5
+    v2[:, i + 1:] = _rand(rng, B, L - i - 1, h_kv, d) * 5
+    o2 = orc.prefill(q, k2, v2)
+    close(o2[:, :i + 1], o[:, :i + 1], 1e-13, "rows <= i unchanged")
+    assert np.max(np.abs(o2[:, i + 1:] - o[:, i + 1:])) > 1e-3, "later rows must move"
+
+
+def pin_shift_invariance(orc):
+    """Moving every position by c leaves the prefill output unchanged."""
+    rng = _rng(11)
+    q = _rand(rng, 1, 8, 4, 16)
+    k = _rand(rng, 1, 8, 2, 16)
+    v = _rand(rng, 1, 8, 2, 16)
+    close(orc.prefill(q, k, v, pos0=0), orc.prefill(q, k, v, pos0=32000), 1e-11,
+          "shift by 32000")
+
+
+# --------------------------------------------------------------- decode --
+
+def pin_decode_is_prefill_row(orc):
+    """A decode step at position p over the rotated cache rows 0..p equals
+    row p of the prefill (the cache holds the same rotated K and V)."""
+    rng = _rng(12)
+    B, L, h_q, h_kv, d = 2, 9, 14, 2, 16
+    q = _rand(rng, B, L, h_q, d)
+    k = _rand(rng, B, L, h_kv, d)
+    v = _rand(rng, B, L, h_kv, d)
+    o = orc.prefill(q, k, v)
+    cap = L + 3
+    kc = np.zeros((B, cap, h_kv, d))
+    vc = np.zeros((B, cap, h_kv, d))
+    kc[:, :L] = orc.rope(k, np.arange(L))
+    vc[:, :L] = v
+    kc[:, L:] = 1e3   # rows past kv_len must be ignored
+    vc[:, L:] = 1e3
+    for p in (0, 4, L - 1):
+        od = orc.decode(q[:, p], kc, vc, kv_len=p + 1, q_pos=p)
+        close(od, o[:, p], 1e-12, f"decode at {p}")
+
+
+def pin_prefill_rows(orc):
+    """Sampled-row evaluation equals the full prefill at those rows."""
+    rng = _rng(13)
+    B, L, h_q, h_kv, d = 2, 17, 6, 3, 8
+    q = _rand(rng, B, L, h_q, d)
+    k = _rand(rng, B, L, h_kv, d)
+    v = _rand(rng, B, L, h_kv, d)
+    o = orc.prefill(q, k, v)
+    rows = [(0, 0, 0), (1, 16, 5), (0, 9, 3), (1, 3, 2)]
+    want = np.stack([o[b, i, t] for b, i, t in rows])
+    close(orc.prefill_rows(q, k, v, rows), want, 1e-12, "prefill_rows")
+
+
+ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
+            pin_rope_half_split_pairing, pin_rope_norm, pin_rope_relative,
+            pin_rope_group_law, pin_group_example, pin_repeat_interleave,
+            pin_sdpa, pin_brute, pin_softmax_causal, pin_future_invariance,
+            pin_shift_invariance, pin_decode_is_prefill_row, pin_prefill_rows]

@@ -1,0 +1,142 @@
+"""Plant plausible mistakes in a private copy of the oracle (on the CPU) and
+check that at least one pin catches each of them."""
+
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "gqa_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("oracle_mutant", ORACLE_SRC)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _rope_variant(mod, kind):
+    orig_inv = mod.inv_freq
+
+    def rope(x, positions, theta=mod.ROPE_THETA):
+        x = np.asarray(x, np.float64)
+        d = x.shape[-1]
+        half = d // 2
+        pos = np.asarray(positions, np.float64)
+        ang = pos[..., None] * orig_inv(d, theta)
+        c = np.cos(ang)[..., None, :]
+        s = np.sin(ang)[..., None, :]
+        if kind == "interleaved":
+            x1, x2 = x[..., 0::2], x[..., 1::2]
+            out = np.empty_like(x)
+            out[..., 0::2] = x1 * c - x2 * s
+            out[..., 1::2] = x2 * c + x1 * s
+            return out
+        x1, x2 = x[..., :half], x[..., half:]
+        if kind == "clockwise":
+            return np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=-1)
+        if kind == "dropped_term":
+            return np.concatenate([x1 * c, x2 * c + x1 * s], axis=-1)
+        raise AssertionError(kind)
+    return rope
+
+
+def m_group_tiled(mod):
+    mod.kv_group = lambda t, h_q, h_kv: t % h_kv
+
+
+def m_group_off_by_one(mod):
+    mod.kv_group = lambda t, h_q, h_kv: min((t + 1) // (h_q // h_kv), h_kv - 1)
+
+
+def m_rope_interleaved(mod):
+    mod.rope = _rope_variant(mod, "interleaved")
+
+
+def m_rope_clockwise(mod):
+    mod.rope = _rope_variant(mod, "clockwise")
+
+
+def m_rope_dropped_term(mod):
+    mod.rope = _rope_variant(mod, "dropped_term")
+
+
+def m_freq_no_factor_two(mod):
+    mod.inv_freq = lambda d, theta=1e6: np.power(theta, -np.arange(d // 2) / d)
+
+
+def m_theta_1e4(mod):
+    orig = mod.inv_freq
+    mod.inv_freq = lambda d, theta=1e6: orig(d, 1.0e4)
+
+
+def m_mask_strict(mod):
+    mod.visible = lambda qp, kp: np.asarray(kp)[None, :] < np.asarray(qp)[:, None]
+
+
+def m_mask_transposed(mod):
+    mod.visible = lambda qp, kp: np.asarray(kp)[None, :] >= np.asarray(qp)[:, None]
+
+
+def m_no_scale(mod):
+    orig = mod.head_weights
+    mod.head_weights = lambda q, k, scale, vis: orig(q, k, 1.0, vis)
+
+
+def m_transposed_weights(mod):
+    orig = mod.head_weights
+
+    def attend(q, k, v, scale, vis):
+        return orig(q, k, scale, vis).T @ np.asarray(v, np.float64)
+    mod.attend = attend
+
+
+def m_softmax_no_norm(mod):
+    def softmax_rows(s, vis):
+        s = np.where(vis, s, -np.inf)
+        return np.exp(s - np.max(s, axis=-1, keepdims=True))
+    mod.softmax_rows = softmax_rows
+
+
+def m_decode_unrotated_query(mod):
+    orig = mod.rope
+
+    def rope(x, positions, theta=mod.ROPE_THETA):
+        x = np.asarray(x)
+        if x.ndim == 4 and x.shape[1] == 1 and np.size(positions) == 1 and x.shape[0] > 1:
+            return np.asarray(x, np.float64)
+        return orig(x, positions, theta)
+    mod.rope = rope
+
+
+MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
+           m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
+           m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
+           m_transposed_weights, m_softmax_no_norm, m_decode_unrotated_query]
+
+
+def failing_pins(mod):
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception as e:   # any error counts as the pin catching it
+            failed.append((pin.__name__, type(e).__name__))
+    return failed
+
+
+def test_unmutated_copy_passes():
+    assert failing_pins(fresh_oracle()) == []
+
+
+@pytest.mark.parametrize("mutate", MUTANTS, ids=lambda m: m.__name__)
+def test_mutant_is_caught(mutate):
+    mod = fresh_oracle()
+    mutate(mod)
+    assert failing_pins(mod), f"no pin catches {mutate.__name__}"
