@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark: causal GQA prefill TFLOP/s + decode KV-stream GB/s on one MI355X.
+
+One step = one pass of the whole hot path over resident synthetic inputs:
+  * gqa_prefill on the Qwen2-7B-shaped workload (B=4, L=4096, 28 query heads
+    over 4 KV heads, head size 128, bf16 in, fp32 accumulate and out, causal,
+    RoPE theta 1e6): RoPE table, K/V preparation, attention;
+  * gqa_decode on the Qwen2-7B-shaped decode workload (B=32 sequences, a
+    32768-position bf16 cache, one new token at position 32768).
+`value` is the prefill rate in TFLOP/s over the causal pairs only
+(4 * B * h_q * d * L(L+1)/2 flop per call) measured around the whole call;
+the decode rate (K/V cache bytes read once per KV group / call time) is
+reported beside it.  Kernel durations for the roofline objects come from HIP
+events that the library records on the launch stream around its attention
+and split-K kernels.  The CPU baseline is the fp64 oracle timed on a bounded
+sample of the prefill workload.
+
+Prints one JSON line.  Only one GPU is supported.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GQA prefill TFLOP/s + decode KV-stream GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
+# HBM bytes per dispatch measured by rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE,
+# scaled by the copy-kernel calibration); None until measured for the
+# current kernels.
+TRAFFIC_PREFILL_BYTES = None
+TRAFFIC_DECODE_BYTES = None
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+                   help="run one half of the step (for profiling)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mb", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def cpu_baseline(w):
+    """Time the fp64 oracle (as it stands) on batch slice 0 of the prefill
+    workload (all heads, all positions)."""
+    import oracle
+    from synthetic import gen_prefill
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    q, k, v = gen_prefill(w, B=1)
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, theta=w.theta, scale=w.scale)
+    dt = time.perf_counter() - t0
+    flops = 4 * 1 * w.h_q * w.d * w.L * (w.L + 1) // 2
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch 0 of {w.B} ({w.h_q} query heads, all {w.L} positions) of "
+                      f"{w.name}; {flops / 1e9:.1f} causal GFLOP in {dt:.2f} s (fp64 NumPy)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rope_causal_grouped_amd as gqa
+    from synthetic import WORKLOADS, gen_decode_cache_b, gen_decode_query, gen_prefill
+
+    wp, wd = WORKLOADS["c2"], WORKLOADS["c3"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    run_p = args.only in (None, "prefill")
+    run_d = args.only in (None, "decode")
+
+    # ---- inputs resident in HBM
+    if run_p:
+        log(f"[bench] generating {wp.name}")
+        q, k, v = gen_prefill(wp)
+        qd, kd, vd = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in (q, k, v))
+        del q, k, v
+        od = torch.empty((wp.B, wp.L, wp.h_q, wp.d), dtype=torch.float32, device=dev)
+        wsp = torch.empty(gqa.prefill_workspace_size(torch.bfloat16, wp.B, wp.L, wp.h_kv, wp.d),
+                          dtype=torch.uint8, device=dev)
+    if run_d:
+        log(f"[bench] generating {wd.name}")
+        qh = torch.from_numpy(gen_decode_query(wd)).to(dev, torch.bfloat16)
+        kc = torch.empty((wd.B, wd.L, wd.h_kv, wd.d), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        for b in range(wd.B):
+            kb, vb = gen_decode_cache_b(wd, b)
+            kc[b].copy_(torch.from_numpy(kb))
+            vc[b].copy_(torch.from_numpy(vb))
+        odd = torch.empty((wd.B, wd.h_q, wd.d), dtype=torch.float32, device=dev)
+        wsd = torch.empty(gqa.decode_workspace_size(wd.B, wd.h_q, wd.h_kv, wd.d, wd.L),
+                          dtype=torch.uint8, device=dev)
+
+    def step():
+        if run_p:
+            gqa.prefill(qd, kd, vd, out=od, workspace=wsp)
+        if run_d:
+            gqa.decode(qh, kc, vc, kv_len=wd.L, q_pos=wd.q_pos, out=odd, workspace=wsd)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K)]
+    gqa.timing_enable(True)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for s in range(K):
+        ev[3 * s].record()
+        if run_p:
+            gqa.prefill(qd, kd, vd, out=od, workspace=wsp)
+        ev[3 * s + 1].record()
+        if run_d:
+            gqa.decode(qh, kc, vc, kv_len=wd.L, q_pos=wd.q_pos, out=odd, workspace=wsd)
+        ev[3 * s + 2].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    gqa.timing_enable(False)
+    total_ms = t_start.elapsed_time(t_end)
+    pre_ms = sum(ev[3 * s].elapsed_time(ev[3 * s + 1]) for s in range(K)) / K
+    dec_ms = sum(ev[3 * s + 1].elapsed_time(ev[3 * s + 2]) for s in range(K)) / K
+    attn_ms, attn_n = gqa.timing_read(0)
+    split_ms, split_n = gqa.timing_read(1)
+    log(f"[bench] timed {K} steps: {total_ms:.2f} ms total")
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mb} MiB x3 done")
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_step": total_ms / K, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if run_p:
+        flops = wp.prefill_flops()
+        attn_avg = attn_ms / max(attn_n, 1)
+        out["value"] = flops / (pre_ms * 1e-3) / 1e12
+        out["unit"] = "TFLOP/s"
+        out["config"] = {
+            "workload": f"{wp.name}: B{wp.B} L{wp.L} h_q{wp.h_q} h_kv{wp.h_kv} d{wp.d} causal "
+                        f"RoPE theta 1e6, bf16 in / fp32 out; plus {wd.name}: B{wd.B} "
+                        f"cache {wd.L} h_q{wd.h_q} h_kv{wd.h_kv} d{wd.d} bf16",
+            "global_batch": wp.B, "seq_len": wp.L, "parallelism": "single-gpu"}
+        out["prefill_call_ms"] = pre_ms
+        ach = flops / (attn_avg * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel",
+                           "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / PEAK_BF16_TFLOPS, "kernel_ms": attn_avg,
+                           "traffic": TRAFFIC_PREFILL_BYTES}
+    if run_d:
+        kvb = wd.decode_kv_bytes()
+        split_avg = split_ms / max(split_n, 1)
+        dach = kvb / (split_avg * 1e-3) / 1e9
+        dec = {"workload": f"{wd.name}: B{wd.B} cache {wd.L} h_q{wd.h_q} h_kv{wd.h_kv} "
+                           f"d{wd.d} q_pos {wd.q_pos}",
+               "value": kvb / (dec_ms * 1e-3) / 1e9, "unit": "GB/s", "call_ms": dec_ms,
+               "roofline": {"bound": "hbm", "kernel": "decode_split_bf16_kernel",
+                            "achieved": dach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": dach / PEAK_HBM_GBS, "kernel_ms": split_avg,
+                            "traffic": TRAFFIC_DECODE_BYTES}}
+        out["decode"] = dec
+        if not run_p:
+            out["value"], out["unit"] = dec["value"], "GB/s"
+            out["config"] = {"workload": dec["workload"], "global_batch": wd.B,
+                             "seq_len": wd.L, "parallelism": "single-gpu"}
+            out["roofline"] = dec["roofline"]
+    if run_p and not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

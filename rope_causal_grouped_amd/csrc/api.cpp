@@ -1,0 +1,297 @@
+// C ABI of the library (declared in include/gqa.h): argument validation,
+// workspace carving and kernel dispatch.  Nothing here allocates device
+// memory or synchronises the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "gqa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool dtype_ok(int dt) { return dt == GQA_F32 || dt == GQA_BF16; }
+
+// ---- benchmark timing: HIP event pairs around the main kernel of a call
+struct Timing {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[2];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  std::pair<hipEvent_t, hipEvent_t> take() {
+    if (!pool.empty()) {
+      auto p = pool.back();
+      pool.pop_back();
+      return p;
+    }
+    std::pair<hipEvent_t, hipEvent_t> p{nullptr, nullptr};
+    if (hipEventCreate(&p.first) != hipSuccess || hipEventCreate(&p.second) != hipSuccess)
+      return {nullptr, nullptr};
+    return p;
+  }
+};
+Timing g_timing;
+
+struct Shape {
+  int64_t B, L;
+  int h_q, h_kv, d;
+};
+
+int check_heads(int h_q, int h_kv) {
+  if (h_q < 1 || h_kv < 1)
+    return fail(GQA_ERR_INVALID_ARG, "head counts must be >= 1 (h_q=%d, h_kv=%d)", h_q, h_kv);
+  if (h_q % h_kv != 0)
+    return fail(GQA_ERR_INVALID_ARG,
+                "h_q must be a multiple of h_kv (h_q=%d, h_kv=%d): each group of g = h_q/h_kv "
+                "query heads shares one K/V head",
+                h_q, h_kv);
+  return GQA_OK;
+}
+
+int check_d(int d) {
+  if (d < 2 || (d & 1)) return fail(GQA_ERR_INVALID_ARG, "d=%d: RoPE needs an even head size", d);
+  if (d != 64 && d != 128)
+    return fail(GQA_ERR_UNSUPPORTED, "d=%d: kernels are built for head sizes 64 and 128", d);
+  return GQA_OK;
+}
+
+int check_theta_scale(double theta, float scale) {
+  if (!(theta > 1.0) || !std::isfinite(theta))
+    return fail(GQA_ERR_INVALID_ARG, "theta=%g must be finite and > 1", theta);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale must be finite");
+  return GQA_OK;
+}
+
+int64_t prefill_lpad(int64_t L) { return (L + gqa::kPrefillTileK - 1) / gqa::kPrefillTileK * gqa::kPrefillTileK; }
+
+// workspace pieces of gqa_prefill
+struct PrefillWs {
+  size_t cs_off, kp_off, vt_off, total;
+};
+
+PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
+  PrefillWs w{};
+  const size_t cs = align256((size_t)L * (size_t)(d / 2) * sizeof(float2));
+  w.cs_off = 0;
+  w.kp_off = cs;
+  if (in_dtype == GQA_BF16) {
+    const size_t kp = align256((size_t)B * h_kv * prefill_lpad(L) * d * 2);
+    w.vt_off = cs + kp;
+    w.total = cs + 2 * kp;
+  } else {
+    const size_t kp = align256((size_t)B * h_kv * L * d * 4);
+    w.vt_off = cs + kp;
+    w.total = cs + kp;
+  }
+  return w;
+}
+
+struct DecodeWs {
+  size_t m_off, l_off, o_off, total;
+};
+
+DecodeWs decode_ws(int64_t B, int h_q, int h_kv, int d, int64_t cap) {
+  const int g = h_q / h_kv;
+  const size_t n = (size_t)B * h_kv * gqa::decode_num_splits(cap) * g;
+  DecodeWs w{};
+  w.m_off = 0;
+  w.l_off = align256(n * 4);
+  w.o_off = w.l_off + align256(n * 4);
+  w.total = w.o_off + align256(n * (size_t)d * 4);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_last_error(void) { return g_err.c_str(); }
+
+const char* gqa_version(void) { return "gqa-mi355x 0.1 (gfx950)"; }
+
+int gqa_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,
+                   double theta, void* stream) {
+  g_err.clear();
+  if (!x) return fail(GQA_ERR_INVALID_ARG, "x is NULL");
+  if (!dtype_ok(dtype)) return fail(GQA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (B < 1 || L < 1 || h < 1) return fail(GQA_ERR_INVALID_ARG, "B, L, h must be >= 1");
+  if (d < 2 || (d & 1)) return fail(GQA_ERR_INVALID_ARG, "d=%d: RoPE needs an even head size", d);
+  if (pos0 < 0 || pos0 > (INT64_C(1) << 40)) return fail(GQA_ERR_INVALID_ARG, "pos0 out of range");
+  if (int rc = check_theta_scale(theta, 1.0f)) return rc;
+  if (!aligned16(x)) return fail(GQA_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  hipError_t e = gqa::launch_rope_apply(x, dtype, B, L, h, d, pos0, std::log2(theta),
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e, "rope_apply launch");
+}
+
+size_t gqa_prefill_workspace_size(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
+  if (!dtype_ok(in_dtype) || B < 1 || L < 1 || h_kv < 1 || d < 2) return 0;
+  return prefill_ws(in_dtype, B, L, h_kv, d).total;
+}
+
+int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dtype, int out_dtype,
+                int64_t B, int64_t L, int h_q, int h_kv, int d, double theta, float scale,
+                int causal, void* k_cache, void* v_cache, int64_t cap, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!q || !k || !v || !o) return fail(GQA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in=%d, out=%d)", in_dtype, out_dtype);
+  if (B < 1 || L < 1) return fail(GQA_ERR_INVALID_ARG, "B and L must be >= 1");
+  if (int rc = check_heads(h_q, h_kv)) return rc;
+  if (int rc = check_d(d)) return rc;
+  if (int rc = check_theta_scale(theta, scale)) return rc;
+  if ((k_cache == nullptr) != (v_cache == nullptr))
+    return fail(GQA_ERR_INVALID_ARG, "k_cache and v_cache must both be set or both be NULL");
+  if (k_cache && cap < L) return fail(GQA_ERR_INVALID_ARG, "cap=%lld < L=%lld", (long long)cap, (long long)L);
+  const int g = h_q / h_kv;
+  if (L * g + gqa::kPrefillRowsWG > INT_MAX || B * h_kv > 65535 || L > (INT64_C(1) << 24))
+    return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
+  const int64_t n_rb = (L * g + gqa::kPrefillRowsWG - 1) / gqa::kPrefillRowsWG;
+  if (n_rb * B * h_kv > INT_MAX) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(workspace))
+    return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const PrefillWs ws = prefill_ws(in_dtype, B, L, h_kv, d);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                workspace ? workspace_bytes : (size_t)0);
+
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  float2* cs = (float2*)(wsb + ws.cs_off);
+  const double l2t = std::log2(theta);
+  hipError_t e = gqa::launch_rope_table(cs, L, d, 0, l2t, st);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (g_timing.on) ev = g_timing.take();
+
+  if (in_dtype == GQA_BF16) {
+    const int64_t Lpad = prefill_lpad(L);
+    uint16_t* kp = (uint16_t*)(wsb + ws.kp_off);
+    uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
+    e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, cs, kp, vt,
+                                    (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad, h_kv, d,
+                                    cap, st);
+    if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
+    if (ev.first) (void)hipEventRecord(ev.first, st);
+    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, cs, o, out_dtype == GQA_BF16, B, L,
+                                 Lpad, h_q, h_kv, d, scale, causal, st);
+  } else {
+    float* kp = (float*)(wsb + ws.kp_off);
+    e = gqa::launch_kv_prepare_f32((const float*)k, (const float*)v, cs, kp, (float*)k_cache,
+                                   (float*)v_cache, B, L, h_kv, d, cap, st);
+    if (e != hipSuccess) return hip_fail(e, "K preparation launch");
+    if (ev.first) (void)hipEventRecord(ev.first, st);
+    e = gqa::launch_prefill_f32((const float*)q, kp, (const float*)v, cs, o,
+                                out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, st);
+  }
+  if (ev.second) {
+    (void)hipEventRecord(ev.second, st);
+    g_timing.rec[0].push_back(ev);
+  }
+  return e == hipSuccess ? GQA_OK : hip_fail(e, "prefill attention launch");
+}
+
+size_t gqa_decode_workspace_size(int64_t B, int h_q, int h_kv, int d, int64_t cap) {
+  if (B < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv || d < 2 || cap < 1) return 0;
+  return decode_ws(B, h_q, h_kv, d, cap).total;
+}
+
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int in_dtype,
+               int out_dtype, int64_t B, int h_q, int h_kv, int d, int64_t cap, int64_t kv_len,
+               int64_t q_pos, double theta, float scale, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  g_err.clear();
+  if (!q || !k_cache || !v_cache || !o)
+    return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-NULL");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in=%d, out=%d)", in_dtype, out_dtype);
+  if (B < 1) return fail(GQA_ERR_INVALID_ARG, "B must be >= 1");
+  if (int rc = check_heads(h_q, h_kv)) return rc;
+  if (int rc = check_d(d)) return rc;
+  if (int rc = check_theta_scale(theta, scale)) return rc;
+  if (cap < 1) return fail(GQA_ERR_INVALID_ARG, "cap must be >= 1");
+  if (kv_len < 1 || kv_len > cap)
+    return fail(GQA_ERR_INVALID_ARG, "kv_len=%lld outside [1, cap=%lld]", (long long)kv_len,
+                (long long)cap);
+  if (q_pos < 0 || kv_len > q_pos + 1)
+    return fail(GQA_ERR_INVALID_ARG,
+                "kv_len=%lld > q_pos+1=%lld: the query may only see keys at or before its position",
+                (long long)kv_len, (long long)(q_pos + 1));
+  if (cap > (INT64_C(1) << 30) || q_pos > (INT64_C(1) << 40) || B > 65535 || h_q > 65535)
+    return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(workspace))
+    return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const DecodeWs ws = decode_ws(B, h_q, h_kv, d, cap);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char* wsb = (char*)workspace;
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (g_timing.on) ev = g_timing.take();
+  hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
+                                    out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, kv_len, q_pos,
+                                    std::log2(theta), scale, (float*)(wsb + ws.m_off),
+                                    (float*)(wsb + ws.l_off), (float*)(wsb + ws.o_off),
+                                    (hipStream_t)stream, ev.first, ev.second);
+  if (ev.first) g_timing.rec[1].push_back(ev);
+  return e == hipSuccess ? GQA_OK : hip_fail(e, "decode launch");
+}
+
+int gqa_timing_enable(int on) {
+  g_timing.on = on != 0;
+  return GQA_OK;
+}
+
+int gqa_timing_read(int which, double* total_ms, int64_t* count) {
+  g_err.clear();
+  if (which < 0 || which > 1 || !total_ms || !count)
+    return fail(GQA_ERR_INVALID_ARG, "bad timing query");
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& p : g_timing.rec[which]) {
+    hipError_t e = hipEventSynchronize(p.second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, p.first, p.second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    tot += ms;
+    ++n;
+    g_timing.pool.push_back(p);
+  }
+  g_timing.rec[which].clear();
+  *total_ms = tot;
+  *count = n;
+  return GQA_OK;
+}
+
+}  // extern "C"

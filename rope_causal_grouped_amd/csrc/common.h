@@ -1,0 +1,52 @@
+// Device helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 2*pi split in two doubles (head + tail) for argument reduction.
+constexpr double kTwoPiHi = 6.283185307179586232;
+constexpr double kTwoPiLo = 2.449293598294706414e-16;
+constexpr double kInvTwoPi = 0.15915494309189533577;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bit pattern.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// RoPE inverse frequency of pair j: theta^(-2j/d), in fp64.
+__device__ __forceinline__ double rope_omega(int j, int d, double log2_theta) {
+  return exp2(-(2.0 * (double)j / (double)d) * log2_theta);
+}
+
+// cos and sin of pos * omega.  The angle is formed and reduced to
+// [-pi, pi] in fp64 (at position 32768 an fp32 angle would already be off
+// by ~2e-3 rad), then evaluated in fp32.
+__device__ __forceinline__ void rope_cos_sin(double pos, double omega, float& c,
+                                             float& s) {
+  double a = pos * omega;
+  double n = rint(a * kInvTwoPi);
+  double r = fma(-n, kTwoPiHi, a);
+  r = fma(-n, kTwoPiLo, r);
+  sincosf((float)r, &s, &c);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+}  // namespace gqa

@@ -1,0 +1,361 @@
+// Split-K GQA decode over a contiguous per-layer KV cache.
+//
+// One new query token per sequence at position q_pos attends to the cached,
+// already rotated keys 0 .. kv_len-1 (Qwen2 technical-report walkthrough,
+// aicoding.csdn.net, §4.1.3: the cache holds only the h_kv groups' K and V,
+// appended every step).  The query is rotated here at q_pos.
+//
+// The cache of one (batch, group) is cut into chunks of kDecodeChunk keys;
+// a workgroup streams one chunk exactly once for all g query heads of the
+// group (that single pass over the h_kv-group cache is what GQA saves in
+// bandwidth, same page §4.1.1) and leaves an unnormalised partial state
+// (row max m, sum l, weighted sum o).  A second kernel merges the chunks:
+//   M = max_s m_s,  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// which equals the unsplit softmax exactly (up to rounding).  Maxima are
+// kept in the log2 domain (scores pre-multiplied by scale * log2 e).
+
+#include "common.h"
+#include "launch.h"
+
+namespace gqa {
+
+int decode_num_splits(int64_t kv_len) {
+  return (int)((kv_len + kDecodeChunk - 1) / kDecodeChunk);
+}
+
+// bf16 cache, matrix cores.  Workgroup = (chunk, group u x head block, b);
+// four waves take a quarter of the chunk each.  Per 32-key step a wave
+// computes S^T = K q^T (v_mfma_f32_16x16x32_bf16: 16 keys x 16 heads, K
+// rows straight from HBM into the A operand), then O^T += V^T P^T with V
+// staged through a wave-private LDS slab to turn key-major rows into the
+// key-contiguous operand.  Heads beyond 16 per group run as extra head
+// blocks (another pass over the chunk).
+template <int D>
+__global__ __launch_bounds__(256) void decode_split_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int64_t cap, int kv_len,
+    double q_pos, double log2_theta, float sl2, int n_split) {
+  constexpr int CH = kDecodeChunk;
+  constexpr int WK = CH / 4;            // keys per wave
+  constexpr int NS = D / 32;            // 32-dim k-steps of S^T
+  constexpr int NDB = D / 16;           // 16-dim blocks of O^T
+  constexpr int VPITCH = D + 8;         // LDS pitch of a staged V row (elements)
+  constexpr int VLD = 32 * D / 8 / 64;  // 16-byte V loads per lane per 32-key step
+  __shared__ __attribute__((aligned(16))) uint16_t vsh[4][32 * VPITCH];
+  __shared__ float cm[4][16], cl[4][16];
+  __shared__ float co[4][16][D + 1];
+
+  const int split = blockIdx.x;
+  const int u = blockIdx.y / n_hb, hb = blockIdx.y % n_hb;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, h4 = lane >> 4;
+  const int c = hb * 16 + col;
+
+  // ---- rotated query, B operand: lane holds head `col`, dims s*32 + h4*8 + e
+  bf16x8 qb[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qb[s][e] = (__bf16)0.f;
+  if (c < g) {
+    const uint16_t* qrow = q + ((int64_t)b * h_q + (int64_t)u * g + c) * D;
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s) {
+      const u32x4 r1 = *(const u32x4*)(qrow + s * 32 + h4 * 8);
+      const u32x4 r2 = *(const u32x4*)(qrow + s * 32 + h4 * 8 + D / 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = s * 32 + h4 * 8 + e;
+        float cs_c, cs_s;
+        rope_cos_sin(q_pos, rope_omega(j, D, log2_theta), cs_c, cs_s);
+        const float x1 = (e & 1) ? __uint_as_float(r1[e >> 1] & 0xffff0000u)
+                                 : __uint_as_float(r1[e >> 1] << 16);
+        const float x2 = (e & 1) ? __uint_as_float(r2[e >> 1] & 0xffff0000u)
+                                 : __uint_as_float(r2[e >> 1] << 16);
+        qb[s][e] = (__bf16)fmaf(x1, cs_c, -x2 * cs_s);
+        qb[s + NS / 2][e] = (__bf16)fmaf(x2, cs_c, x1 * cs_s);
+      }
+    }
+  }
+
+  const int64_t RS = (int64_t)h_kv * D;  // elements between consecutive keys
+  const uint16_t* kbase = kc + ((int64_t)b * cap * h_kv + u) * D;
+  const uint16_t* vbase = vc + ((int64_t)b * cap * h_kv + u) * D;
+  const int kw0 = split * CH + wave * WK;
+  const int kw1 = min(kw0 + WK, kv_len);
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* vw = vsh[wave];
+
+  for (int k0 = kw0; k0 < kw1; k0 += 32) {
+    u32x4 ka[2][NS];
+    u32x4 va[VLD];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int key = min(k0 + blk * 16 + col, kv_len - 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        ka[blk][s] = *(const u32x4*)(kbase + key * RS + s * 32 + h4 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int ch = lane + 64 * i;
+      const int key = min(k0 + ch / (D / 8), kv_len - 1);
+      va[i] = *(const u32x4*)(vbase + key * RS + (ch % (D / 8)) * 8);
+    }
+    // S^T for 2 x 16 keys
+    f32x4 sacc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sacc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        sacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, ka[blk][s]), qb[s], sacc[blk], 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (k0 + blk * 16 + h4 * 4 + i >= kw1) sacc[blk][i] = -INFINITY;
+        mx = fmaxf(mx, sacc[blk][i]);
+      }
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m, mx * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    bf16x8 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 p = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[e >> 2][e & 3], sl2, -m_new));
+      pb[e] = p;
+      psum += (float)p;
+    }
+    l = fmaf(l, alpha, psum);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+    // V rows -> wave-private LDS (row-major), then the key-contiguous operand
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int ch = lane + 64 * i;
+      *(u32x4*)(vw + (ch / (D / 8)) * VPITCH + (ch % (D / 8)) * 8) = va[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      bf16x8 a;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = (e < 4) ? h4 * 4 + e : 16 + h4 * 4 + (e - 4);
+        a[e] = __builtin_bit_cast(__bf16, vw[kk * VPITCH + db * 16 + col]);
+      }
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[db], 0, 0, 0);
+    }
+  }
+
+  // ---- combine the four waves of the workgroup
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (h4 == 0) {
+    cm[wave][col] = m;
+    cl[wave][col] = l;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) co[wave][col][db * 16 + h4 * 4 + i] = oacc[db][i];
+  __syncthreads();
+  for (int idx = tid; idx < 16 * D; idx += 256) {
+    const int cc = idx / D, dim = idx % D;
+    if (hb * 16 + cc >= g) continue;
+    float M = cm[0][cc];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, cm[w][cc]);
+    float so = 0.f, sl = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = __builtin_amdgcn_exp2f(cm[w][cc] - M);
+      so = fmaf(f, co[w][cc][dim], so);
+      sl = fmaf(f, cl[w][cc], sl);
+    }
+    const int64_t out = (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16 + cc;
+    po[out * D + dim] = so;
+    if (dim == 0) {
+      pm[out] = M;
+      pl[out] = sl;
+    }
+  }
+}
+
+// fp32 cache, vector ALU (the fp32 parity path).  Workgroup = (chunk, u x
+// head block, b); 16 threads per head.  Scores of the chunk go to LDS, then
+// each thread reduces one head's max and sum and accumulates 1/16 of its
+// output dims.
+template <int D>
+__global__ __launch_bounds__(256) void decode_split_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
+    float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po, int h_q, int h_kv,
+    int g, int n_hb, int64_t cap, int kv_len, double q_pos, double log2_theta, float scale,
+    int n_split) {
+  constexpr int CH = kDecodeChunk;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ float qs[16][D];
+  __shared__ float sc[16][CH];
+  const int split = blockIdx.x;
+  const int u = blockIdx.y / n_hb, hb = blockIdx.y % n_hb;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int nh = min(16, g - hb * 16);
+
+  for (int idx = tid; idx < 16 * (D / 2); idx += 256) {
+    const int cc = idx / (D / 2), j = idx % (D / 2);
+    float y1 = 0.f, y2 = 0.f;
+    if (cc < nh) {
+      const float* qrow = q + ((int64_t)b * h_q + (int64_t)u * g + hb * 16 + cc) * D;
+      float c, s;
+      rope_cos_sin(q_pos, rope_omega(j, D, log2_theta), c, s);
+      y1 = fmaf(qrow[j], c, -qrow[j + D / 2] * s);
+      y2 = fmaf(qrow[j + D / 2], c, qrow[j] * s);
+    }
+    qs[cc][j] = y1;
+    qs[cc][j + D / 2] = y2;
+  }
+  __syncthreads();
+
+  const int k0 = split * CH;
+  const int nk = min(CH, kv_len - k0);
+  const int64_t RS = (int64_t)h_kv * D;
+  const float* kbase = kc + ((int64_t)b * cap * h_kv + u) * D;
+  const float* vbase = vc + ((int64_t)b * cap * h_kv + u) * D;
+  for (int kk = tid; kk < nk; kk += 256) {
+    const float* krow = kbase + (int64_t)(k0 + kk) * RS;
+    for (int cc = 0; cc < nh; ++cc) {
+      float dot = 0.f;
+      for (int dd = 0; dd < D; ++dd) dot = fmaf(qs[cc][dd], krow[dd], dot);
+      sc[cc][kk] = dot * scale;
+    }
+  }
+  __syncthreads();
+
+  const int cc = tid >> 4, sub = tid & 15;
+  float M = -INFINITY;
+  if (cc < nh)
+    for (int kk = sub; kk < nk; kk += 16) M = fmaxf(M, sc[cc][kk]);
+  for (int msk = 1; msk < 16; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk, 64));
+  __syncthreads();
+  float Ls = 0.f;
+  if (cc < nh)
+    for (int kk = sub; kk < nk; kk += 16) {
+      const float p = expf(sc[cc][kk] - M);
+      sc[cc][kk] = p;
+      Ls += p;
+    }
+  for (int msk = 1; msk < 16; msk <<= 1) Ls += __shfl_xor(Ls, msk, 64);
+  __syncthreads();
+  if (cc < nh) {
+    constexpr int DPT = D / 16;
+    float acc[DPT];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+    for (int kk = 0; kk < nk; ++kk) {
+      const float p = sc[cc][kk];
+      const float* vrow = vbase + (int64_t)(k0 + kk) * RS + sub * DPT;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) acc[e] = fmaf(p, vrow[e], acc[e]);
+    }
+    const int64_t out = (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16 + cc;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) po[out * D + sub * DPT + e] = acc[e];
+    if (sub == 0) {
+      pm[out] = M * kLog2e;
+      pl[out] = Ls;
+    }
+  }
+}
+
+// Merge the chunk partials of one (b, query head); one thread per dim.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restrict__ pm,
+                                                           const float* __restrict__ pl,
+                                                           const float* __restrict__ po,
+                                                           void* __restrict__ o, int h_q, int h_kv,
+                                                           int g, int d, int n_split) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int u = t / g, c = t % g;
+  const int64_t base = (((int64_t)b * h_kv + u) * n_split) * g + c;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pm[base + (int64_t)s * g]);
+  float L = 0.f;
+  for (int s = 0; s < n_split; ++s)
+    L = fmaf(__builtin_amdgcn_exp2f(pm[base + (int64_t)s * g] - M), pl[base + (int64_t)s * g], L);
+  const float inv = 1.0f / L;
+  for (int dim = threadIdx.x; dim < d; dim += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+      const int64_t idx = base + (int64_t)s * g;
+      acc = fmaf(__builtin_amdgcn_exp2f(pm[idx] - M), po[idx * d + dim], acc);
+    }
+    const int64_t oo = ((int64_t)b * h_q + t) * d + dim;
+    if constexpr (OUT_BF16)
+      ((uint16_t*)o)[oo] = f32_to_bf16_bits(acc * inv);
+    else
+      ((float*)o)[oo] = acc * inv;
+  }
+}
+
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, int in_bf16,
+                         int out_bf16, int64_t B, int h_q, int h_kv, int d, int64_t cap,
+                         int64_t kv_len, int64_t q_pos, double log2_theta, float scale,
+                         float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
+                         hipEvent_t ev_begin, hipEvent_t ev_end) {
+  const int g = h_q / h_kv;
+  const int n_hb = (g + 15) / 16;
+  const int n_split = decode_num_splits(kv_len);
+  dim3 grid((unsigned)n_split, (unsigned)(h_kv * n_hb), (unsigned)B);
+  const float sl2 = scale * 1.4426950408889634f;
+  if (ev_begin) (void)hipEventRecord(ev_begin, st);
+  if (in_bf16) {
+    if (d == 128)
+      decode_split_bf16_kernel<128><<<grid, 256, 0, st>>>(
+          (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
+          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split);
+    else
+      decode_split_bf16_kernel<64><<<grid, 256, 0, st>>>(
+          (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
+          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split);
+  } else {
+    if (d == 128)
+      decode_split_f32_kernel<128><<<grid, 256, 0, st>>>(
+          (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
+          n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split);
+    else
+      decode_split_f32_kernel<64><<<grid, 256, 0, st>>>(
+          (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
+          n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split);
+  }
+  hipError_t err = hipGetLastError();
+  if (ev_end) (void)hipEventRecord(ev_end, st);
+  if (err != hipSuccess) return err;
+  dim3 mgrid((unsigned)h_q, (unsigned)B);
+  if (out_bf16)
+    decode_merge_kernel<true><<<mgrid, 128, 0, st>>>(ws_m, ws_l, ws_o, o, h_q, h_kv, g, d, n_split);
+  else
+    decode_merge_kernel<false><<<mgrid, 128, 0, st>>>(ws_m, ws_l, ws_o, o, h_q, h_kv, g, d,
+                                                      n_split);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

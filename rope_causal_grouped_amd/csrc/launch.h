@@ -1,0 +1,46 @@
+// Internal launchers behind the C ABI (include/gqa.h).  Every launcher
+// assumes the API layer has validated its arguments and enqueues on `st`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kPrefillTileK = 64;      // keys per K/V tile (bf16 prefill)
+constexpr int kPrefillRowsWG = 256;    // stacked (position, head) rows per workgroup
+constexpr int kDecodeChunk = 1024;     // keys per decode split
+
+hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,
+                             double log2_theta, hipStream_t st);
+
+hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double log2_theta,
+                             hipStream_t st);
+
+hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
+                                  uint16_t* kp, uint16_t* vt, uint16_t* kc, uint16_t* vc,
+                                  int64_t B, int64_t L, int64_t Lpad, int h_kv, int d, int64_t cap,
+                                  hipStream_t st);
+
+hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* cs, float* kp,
+                                 float* kc, float* vc, int64_t B, int64_t L, int h_kv, int d,
+                                 int64_t cap, hipStream_t st);
+
+hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
+                               const float2* cs, void* o, int out_bf16, int64_t B, int64_t L,
+                               int64_t Lpad, int h_q, int h_kv, int d, float scale, int causal,
+                               hipStream_t st);
+
+hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, const float2* cs,
+                              void* o, int out_bf16, int64_t B, int64_t L, int h_q, int h_kv,
+                              int d, float scale, int causal, hipStream_t st);
+
+int decode_num_splits(int64_t kv_len);
+
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, int in_bf16,
+                         int out_bf16, int64_t B, int h_q, int h_kv, int d, int64_t cap,
+                         int64_t kv_len, int64_t q_pos, double log2_theta, float scale,
+                         float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
+                         hipEvent_t ev_begin, hipEvent_t ev_end);
+
+}  // namespace gqa

@@ -1,0 +1,248 @@
+// Causal GQA prefill on bf16 matrix cores (gfx950), RoPE fused into the Q
+// load, fp32 accumulation, online softmax.
+//
+// What it computes (Qwen2 technical-report walkthrough, aicoding.csdn.net,
+// §4.1.3 steps 3-4): for query head t and its KV group u = t / g,
+//   O_t = softmax(Q'_t K'_u^T * scale + M) V_u,  M_ij = -inf for j > i,
+// with Q', K' the rotated rows.  The same page notes the L x L score matrix
+// need not be materialised (flash-style); this kernel keeps it in registers.
+//
+// Work split.  The g query heads of one KV group read the same K and V, so
+// for a fixed (batch b, group u) the rows (position i, head t in the group)
+// form one "stacked" query matrix of L*g rows, ordered position-major; that
+// matrix is contiguous in q (g heads of one position are adjacent).  A
+// workgroup owns 256 consecutive stacked rows (about 256/g positions, all g
+// heads) and streams the K/V tiles of group u through LDS once for all of
+// them: this is the g-fold K/V reuse GQA offers (same page, closing note of
+// §4.1.3).  Eight waves each own 32 rows.
+//
+// Per 64-key tile, each wave computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the wave's rotated
+// Q rows resident in VGPRs as the B operand), so every lane holds one query
+// row's scores and the row max needs a single exchange with lane ^ 32.  The
+// probabilities, rounded to bf16, are already in the B-operand layout of
+// O^T += V^T P^T; V arrives pre-transposed (keys contiguous, in the lane
+// order of the accumulator) from the preparation pass.
+
+#include "common.h"
+#include "launch.h"
+
+namespace gqa {
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(512) void prefill_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
+    const uint16_t* __restrict__ vt, const float2* __restrict__ cs, void* __restrict__ o, int L,
+    int Lpad, int h_q, int h_kv, int g, int n_rb, int n_bu, float sl2, int causal) {
+  constexpr int TK = 64;          // keys per tile
+  constexpr int KP = D + 8;       // LDS pitch (elements) of a K row: +16 B against bank conflicts
+  constexpr int VP = TK + 8;      // LDS pitch of a V^T row
+  constexpr int NS = D / 16;      // k-steps of 16 dims for S^T
+  constexpr int NDB = D / 32;     // 32-dim blocks of O^T
+  constexpr int CPT = TK * D / 8 / 512;   // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][TK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, c32 = lane & 31;
+
+  // Heaviest row blocks (latest positions, most keys) are dispatched first.
+  const int id = blockIdx.x;
+  const int rb = n_rb - 1 - id / n_bu;
+  const int bu = id % n_bu;
+  const int b = bu / h_kv, u = bu % h_kv;
+
+  const int rows_total = L * g;
+  const int R0 = rb * 256;
+  const int r = R0 + wave * 32 + c32;
+  const bool row_valid = r < rows_total;
+  const int rr = row_valid ? r : rows_total - 1;
+  const int pos = rr / g;
+  const int t = u * g + (rr - pos * g);
+
+  // ---- Q rows: load, rotate at `pos`, round to bf16 (B operand layout:
+  // lane holds dims s*16 + hl*8 + e of its row; pairs (s, s + NS/2)).
+  bf16x8 qb[NS];
+  {
+    const uint16_t* qrow = q + ((int64_t)((int64_t)b * L + pos) * h_q + t) * D;
+    u32x4 raw[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) raw[s] = *(const u32x4*)(qrow + s * 16 + hl * 8);
+    const float2* csr = cs + (int64_t)pos * (D / 2) + hl * 8;
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 r2 = csr[s * 16 + e];
+        const uint32_t w1 = raw[s][e >> 1], w2 = raw[s + NS / 2][e >> 1];
+        const float x1 = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
+        const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);
+        qb[s][e] = (__bf16)fmaf(x1, r2.x, -x2 * r2.y);
+        qb[s + NS / 2][e] = (__bf16)fmaf(x2, r2.x, x1 * r2.y);
+      }
+    }
+  }
+
+  // ---- key range
+  const int rmax = min(R0 + 255, rows_total - 1);
+  const int n_keys = causal ? rmax / g + 1 : L;
+  const int n_tiles = (n_keys + TK - 1) / TK;
+  const int wr0 = min(R0 + wave * 32, rows_total - 1);
+  const int wr1 = min(R0 + wave * 32 + 31, rows_total - 1);
+  const int wpos_lo = wr0 / g, wpos_hi = wr1 / g;
+
+  const uint16_t* kbase = kp + (int64_t)bu * Lpad * D;
+  const uint16_t* vbase = vt + (int64_t)bu * Lpad * D;
+
+  u32x4 kreg[CPT], vreg[CPT];
+  auto gload = [&](int tile) {
+    const uint16_t* ksrc = kbase + (int64_t)tile * TK * D;
+    const uint16_t* vsrc = vbase + (int64_t)tile * TK * D;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 512;
+      kreg[c] = *(const u32x4*)(ksrc + ch * 8);
+      vreg[c] = *(const u32x4*)(vsrc + ch * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 512;
+      *(u32x4*)&ks[buf][(ch / (D / 8)) * KP + (ch % (D / 8)) * 8] = kreg[c];
+      *(u32x4*)&vs[buf][(ch / 8) * VP + (ch % 8) * 8] = vreg[c];
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_tiles) gload(kt + 1);
+    const int k0 = kt * TK;
+    if (!causal || k0 <= wpos_hi) {
+      // ---- S^T = K Q^T for two 32-key blocks
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+        const uint16_t* krow = &ks[buf][(kb * 32 + c32) * KP + hl * 8];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 a = *(const bf16x8*)(krow + s * 16);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[s], sacc[kb], 0, 0, 0);
+        }
+      }
+      // ---- causal / tail mask (only tiles that reach past the wave's first row)
+      const bool need_mask = (causal && k0 + TK - 1 > wpos_lo) || (k0 + TK > L);
+      if (need_mask) {
+        const int lim = causal ? min(pos, L - 1) : L - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
+            if (key > lim) sacc[kb][i] = -INFINITY;
+          }
+      }
+      // ---- online softmax (log2 domain)
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      bf16x8 pb[2][2];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, -m_new));
+          const __bf16 pbf = (__bf16)p;
+          pb[kb][i >> 3][i & 7] = pbf;
+          psum += (float)pbf;
+        }
+      l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint16_t* vrow = &vs[buf][(db * 32 + c32) * VP + hl * 8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            const bf16x8 a = *(const bf16x8*)(vrow + kb * 32 + hs * 16);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][hs], oacc[db], 0, 0, 0);
+          }
+      }
+    }
+    if (kt + 1 < n_tiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O / l; lane holds dims db*32 + grp*8 + hl*4 + (0..3)
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+  if (row_valid) {
+    const int64_t orow = ((int64_t)((int64_t)b * L + pos) * h_q + t) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int dim = db * 32 + grp * 8 + hl * 4;
+        const float y0 = oacc[db][grp * 4 + 0] * inv, y1 = oacc[db][grp * 4 + 1] * inv;
+        const float y2 = oacc[db][grp * 4 + 2] * inv, y3 = oacc[db][grp * 4 + 3] * inv;
+        if constexpr (OUT_BF16) {
+          u32x2 w;
+          w[0] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
+          w[1] = (uint32_t)f32_to_bf16_bits(y2) | ((uint32_t)f32_to_bf16_bits(y3) << 16);
+          *(u32x2*)((uint16_t*)o + orow + dim) = w;
+        } else {
+          f32x4 w = {y0, y1, y2, y3};
+          *(f32x4*)((float*)o + orow + dim) = w;
+        }
+      }
+  }
+}
+
+hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
+                               const float2* cs, void* o, int out_bf16, int64_t B, int64_t L,
+                               int64_t Lpad, int h_q, int h_kv, int d, float scale, int causal,
+                               hipStream_t st) {
+  const int g = h_q / h_kv;
+  const int n_rb = (int)((L * g + kPrefillRowsWG - 1) / kPrefillRowsWG);
+  const int n_bu = (int)(B * h_kv);
+  const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e): exp(x) = exp2(x log2 e)
+  const unsigned grid = (unsigned)((int64_t)n_rb * n_bu);
+#define GQA_LAUNCH(DD, OB)                                                                    \
+  prefill_bf16_kernel<DD, OB><<<grid, 512, 0, st>>>(q, kp, vt, cs, o, (int)L, (int)Lpad, h_q, \
+                                                    h_kv, g, n_rb, n_bu, sl2, causal)
+  if (d == 128) {
+    if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);
+  } else {
+    if (out_bf16) GQA_LAUNCH(64, true); else GQA_LAUNCH(64, false);
+  }
+#undef GQA_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace gqa

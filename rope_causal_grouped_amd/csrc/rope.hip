@@ -1,0 +1,216 @@
+// RoPE kernels: in-place rotation, the per-call cos/sin table, and the
+// K/V preparation pass that runs ahead of prefill attention.
+//
+// RoPE (Qwen2 technical-report walkthrough, aicoding.csdn.net, §3.5.2 and
+// §4.1.3 step 3): every row of Q and K is rotated at its position, pair by
+// pair, inside the head's d dims.  Pair j couples dims j and j + d/2 and
+// turns by pos * theta^(-2j/d); theta = 1e6 for Qwen2 (same page §5.2).
+
+#include "common.h"
+#include "launch.h"
+
+namespace gqa {
+
+// ---------------------------------------------------------------------------
+// In-place rotation of x[B, L, h, d]; one thread per (row, pair).
+template <typename T>
+__global__ __launch_bounds__(256) void rope_apply_kernel(T* __restrict__ x, int64_t n_pairs, int64_t L,
+                                                         int h, int d, int64_t pos0,
+                                                         double log2_theta) {
+  const int half = d >> 1;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_pairs;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = idx / half;
+    const int j = (int)(idx - row * half);
+    const int64_t l = (row / h) % L;
+    float c, s;
+    rope_cos_sin((double)(pos0 + l), rope_omega(j, d, log2_theta), c, s);
+    T* p = x + row * d;
+    float x1, x2;
+    if constexpr (sizeof(T) == 2) {
+      x1 = bf16_bits_to_f32(p[j]);
+      x2 = bf16_bits_to_f32(p[j + half]);
+    } else {
+      x1 = p[j];
+      x2 = p[j + half];
+    }
+    const float y1 = fmaf(x1, c, -x2 * s);
+    const float y2 = fmaf(x2, c, x1 * s);
+    if constexpr (sizeof(T) == 2) {
+      p[j] = f32_to_bf16_bits(y1);
+      p[j + half] = f32_to_bf16_bits(y2);
+    } else {
+      p[j] = y1;
+      p[j + half] = y2;
+    }
+  }
+}
+
+hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,
+                             double log2_theta, hipStream_t st) {
+  const int64_t n_pairs = B * L * h * (d / 2);
+  const int64_t want = (n_pairs + 255) / 256;
+  const int grid = (int)(want < 65536 ? want : 65536);
+  if (dtype == 1)
+    rope_apply_kernel<uint16_t><<<grid, 256, 0, st>>>((uint16_t*)x, n_pairs, L, h, d, pos0,
+                                                      log2_theta);
+  else
+    rope_apply_kernel<float><<<grid, 256, 0, st>>>((float*)x, n_pairs, L, h, d, pos0, log2_theta);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// cs[l][j] = (cos, sin)(pos(l) * omega_j) for l < L, j < d/2, pos(l) = pos0 + l.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ cs, int64_t n, int d,
+                                                         int64_t pos0, double log2_theta) {
+  const int half = d >> 1;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t l = idx / half;
+    const int j = (int)(idx - l * half);
+    float c, s;
+    rope_cos_sin((double)(pos0 + l), rope_omega(j, d, log2_theta), c, s);
+    cs[idx] = make_float2(c, s);
+  }
+}
+
+hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double log2_theta,
+                             hipStream_t st) {
+  const int64_t n = L * (d / 2);
+  const int64_t want = (n + 255) / 256;
+  const int grid = (int)(want < 65536 ? want : 65536);
+  rope_table_kernel<<<grid, 256, 0, st>>>(cs, n, d, pos0, log2_theta);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// K/V preparation for the bf16 prefill.  One workgroup per (64-key tile,
+// KV group u, batch b):
+//   kp[b][u][key][:]   rotated K, bf16, keys contiguous per group (a 64-key
+//                      tile is one contiguous 16 KB block for d = 128);
+//   vt[b][u][tile][dim][64] V transposed per tile, so the attention kernel's
+//                      P.V operand reads consecutive keys of one dim; inside
+//                      each 16-key group the keys are stored in the order
+//                      0-3, 8-11, 4-7, 12-15, which is the order in which one
+//                      lane of the 32x32 score accumulator holds them.
+// Rows past L are zero.  If kc/vc are set, the rotated K and the V rows are
+// also written to the per-layer cache [B, cap, h_kv, d].
+template <int D>
+__global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float2* __restrict__ cs,
+    uint16_t* __restrict__ kp, uint16_t* __restrict__ vt, uint16_t* __restrict__ kc,
+    uint16_t* __restrict__ vc, int64_t L, int64_t Lpad, int h_kv, int64_t cap) {
+  constexpr int TK = 64;
+  constexpr int HALF = D / 2;
+  __shared__ uint16_t vs[TK][D + 2];
+  const int tile = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
+  const int64_t key0 = (int64_t)tile * TK;
+  uint16_t* kdst = kp + (((int64_t)b * h_kv + u) * Lpad + key0) * D;
+
+  for (int idx = threadIdx.x; idx < TK * HALF; idx += 256) {
+    const int kk = idx / HALF, j = idx % HALF;
+    const int64_t key = key0 + kk;
+    uint16_t o1 = 0, o2 = 0;
+    if (key < L) {
+      const uint16_t* src = k + (((int64_t)b * L + key) * h_kv + u) * D;
+      const float x1 = bf16_bits_to_f32(src[j]);
+      const float x2 = bf16_bits_to_f32(src[j + HALF]);
+      const float2 r = cs[key * HALF + j];
+      o1 = f32_to_bf16_bits(fmaf(x1, r.x, -x2 * r.y));
+      o2 = f32_to_bf16_bits(fmaf(x2, r.x, x1 * r.y));
+      if (kc) {
+        uint16_t* cdst = kc + (((int64_t)b * cap + key) * h_kv + u) * D;
+        cdst[j] = o1;
+        cdst[j + HALF] = o2;
+      }
+    }
+    kdst[kk * D + j] = o1;
+    kdst[kk * D + j + HALF] = o2;
+  }
+
+  for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
+    const int kk = idx / D, dd = idx % D;
+    const int64_t key = key0 + kk;
+    uint16_t val = 0;
+    if (key < L) {
+      const int64_t off = (((int64_t)b * L + key) * h_kv + u) * D + dd;
+      val = v[off];
+      if (vc) vc[(((int64_t)b * cap + key) * h_kv + u) * D + dd] = val;
+    }
+    vs[kk][dd] = val;
+  }
+  __syncthreads();
+
+  uint16_t* vdst = vt + (((int64_t)b * h_kv + u) * (Lpad / TK) + tile) * (int64_t)D * TK;
+  for (int idx = threadIdx.x; idx < D * TK; idx += 256) {
+    const int dd = idx / TK, p = idx % TK;
+    const int pp = p & 15;
+    const int kk = (p & ~15) + ((pp & 7) >> 2) * 8 + (pp >> 3) * 4 + (pp & 3);
+    vdst[idx] = vs[kk][dd];
+  }
+}
+
+// K preparation for the fp32 prefill: kp[b][u][key][:] = rotated K (fp32),
+// optional cache copies of rotated K and V.
+template <int D>
+__global__ __launch_bounds__(256) void kv_prepare_f32_kernel(
+    const float* __restrict__ k, const float* __restrict__ v, const float2* __restrict__ cs,
+    float* __restrict__ kp, float* __restrict__ kc, float* __restrict__ vc, int64_t L, int h_kv,
+    int64_t cap) {
+  constexpr int TK = 64;
+  constexpr int HALF = D / 2;
+  const int tile = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
+  const int64_t key0 = (int64_t)tile * TK;
+  for (int idx = threadIdx.x; idx < TK * HALF; idx += 256) {
+    const int kk = idx / HALF, j = idx % HALF;
+    const int64_t key = key0 + kk;
+    if (key >= L) continue;
+    const float* src = k + (((int64_t)b * L + key) * h_kv + u) * D;
+    const float x1 = src[j], x2 = src[j + HALF];
+    const float2 r = cs[key * HALF + j];
+    const float o1 = fmaf(x1, r.x, -x2 * r.y);
+    const float o2 = fmaf(x2, r.x, x1 * r.y);
+    float* kdst = kp + (((int64_t)b * h_kv + u) * L + key) * D;
+    kdst[j] = o1;
+    kdst[j + HALF] = o2;
+    if (kc) {
+      float* cdst = kc + (((int64_t)b * cap + key) * h_kv + u) * D;
+      cdst[j] = o1;
+      cdst[j + HALF] = o2;
+    }
+  }
+  if (vc) {
+    for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
+      const int kk = idx / D, dd = idx % D;
+      const int64_t key = key0 + kk;
+      if (key >= L) continue;
+      vc[(((int64_t)b * cap + key) * h_kv + u) * D + dd] =
+          v[(((int64_t)b * L + key) * h_kv + u) * D + dd];
+    }
+  }
+}
+
+hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
+                                  uint16_t* kp, uint16_t* vt, uint16_t* kc, uint16_t* vc,
+                                  int64_t B, int64_t L, int64_t Lpad, int h_kv, int d, int64_t cap,
+                                  hipStream_t st) {
+  dim3 grid((unsigned)(Lpad / 64), (unsigned)h_kv, (unsigned)B);
+  if (d == 128)
+    kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kc, vc, L, Lpad, h_kv, cap);
+  else
+    kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kc, vc, L, Lpad, h_kv, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* cs, float* kp,
+                                 float* kc, float* vc, int64_t B, int64_t L, int h_kv, int d,
+                                 int64_t cap, hipStream_t st) {
+  dim3 grid((unsigned)((L + 63) / 64), (unsigned)h_kv, (unsigned)B);
+  if (d == 128)
+    kv_prepare_f32_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, kc, vc, L, h_kv, cap);
+  else
+    kv_prepare_f32_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, kc, vc, L, h_kv, cap);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

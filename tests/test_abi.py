@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gqa.h declares, and rejects bad arguments on the host before any
+HIP call (validation returns before anything is enqueued)."""
+
+import os
+import re
+
+import pytest
+
+from rope_causal_grouped_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+FAKE = 0x10000   # a 16-byte aligned non-NULL address; never dereferenced here
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def test_every_header_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with gqa.h"
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.gqa_version()
+
+
+def prefill_call(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, in_dt=1, out_dt=0, B=1, L=16, h_q=28, h_kv=4,
+             d=128, theta=1e6, scale=0.088, causal=1, kc=None, vc=None, cap=0,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gqa_prefill(a["q"], a["k"], a["v"], a["o"], a["in_dt"], a["out_dt"], a["B"],
+                           a["L"], a["h_q"], a["h_kv"], a["d"], a["theta"], a["scale"],
+                           a["causal"], a["kc"], a["vc"], a["cap"], a["ws"], a["wsb"],
+                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(h_kv=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(h_q=4, h_kv=28), _lib.GQA_ERR_INVALID_ARG),      # ratio written the wrong way round
+    (dict(h_q=28, h_kv=3), _lib.GQA_ERR_INVALID_ARG),      # not a multiple
+    (dict(d=127), _lib.GQA_ERR_INVALID_ARG),               # odd: no RoPE pairs
+    (dict(d=96), _lib.GQA_ERR_UNSUPPORTED),
+    (dict(B=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(L=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(in_dt=7), _lib.GQA_ERR_INVALID_ARG),
+    (dict(theta=float("nan")), _lib.GQA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _lib.GQA_ERR_INVALID_ARG),
+    (dict(kc=FAKE), _lib.GQA_ERR_INVALID_ARG),             # v_cache missing
+    (dict(kc=FAKE, vc=FAKE, cap=8), _lib.GQA_ERR_INVALID_ARG),  # cap < L
+    (dict(o=FAKE + 4), _lib.GQA_ERR_INVALID_ARG),          # misaligned
+    (dict(ws=None), _lib.GQA_ERR_WORKSPACE),
+    (dict(wsb=16), _lib.GQA_ERR_WORKSPACE),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill_call(lib, **kw) == code
+    assert lib.gqa_last_error()
+
+
+def decode_call(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, in_dt=1, out_dt=0, B=2, h_q=28, h_kv=4, d=128,
+             cap=64, kv_len=64, q_pos=64, theta=1e6, scale=0.088, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    return lib.gqa_decode(a["q"], a["kc"], a["vc"], a["o"], a["in_dt"], a["out_dt"], a["B"],
+                          a["h_q"], a["h_kv"], a["d"], a["cap"], a["kv_len"], a["q_pos"],
+                          a["theta"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(kv_len=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(kv_len=65), _lib.GQA_ERR_INVALID_ARG),           # beyond cap
+    (dict(q_pos=10), _lib.GQA_ERR_INVALID_ARG),            # keys after the query
+    (dict(h_q=4, h_kv=28), _lib.GQA_ERR_INVALID_ARG),
+    (dict(d=80), _lib.GQA_ERR_UNSUPPORTED),
+    (dict(wsb=0), _lib.GQA_ERR_WORKSPACE),
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode_call(lib, **kw) == code
+    assert lib.gqa_last_error()
+
+
+def test_rope_rejects(lib):
+    assert lib.gqa_rope_apply(None, 1, 1, 4, 2, 64, 0, 1e6, None) == _lib.GQA_ERR_INVALID_ARG
+    assert lib.gqa_rope_apply(FAKE, 1, 1, 4, 2, 63, 0, 1e6, None) == _lib.GQA_ERR_INVALID_ARG
+    assert lib.gqa_rope_apply(FAKE, 1, 1, 4, 2, 64, -1, 1e6, None) == _lib.GQA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(lib):
+    # bf16 prefill: cos/sin table + rotated K + transposed V (64-key padded)
+    n = lib.gqa_prefill_workspace_size(1, 4, 4096, 4, 128)
+    assert n == 4096 * 64 * 8 + 2 * 4 * 4 * 4096 * 128 * 2
+    assert lib.gqa_prefill_workspace_size(1, 0, 10, 4, 128) == 0
+    # decode: (m, l, o[d]) per (b, group, 1024-key chunk, head)
+    n = lib.gqa_decode_workspace_size(32, 28, 4, 128, 32768)
+    assert n == 32 * 4 * 32 * 7 * (2 + 128) * 4
+    assert lib.gqa_decode_workspace_size(1, 28, 3, 128, 10) == 0
