@@ -7,8 +7,9 @@
 
 namespace gqa {
 
-constexpr int kPrefillTileK = 64;      // keys per K/V tile (bf16 prefill)
-constexpr int kPrefillRowsWG = 256;    // stacked (position, head) rows per workgroup
+constexpr int kPrefillTileK = 64;      // key padding granule of the prepared K/V
+constexpr int kPrefillTileV = 32;      // keys per attention tile; V^T is stored per such tile
+constexpr int kPrefillRowsWG = 128;    // stacked (position, head) rows per workgroup
 constexpr int kDecodeChunk = 1024;     // keys per decode split
 
 hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,

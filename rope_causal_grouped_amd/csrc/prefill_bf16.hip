@@ -10,38 +10,55 @@
 // Work split.  The g query heads of one KV group read the same K and V, so
 // for a fixed (batch b, group u) the rows (position i, head t in the group)
 // form one "stacked" query matrix of L*g rows, ordered position-major; that
-// matrix is contiguous in q (g heads of one position are adjacent).  A
-// workgroup owns 256 consecutive stacked rows (about 256/g positions, all g
+// matrix is contiguous in q (the g heads of one position are adjacent).  A
+// workgroup owns 128 consecutive stacked rows (about 128/g positions, all g
 // heads) and streams the K/V tiles of group u through LDS once for all of
-// them: this is the g-fold K/V reuse GQA offers (same page, closing note of
-// §4.1.3).  Eight waves each own 32 rows.
+// them: the g-fold K/V reuse GQA offers (same page, closing note of §4.1.3).
+// Its four waves own 32 rows each.  Two workgroups share a CU, so the two
+// waves on each SIMD come from different workgroups, are not tied by a
+// common barrier, and overlap one's matrix-core phase with the other's
+// softmax.
 //
-// Per 64-key tile, each wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the wave's rotated
-// Q rows resident in VGPRs as the B operand), so every lane holds one query
-// row's scores and the row max needs a single exchange with lane ^ 32.  The
-// probabilities, rounded to bf16, are already in the B-operand layout of
-// O^T += V^T P^T; V arrives pre-transposed (keys contiguous, in the lane
-// order of the accumulator) from the preparation pass.
+// Per 64-key tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// (K from LDS as the A operand, the wave's rotated Q rows resident in VGPRs
+// as the B operand), so each lane holds one query row's scores and the row
+// max needs one exchange with lane ^ 32.  The probabilities, rounded to
+// bf16, are already in the B-operand layout of O^T += V^T P^T; V arrives
+// pre-transposed (keys contiguous, in the accumulator's lane order) from the
+// preparation pass, in 32-key sub-tiles.
+//
+// The running max is raised only when a row's max grows by more than 2^8
+// (exp2 units): probabilities then stay <= 256, exact enough in bf16 and far
+// from fp32 overflow, and the O rescale is skipped on almost every tile.
 
 #include "common.h"
 #include "launch.h"
 
 namespace gqa {
 
+namespace {
+
+constexpr int TK = 64;                      // keys per tile
+constexpr int TV = kPrefillTileV;           // keys per prepared V^T sub-tile (32)
+constexpr int NW = 4;                       // waves per workgroup
+constexpr int RW = 32;                      // rows per wave
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
+
+}  // namespace
+
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(512) void prefill_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vt, const float2* __restrict__ cs, void* __restrict__ o, int L,
     int Lpad, int h_q, int h_kv, int g, int n_rb, int n_bu, float sl2, int causal) {
-  constexpr int TK = 64;          // keys per tile
-  constexpr int KP = D + 8;       // LDS pitch (elements) of a K row: +16 B against bank conflicts
-  constexpr int VP = TK + 8;      // LDS pitch of a V^T row
-  constexpr int NS = D / 16;      // k-steps of 16 dims for S^T
-  constexpr int NDB = D / 32;     // 32-dim blocks of O^T
-  constexpr int CPT = TK * D / 8 / 512;   // 16-byte chunks per thread per tile
+  constexpr int KP = D + 8;                   // LDS pitch of a K row (+16 B: no bank conflicts)
+  constexpr int VP = TV + 8;                  // LDS pitch of a V^T row (+16 B)
+  constexpr int NS = D / 16;                  // 16-dim k-steps of S^T
+  constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
+  constexpr int CPT = TK * D / 8 / (NW * 64); // 16-byte chunks per thread per tile
+  constexpr int ROWS = NW * RW;
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][TK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][D * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][TK / TV][D * VP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -54,18 +71,18 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(
   const int b = bu / h_kv, u = bu % h_kv;
 
   const int rows_total = L * g;
-  const int R0 = rb * 256;
-  const int r = R0 + wave * 32 + c32;
-  const bool row_valid = r < rows_total;
-  const int rr = row_valid ? r : rows_total - 1;
+  const int R0 = rb * ROWS;
+  const int row = R0 + wave * RW + c32;
+  const bool row_valid = row < rows_total;
+  const int rr = row_valid ? row : rows_total - 1;
   const int pos = rr / g;
-  const int t = u * g + (rr - pos * g);
+  const int head = u * g + (rr - pos * g);
 
-  // ---- Q rows: load, rotate at `pos`, round to bf16 (B operand layout:
-  // lane holds dims s*16 + hl*8 + e of its row; pairs (s, s + NS/2)).
+  // ---- Q row: load, rotate at pos, round to bf16 (B operand layout: lane
+  // holds dims s*16 + hl*8 + e of its row; RoPE pairs are (s, s + NS/2)).
   bf16x8 qb[NS];
   {
-    const uint16_t* qrow = q + ((int64_t)((int64_t)b * L + pos) * h_q + t) * D;
+    const uint16_t* qrow = q + ((int64_t)((int64_t)b * L + pos) * h_q + head) * D;
     u32x4 raw[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) raw[s] = *(const u32x4*)(qrow + s * 16 + hl * 8);
@@ -85,12 +102,13 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(
   }
 
   // ---- key range
-  const int rmax = min(R0 + 255, rows_total - 1);
+  const int rmax = min(R0 + ROWS - 1, rows_total - 1);
   const int n_keys = causal ? rmax / g + 1 : L;
   const int n_tiles = (n_keys + TK - 1) / TK;
-  const int wr0 = min(R0 + wave * 32, rows_total - 1);
-  const int wr1 = min(R0 + wave * 32 + 31, rows_total - 1);
+  const int wr0 = min(R0 + wave * RW, rows_total - 1);
+  const int wr1 = min(R0 + wave * RW + RW - 1, rows_total - 1);
   const int wpos_lo = wr0 / g, wpos_hi = wr1 / g;
+  const int lim = causal ? min(pos, L - 1) : L - 1;   // last key this row may see
 
   const uint16_t* kbase = kp + (int64_t)bu * Lpad * D;
   const uint16_t* vbase = vt + (int64_t)bu * Lpad * D;
@@ -101,7 +119,7 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(
     const uint16_t* vsrc = vbase + (int64_t)tile * TK * D;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 512;
+      const int ch = tid + c * NW * 64;
       kreg[c] = *(const u32x4*)(ksrc + ch * 8);
       vreg[c] = *(const u32x4*)(vsrc + ch * 8);
     }
@@ -109,9 +127,11 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 512;
+      const int ch = tid + c * NW * 64;
       *(u32x4*)&ks[buf][(ch / (D / 8)) * KP + (ch % (D / 8)) * 8] = kreg[c];
-      *(u32x4*)&vs[buf][(ch / 8) * VP + (ch % 8) * 8] = vreg[c];
+      // V^T sub-tile ch / (D*TV/8), row (dim) and 8-key column inside it
+      const int sub = ch / (D * TV / 8), rem = ch % (D * TV / 8);
+      *(u32x4*)&vs[buf][sub][(rem / (TV / 8)) * VP + (rem % (TV / 8)) * 8] = vreg[c];
     }
   };
 
@@ -131,23 +151,22 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(
     if (kt + 1 < n_tiles) gload(kt + 1);
     const int k0 = kt * TK;
     if (!causal || k0 <= wpos_hi) {
-      // ---- S^T = K Q^T for two 32-key blocks
+      // ---- S^T = K Q^T for two 32-key blocks (independent MFMA chains)
       f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-        const uint16_t* krow = &ks[buf][(kb * 32 + c32) * KP + hl * 8];
+      const uint16_t* krow = &ks[buf][c32 * KP + hl * 8];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 a = *(const bf16x8*)(krow + s * 16);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[s], sacc[kb], 0, 0, 0);
-        }
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a0 = *(const bf16x8*)(krow + s * 16);
+        const bf16x8 a1 = *(const bf16x8*)(krow + 32 * KP + s * 16);
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[s], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[s], sacc[1], 0, 0, 0);
       }
       // ---- causal / tail mask (only tiles that reach past the wave's first row)
-      const bool need_mask = (causal && k0 + TK - 1 > wpos_lo) || (k0 + TK > L);
-      if (need_mask) {
-        const int lim = causal ? min(pos, L - 1) : L - 1;
+      if ((causal && k0 + TK - 1 > wpos_lo) || (k0 + TK > L)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -156,43 +175,49 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(
             if (key > lim) sacc[kb][i] = -INFINITY;
           }
       }
-      // ---- online softmax (log2 domain)
-      float mx = sacc[0][0];
+      // ---- row max; raise the running max only past the threshold
+      float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
+      mx = max_xor32(mx) * sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+        for (int db = 0; db < NDB; ++db) {
+          // keep the accumulators in AGPRs outside this rare branch
+          asm volatile("" : "+a"(oacc[db]));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+          asm volatile("" : "+a"(oacc[db]));
+        }
+      }
+      // ---- probabilities (bf16, B operand of P.V) and their fp32 row sum
       bf16x8 pb[2][2];
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, -m_new));
-          const __bf16 pbf = (__bf16)p;
-          pb[kb][i >> 3][i & 7] = pbf;
-          psum += (float)pbf;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, -m_run));
+          pb[kb][i >> 3][i & 7] = (__bf16)p;
+          psum += p;
         }
-      l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      l_run += psum;
       // ---- O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vrow = &vs[buf][(db * 32 + c32) * VP + hl * 8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint16_t* vrow = &vs[buf][kb][(db * 32 + c32) * VP + hl * 8];
 #pragma unroll
           for (int hs = 0; hs < 2; ++hs) {
-            const bf16x8 a = *(const bf16x8*)(vrow + kb * 32 + hs * 16);
+            const bf16x8 a = *(const bf16x8*)(vrow + hs * 16);
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][hs], oacc[db], 0, 0, 0);
           }
+        }
       }
     }
     if (kt + 1 < n_tiles) lstore(buf ^ 1);
@@ -200,10 +225,9 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(
   }
 
   // ---- epilogue: O = O / l; lane holds dims db*32 + grp*8 + hl*4 + (0..3)
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
+  const float inv = 1.0f / sum_xor32(l_run);
   if (row_valid) {
-    const int64_t orow = ((int64_t)((int64_t)b * L + pos) * h_q + t) * D;
+    const int64_t orow = ((int64_t)((int64_t)b * L + pos) * h_q + head) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -234,8 +258,8 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e): exp(x) = exp2(x log2 e)
   const unsigned grid = (unsigned)((int64_t)n_rb * n_bu);
 #define GQA_LAUNCH(DD, OB)                                                                    \
-  prefill_bf16_kernel<DD, OB><<<grid, 512, 0, st>>>(q, kp, vt, cs, o, (int)L, (int)Lpad, h_q, \
-                                                    h_kv, g, n_rb, n_bu, sl2, causal)
+  prefill_bf16_kernel<DD, OB><<<grid, NW * 64, 0, st>>>(q, kp, vt, cs, o, (int)L, (int)Lpad, \
+                                                        h_q, h_kv, g, n_rb, n_bu, sl2, causal)
   if (d == 128) {
     if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);
   } else {

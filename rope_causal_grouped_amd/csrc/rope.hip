@@ -88,11 +88,12 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double 
 // KV group u, batch b):
 //   kp[b][u][key][:]   rotated K, bf16, keys contiguous per group (a 64-key
 //                      tile is one contiguous 16 KB block for d = 128);
-//   vt[b][u][tile][dim][64] V transposed per tile, so the attention kernel's
-//                      P.V operand reads consecutive keys of one dim; inside
-//                      each 16-key group the keys are stored in the order
-//                      0-3, 8-11, 4-7, 12-15, which is the order in which one
-//                      lane of the 32x32 score accumulator holds them.
+//   vt[b][u][t32][dim][32] V transposed per 32-key attention tile, so the
+//                      attention kernel's P.V operand reads consecutive keys
+//                      of one dim; inside each 16-key group the keys are
+//                      stored in the order 0-3, 8-11, 4-7, 12-15, which is
+//                      the order in which one lane of the 32x32 score
+//                      accumulator holds them.
 // Rows past L are zero.  If kc/vc are set, the rotated K and the V rows are
 // also written to the per-layer cache [B, cap, h_kv, d].
 template <int D>
@@ -141,11 +142,14 @@ __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
   }
   __syncthreads();
 
-  uint16_t* vdst = vt + (((int64_t)b * h_kv + u) * (Lpad / TK) + tile) * (int64_t)D * TK;
+  // V^T in tiles of TV keys: vt[b][u][key / TV][dim][TV]
+  constexpr int TV = kPrefillTileV;
+  uint16_t* vdst = vt + (((int64_t)b * h_kv + u) * Lpad + key0) * D;
   for (int idx = threadIdx.x; idx < D * TK; idx += 256) {
-    const int dd = idx / TK, p = idx % TK;
+    const int sub = idx / (D * TV), rem = idx % (D * TV);
+    const int dd = rem / TV, p = rem % TV;
     const int pp = p & 15;
-    const int kk = (p & ~15) + ((pp & 7) >> 2) * 8 + (pp >> 3) * 4 + (pp & 3);
+    const int kk = sub * TV + (p & ~15) + ((pp & 7) >> 2) * 8 + (pp >> 3) * 4 + (pp & 3);
     vdst[idx] = vs[kk][dd];
   }
 }
