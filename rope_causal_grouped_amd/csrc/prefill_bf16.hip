@@ -27,6 +27,13 @@
 // pre-transposed (keys contiguous, in the accumulator's lane order) from the
 // preparation pass, in 32-key sub-tiles.
 //
+// K and V^T tiles go from HBM straight into LDS (global_load_lds_dwordx4,
+// no staging registers).  That instruction writes 16 bytes per lane at
+// consecutive LDS addresses, so the tiles are stored unpadded and bank
+// conflicts are avoided instead by XOR-swizzling the 16-byte chunk index of
+// each row with bits of the row index; the operand reads apply the same
+// swizzle.
+//
 // The running max is raised only when a row's max grows by more than 2^8
 // (exp2 units): probabilities then stay <= 256, exact enough in bf16 and far
 // from fp32 overflow, and the O rescale is skipped on almost every tile.
@@ -51,14 +58,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vt, const float2* __restrict__ cs, void* __restrict__ o, int L,
     int Lpad, int h_q, int h_kv, int g, int n_rb, int n_bu, float sl2, int causal) {
-  constexpr int KP = D + 8;                   // LDS pitch of a K row (+16 B: no bank conflicts)
-  constexpr int VP = TV + 8;                  // LDS pitch of a V^T row (+16 B)
   constexpr int NS = D / 16;                  // 16-dim k-steps of S^T
   constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
-  constexpr int CPT = TK * D / 8 / (NW * 64); // 16-byte chunks per thread per tile
   constexpr int ROWS = NW * RW;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][TK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][TK / TV][D * VP];
+  // tile geometry in 16-byte chunks
+  constexpr int KCPR = D / 8;                 // chunks per K row (16 for d = 128)
+  constexpr int KRPB = KCPR >= 16 ? 1 : 16 / KCPR;   // K rows per 256 bytes
+  constexpr int VCPR = TV / 8;                // chunks per V^T row (4)
+  constexpr int VRPB = 16 / VCPR;             // V^T rows per 256 bytes
+  constexpr int TILE_CH = TK * D / 8;         // chunks per K (or V^T) tile
+  constexpr int LPW = TILE_CH / 64 / NW;      // direct loads per wave per tile and tensor
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][TK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][TK * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -110,30 +121,52 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   const int wpos_lo = wr0 / g, wpos_hi = wr1 / g;
   const int lim = causal ? min(pos, L - 1) : L - 1;   // last key this row may see
 
+  // ---- direct HBM -> LDS tile loads.  Instruction i of wave w fills LDS
+  // chunks [(w*LPW + i)*64, +64); lane l's chunk P sits at row P / CPR,
+  // physical slot P % CPR, and holds logical chunk slot ^ swizzle(row).
   const uint16_t* kbase = kp + (int64_t)bu * Lpad * D;
   const uint16_t* vbase = vt + (int64_t)bu * Lpad * D;
+  int koff[LPW], voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int P = (wave * LPW + i) * 64 + lane;
+    const int kr = P / KCPR, kslot = P % KCPR;
+    koff[i] = kr * D + ((kslot ^ ((kr / KRPB) % KCPR)) * 8);
+    const int sub = P / (D * VCPR), rem = P % (D * VCPR);
+    const int vr = rem / VCPR, vslot = rem % VCPR;
+    voff[i] = sub * D * TV + vr * TV + ((vslot ^ ((vr / VRPB) % VCPR)) * 8);
+  }
+  // load n of the 2*LPW direct loads a wave issues per tile (K first, then V)
+  auto issue_one = [&](int n, int tile, int buf) {
+    const int i = n % LPW;
+    const int dst = (wave * LPW + i) * 64 * 8;
+    if (n < LPW)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(kbase + (int64_t)tile * TK * D + koff[i]),
+          (void __attribute__((address_space(3)))*)&ks[buf][dst], 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(vbase + (int64_t)tile * TK * D + voff[i]),
+          (void __attribute__((address_space(3)))*)&vs[buf][dst], 16, 0, 0);
+  };
+  auto issue_tile = [&](int tile, int buf) {
+#pragma unroll
+    for (int n = 0; n < 2 * LPW; ++n) issue_one(n, tile, buf);
+  };
+  auto tile_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // next tile to prefetch; past the last tile the last one is loaded again
+  // into the idle buffer (harmless), which keeps the loop body uniform
+  auto next_tile = [&](int kt) { return min(kt + 1, n_tiles - 1); };
 
-  u32x4 kreg[CPT], vreg[CPT];
-  auto gload = [&](int tile) {
-    const uint16_t* ksrc = kbase + (int64_t)tile * TK * D;
-    const uint16_t* vsrc = vbase + (int64_t)tile * TK * D;
+  // ---- operand read offsets (elements), swizzled like the stores
+  const int kswz = (c32 / KRPB) % KCPR;       // same for key rows c32 and 32 + c32
+  int kread[NS];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NW * 64;
-      kreg[c] = *(const u32x4*)(ksrc + ch * 8);
-      vreg[c] = *(const u32x4*)(vsrc + ch * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
+  for (int s = 0; s < NS; ++s) kread[s] = c32 * D + (((2 * s + hl) ^ kswz) * 8);
+  const int vswz = (c32 / VRPB) % VCPR;       // same for dim rows db*32 + c32
+  int vread[2];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NW * 64;
-      *(u32x4*)&ks[buf][(ch / (D / 8)) * KP + (ch % (D / 8)) * 8] = kreg[c];
-      // V^T sub-tile ch / (D*TV/8), row (dim) and 8-key column inside it
-      const int sub = ch / (D * TV / 8), rem = ch % (D * TV / 8);
-      *(u32x4*)&vs[buf][sub][(rem / (TV / 8)) * VP + (rem % (TV / 8)) * 8] = vreg[c];
-    }
-  };
+  for (int hs = 0; hs < 2; ++hs) vread[hs] = c32 * TV + (((2 * hs + hl) ^ vswz) * 8);
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -142,26 +175,26 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  gload(0);
-  lstore(0);
+  issue_tile(0, 0);
+  tile_landed();
   __syncthreads();
 
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_tiles) gload(kt + 1);
     const int k0 = kt * TK;
     if (!causal || k0 <= wpos_hi) {
+      issue_tile(next_tile(kt), buf ^ 1);
       // ---- S^T = K Q^T for two 32-key blocks (independent MFMA chains)
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const uint16_t* krow = &ks[buf][c32 * KP + hl * 8];
+      const uint16_t* kt0 = ks[buf];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const bf16x8 a0 = *(const bf16x8*)(krow + s * 16);
-        const bf16x8 a1 = *(const bf16x8*)(krow + 32 * KP + s * 16);
+        const bf16x8 a0 = *(const bf16x8*)(kt0 + kread[s]);
+        const bf16x8 a1 = *(const bf16x8*)(kt0 + 32 * D + kread[s]);
         sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[s], sacc[0], 0, 0, 0);
         sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[s], sacc[1], 0, 0, 0);
       }
@@ -206,21 +239,21 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
           psum += p;
         }
       l_run += psum;
-      // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T: per 16-key step, one MFMA per 32-dim block
+      const uint16_t* vt0 = vs[buf];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint16_t* vrow = &vs[buf][kb][(db * 32 + c32) * VP + hl * 8];
+        for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
-            const bf16x8 a = *(const bf16x8*)(vrow + hs * 16);
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x8 a = *(const bf16x8*)(vt0 + kb * D * TV + db * 32 * TV + vread[hs]);
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][hs], oacc[db], 0, 0, 0);
           }
-        }
-      }
+    } else {
+      issue_tile(next_tile(kt), buf ^ 1);
     }
-    if (kt + 1 < n_tiles) lstore(buf ^ 1);
+    tile_landed();
     __syncthreads();
   }
 
