@@ -92,7 +92,7 @@ int64_t prefill_lpad(int64_t L) { return (L + gqa::kPrefillTileK - 1) / gqa::kPr
 
 // workspace pieces of gqa_prefill
 struct PrefillWs {
-  size_t cs_off, kp_off, vt_off, total;
+  size_t cs_off, kp_off, vt_off, kmax_off, total;
 };
 
 PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
@@ -103,10 +103,12 @@ PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
   if (in_dtype == GQA_BF16) {
     const size_t kp = align256((size_t)B * h_kv * prefill_lpad(L) * d * 2);
     w.vt_off = cs + kp;
-    w.total = cs + 2 * kp;
+    w.kmax_off = cs + 2 * kp;
+    w.total = w.kmax_off + align256((size_t)B * h_kv * (prefill_lpad(L) / gqa::kPrefillTileK) * 4);
   } else {
     const size_t kp = align256((size_t)B * h_kv * L * d * 4);
     w.vt_off = cs + kp;
+    w.kmax_off = cs + kp;
     w.total = cs + kp;
   }
   return w;
@@ -197,12 +199,13 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     const int64_t Lpad = prefill_lpad(L);
     uint16_t* kp = (uint16_t*)(wsb + ws.kp_off);
     uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
-    e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, cs, kp, vt,
+    float* kmax = (float*)(wsb + ws.kmax_off);
+    e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, cs, kp, vt, kmax,
                                     (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad, h_kv, d,
                                     cap, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     if (ev.first) (void)hipEventRecord(ev.first, st);
-    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, cs, o, out_dtype == GQA_BF16, B, L,
+    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, cs, o, out_dtype == GQA_BF16, B, L,
                                  Lpad, h_q, h_kv, d, scale, causal, st);
   } else {
     float* kp = (float*)(wsb + ws.kp_off);

@@ -19,16 +19,16 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double 
                              hipStream_t st);
 
 hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
-                                  uint16_t* kp, uint16_t* vt, uint16_t* kc, uint16_t* vc,
-                                  int64_t B, int64_t L, int64_t Lpad, int h_kv, int d, int64_t cap,
-                                  hipStream_t st);
+                                  uint16_t* kp, uint16_t* vt, float* kmax, uint16_t* kc,
+                                  uint16_t* vc, int64_t B, int64_t L, int64_t Lpad, int h_kv, int d,
+                                  int64_t cap, hipStream_t st);
 
 hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* cs, float* kp,
                                  float* kc, float* vc, int64_t B, int64_t L, int h_kv, int d,
                                  int64_t cap, hipStream_t st);
 
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
-                               const float2* cs, void* o, int out_bf16, int64_t B, int64_t L,
+                               const float* kmax, const float2* cs, void* o, int out_bf16, int64_t B, int64_t L,
                                int64_t Lpad, int h_q, int h_kv, int d, float scale, int causal,
                                hipStream_t st);
 

@@ -37,6 +37,14 @@
 // The running max is raised only when a row's max grows by more than 2^8
 // (exp2 units): probabilities then stay <= 256, exact enough in bf16 and far
 // from fp32 overflow, and the O rescale is skipped on almost every tile.
+// Waiting for a tile's max before the exponentials would serialise each
+// tile, so on the common path the probabilities are formed against the
+// running max straight away; that is safe when |q'| * max|k'| over the tile
+// (the preparation pass stores max|k'| per 64-key tile) is within 2^64 of
+// the running max.  The tile max is then taken alongside P.V, and if it
+// grew past the threshold, O and l (which already hold this tile) are
+// rescaled together.  The first tile, the diagonal (masked) tiles and tiles
+// that fail the bound take the max-first path.
 
 #include "common.h"
 #include "launch.h"
@@ -50,13 +58,15 @@ constexpr int TV = kPrefillTileV;           // keys per prepared V^T sub-tile (3
 constexpr int NW = 4;                       // waves per workgroup
 constexpr int RW = 32;                      // rows per wave
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
+constexpr float kStaleMaxHeadroom = 64.0f;  // log2 units: p <= 2^64 against a stale max
 
 }  // namespace
 
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
-    const uint16_t* __restrict__ vt, const float2* __restrict__ cs, void* __restrict__ o, int L,
+    const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
+    const float2* __restrict__ cs, void* __restrict__ o, int L,
     int Lpad, int h_q, int h_kv, int g, int n_rb, int n_bu, float sl2, int causal) {
   constexpr int NS = D / 16;                  // 16-dim k-steps of S^T
   constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
@@ -111,6 +121,22 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
       }
     }
   }
+  // |q'| of the row (from the bf16 values the matrix cores see), times the
+  // score scale: |q'| * max|k'| bounds every score of a tile (Cauchy-Schwarz;
+  // the rotation keeps norms), with a small margin for fp32 rounding
+  float qcap;
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)qb[s][e];
+        ss = fmaf(x, x, ss);
+      }
+    qcap = sqrtf(sum_xor32(ss)) * sl2 * 1.01f;
+  }
+  const float* kmax_bu = kmax + (int64_t)bu * (Lpad / TK);
 
   // ---- key range
   const int rmax = min(R0 + ROWS - 1, rows_total - 1);
@@ -175,6 +201,66 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  // S^T = K Q^T for two 32-key blocks (independent MFMA chains)
+  auto qk = [&](f32x16 (&sacc)[2], int buf) {
+    const uint16_t* kt0 = ks[buf];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a0 = *(const bf16x8*)(kt0 + kread[s]);
+      const bf16x8 a1 = *(const bf16x8*)(kt0 + 32 * D + kread[s]);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[s], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[s], sacc[1], 0, 0, 0);
+    }
+  };
+  // row max of a tile's scores (exp2 units)
+  auto tile_max = [&](const f32x16 (&sacc)[2]) {
+    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
+    return max_xor32(mx) * sl2;
+  };
+  auto rescale = [&](float mx) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      // keep the accumulators in AGPRs outside this rare branch
+      asm volatile("" : "+a"(oacc[db]));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      asm volatile("" : "+a"(oacc[db]));
+    }
+  };
+  // probabilities against the running max (bf16, B operand of P.V); returns
+  // their fp32 sum
+  auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, -m_run));
+        pb[kb][i >> 3][i & 7] = (__bf16)p;
+        psum += p;
+      }
+    return psum;
+  };
+  // O^T += V^T P^T: per 16-key step, one MFMA per 32-dim block
+  auto pv = [&](const bf16x8 (&pb)[2][2], int buf) {
+    const uint16_t* vt0 = vs[buf];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 a = *(const bf16x8*)(vt0 + kb * D * TV + db * 32 * TV + vread[hs]);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][hs], oacc[db], 0, 0, 0);
+        }
+  };
+
   issue_tile(0, 0);
   tile_landed();
   __syncthreads();
@@ -182,24 +268,20 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
     const int k0 = kt * TK;
+    issue_tile(next_tile(kt), buf ^ 1);
     if (!causal || k0 <= wpos_hi) {
-      issue_tile(next_tile(kt), buf ^ 1);
-      // ---- S^T = K Q^T for two 32-key blocks (independent MFMA chains)
+      const bool masked = (causal && k0 + TK - 1 > wpos_lo) || (k0 + TK > L);
+      // fast path: no mask on this tile and every score provably within the
+      // headroom of the running max, so P can be formed before the tile max
+      const bool fast = !masked && !__builtin_amdgcn_ballot_w64(
+                                       qcap * kmax_bu[kt] > m_run + kStaleMaxHeadroom);
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const uint16_t* kt0 = ks[buf];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 a0 = *(const bf16x8*)(kt0 + kread[s]);
-        const bf16x8 a1 = *(const bf16x8*)(kt0 + 32 * D + kread[s]);
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[s], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[s], sacc[1], 0, 0, 0);
-      }
-      // ---- causal / tail mask (only tiles that reach past the wave's first row)
-      if ((causal && k0 + TK - 1 > wpos_lo) || (k0 + TK > L)) {
+      qk(sacc, buf);
+      if (masked) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -208,50 +290,17 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
             if (key > lim) sacc[kb][i] = -INFINITY;
           }
       }
-      // ---- row max; raise the running max only past the threshold
-      float mx = fmaxf(sacc[0][0], sacc[1][0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
-      mx = max_xor32(mx) * sl2;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          // keep the accumulators in AGPRs outside this rare branch
-          asm volatile("" : "+a"(oacc[db]));
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-          asm volatile("" : "+a"(oacc[db]));
-        }
+      if (!fast) {   // max first
+        const float mx = tile_max(sacc);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) rescale(mx);
       }
-      // ---- probabilities (bf16, B operand of P.V) and their fp32 row sum
       bf16x8 pb[2][2];
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, -m_run));
-          pb[kb][i >> 3][i & 7] = (__bf16)p;
-          psum += p;
-        }
-      l_run += psum;
-      // ---- O^T += V^T P^T: per 16-key step, one MFMA per 32-dim block
-      const uint16_t* vt0 = vs[buf];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const bf16x8 a = *(const bf16x8*)(vt0 + kb * D * TV + db * 32 * TV + vread[hs]);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][hs], oacc[db], 0, 0, 0);
-          }
-    } else {
-      issue_tile(next_tile(kt), buf ^ 1);
+      l_run += probs(sacc, pb);
+      pv(pb, buf);
+      if (fast) {    // the tile max off the critical path; rescale what holds it
+        const float mx = tile_max(sacc);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) rescale(mx);
+      }
     }
     tile_landed();
     __syncthreads();
@@ -282,7 +331,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
 }
 
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
-                               const float2* cs, void* o, int out_bf16, int64_t B, int64_t L,
+                               const float* kmax, const float2* cs, void* o, int out_bf16, int64_t B, int64_t L,
                                int64_t Lpad, int h_q, int h_kv, int d, float scale, int causal,
                                hipStream_t st) {
   const int g = h_q / h_kv;
@@ -291,7 +340,7 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e): exp(x) = exp2(x log2 e)
   const unsigned grid = (unsigned)((int64_t)n_rb * n_bu);
 #define GQA_LAUNCH(DD, OB)                                                                    \
-  prefill_bf16_kernel<DD, OB><<<grid, NW * 64, 0, st>>>(q, kp, vt, cs, o, (int)L, (int)Lpad, \
+  prefill_bf16_kernel<DD, OB><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, cs, o, (int)L, (int)Lpad, \
                                                         h_q, h_kv, g, n_rb, n_bu, sl2, causal)
   if (d == 128) {
     if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);

@@ -88,6 +88,8 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double 
 // KV group u, batch b):
 //   kp[b][u][key][:]   rotated K, bf16, keys contiguous per group (a 64-key
 //                      tile is one contiguous 16 KB block for d = 128);
+//   kmax[b][u][tile]   the largest rotated-K row norm of the tile (an upper
+//                      bound on its scores for a given query norm);
 //   vt[b][u][t32][dim][32] V transposed per 32-key attention tile, so the
 //                      attention kernel's P.V operand reads consecutive keys
 //                      of one dim; inside each 16-key group the keys are
@@ -99,58 +101,99 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double 
 template <int D>
 __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float2* __restrict__ cs,
-    uint16_t* __restrict__ kp, uint16_t* __restrict__ vt, uint16_t* __restrict__ kc,
-    uint16_t* __restrict__ vc, int64_t L, int64_t Lpad, int h_kv, int64_t cap) {
+    uint16_t* __restrict__ kp, uint16_t* __restrict__ vt, float* __restrict__ kmax,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t L, int64_t Lpad, int h_kv,
+    int64_t cap) {
   constexpr int TK = 64;
   constexpr int HALF = D / 2;
-  __shared__ uint16_t vs[TK][D + 2];
+  constexpr int PP = HALF / 4;        // RoPE pairs per thread: 4 threads per key row
+  constexpr int TV = kPrefillTileV;
+  __shared__ __attribute__((aligned(16))) uint16_t vs[TK][D + 8];
+  __shared__ float wmax[4];
   const int tile = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
   const int64_t key0 = (int64_t)tile * TK;
-  uint16_t* kdst = kp + (((int64_t)b * h_kv + u) * Lpad + key0) * D;
 
-  for (int idx = threadIdx.x; idx < TK * HALF; idx += 256) {
-    const int kk = idx / HALF, j = idx % HALF;
+  // ---- K: thread (row tid/4, quarter tid%4) rotates pairs q*PP .. q*PP+PP-1
+  {
+    const int kk = tid >> 2, part = tid & 3;
     const int64_t key = key0 + kk;
-    uint16_t o1 = 0, o2 = 0;
+    uint16_t o1[PP], o2[PP];
+    float ss = 0.f;
     if (key < L) {
-      const uint16_t* src = k + (((int64_t)b * L + key) * h_kv + u) * D;
-      const float x1 = bf16_bits_to_f32(src[j]);
-      const float x2 = bf16_bits_to_f32(src[j + HALF]);
-      const float2 r = cs[key * HALF + j];
-      o1 = f32_to_bf16_bits(fmaf(x1, r.x, -x2 * r.y));
-      o2 = f32_to_bf16_bits(fmaf(x2, r.x, x1 * r.y));
-      if (kc) {
-        uint16_t* cdst = kc + (((int64_t)b * cap + key) * h_kv + u) * D;
-        cdst[j] = o1;
-        cdst[j + HALF] = o2;
+      const uint16_t* src = k + (((int64_t)b * L + key) * h_kv + u) * D + part * PP;
+      uint16_t x1[PP], x2[PP];
+#pragma unroll
+      for (int c = 0; c < PP / 8; ++c) {
+        *(u32x4*)&x1[c * 8] = *(const u32x4*)(src + c * 8);
+        *(u32x4*)&x2[c * 8] = *(const u32x4*)(src + HALF + c * 8);
       }
+      const float2* csr = cs + key * HALF + part * PP;
+#pragma unroll
+      for (int e = 0; e < PP; ++e) {
+        const float2 r = csr[e];
+        const float a = bf16_bits_to_f32(x1[e]), bb = bf16_bits_to_f32(x2[e]);
+        o1[e] = f32_to_bf16_bits(fmaf(a, r.x, -bb * r.y));
+        o2[e] = f32_to_bf16_bits(fmaf(bb, r.x, a * r.y));
+        const float y1 = bf16_bits_to_f32(o1[e]), y2 = bf16_bits_to_f32(o2[e]);
+        ss = fmaf(y1, y1, fmaf(y2, y2, ss));
+      }
+      if (kc) {
+        uint16_t* cdst = kc + (((int64_t)b * cap + key) * h_kv + u) * D + part * PP;
+#pragma unroll
+        for (int c = 0; c < PP / 8; ++c) {
+          *(u32x4*)(cdst + c * 8) = *(const u32x4*)&o1[c * 8];
+          *(u32x4*)(cdst + HALF + c * 8) = *(const u32x4*)&o2[c * 8];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PP; ++e) o1[e] = o2[e] = 0;
     }
-    kdst[kk * D + j] = o1;
-    kdst[kk * D + j + HALF] = o2;
+    uint16_t* kdst = kp + (((int64_t)b * h_kv + u) * Lpad + key) * D + part * PP;
+#pragma unroll
+    for (int c = 0; c < PP / 8; ++c) {
+      *(u32x4*)(kdst + c * 8) = *(const u32x4*)&o1[c * 8];
+      *(u32x4*)(kdst + HALF + c * 8) = *(const u32x4*)&o2[c * 8];
+    }
+    // squared row norm (4 threads per row), then the max over the tile's rows
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+#pragma unroll
+    for (int m = 4; m < 64; m <<= 1) ss = fmaxf(ss, __shfl_xor(ss, m, 64));
+    if ((tid & 63) == 0) wmax[tid >> 6] = ss;
   }
 
-  for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
-    const int kk = idx / D, dd = idx % D;
+  // ---- V rows into LDS (and the cache copy), 16 bytes per thread and step
+  for (int c = tid; c < TK * D / 8; c += 256) {
+    const int kk = c / (D / 8), c8 = c % (D / 8);
     const int64_t key = key0 + kk;
-    uint16_t val = 0;
+    u32x4 val = {0u, 0u, 0u, 0u};
     if (key < L) {
-      const int64_t off = (((int64_t)b * L + key) * h_kv + u) * D + dd;
-      val = v[off];
-      if (vc) vc[(((int64_t)b * cap + key) * h_kv + u) * D + dd] = val;
+      val = *(const u32x4*)(v + (((int64_t)b * L + key) * h_kv + u) * D + c8 * 8);
+      if (vc) *(u32x4*)(vc + (((int64_t)b * cap + key) * h_kv + u) * D + c8 * 8) = val;
     }
-    vs[kk][dd] = val;
+    *(u32x4*)&vs[kk][c8 * 8] = val;
   }
   __syncthreads();
+  if (tid == 0)
+    kmax[((int64_t)b * h_kv + u) * (Lpad / TK) + tile] =
+        sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
 
-  // V^T in tiles of TV keys: vt[b][u][key / TV][dim][TV]
-  constexpr int TV = kPrefillTileV;
+  // ---- V^T in tiles of TV keys: vt[b][u][key / TV][dim][TV]; each thread
+  // writes 8 consecutive (permuted) keys of one dim
   uint16_t* vdst = vt + (((int64_t)b * h_kv + u) * Lpad + key0) * D;
-  for (int idx = threadIdx.x; idx < D * TK; idx += 256) {
-    const int sub = idx / (D * TV), rem = idx % (D * TV);
-    const int dd = rem / TV, p = rem % TV;
-    const int pp = p & 15;
-    const int kk = sub * TV + (p & ~15) + ((pp & 7) >> 2) * 8 + (pp >> 3) * 4 + (pp & 3);
-    vdst[idx] = vs[kk][dd];
+  for (int c = tid; c < TK * D / 8; c += 256) {
+    const int sub = c / (D * TV / 8), rem = c % (D * TV / 8);
+    const int dd = rem / (TV / 8), p0 = (rem % (TV / 8)) * 8;
+    uint16_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int p = p0 + e, pp = p & 15;
+      const int kk = sub * TV + (p & ~15) + ((pp & 7) >> 2) * 8 + (pp >> 3) * 4 + (pp & 3);
+      w[e] = vs[kk][dd];
+    }
+    *(u32x4*)(vdst + (int64_t)c * 8) = *(const u32x4*)w;
   }
 }
 
@@ -195,14 +238,16 @@ __global__ __launch_bounds__(256) void kv_prepare_f32_kernel(
 }
 
 hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
-                                  uint16_t* kp, uint16_t* vt, uint16_t* kc, uint16_t* vc,
-                                  int64_t B, int64_t L, int64_t Lpad, int h_kv, int d, int64_t cap,
-                                  hipStream_t st) {
+                                  uint16_t* kp, uint16_t* vt, float* kmax, uint16_t* kc,
+                                  uint16_t* vc, int64_t B, int64_t L, int64_t Lpad, int h_kv, int d,
+                                  int64_t cap, hipStream_t st) {
   dim3 grid((unsigned)(Lpad / 64), (unsigned)h_kv, (unsigned)B);
   if (d == 128)
-    kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kc, vc, L, Lpad, h_kv, cap);
+    kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kc, vc, L, Lpad,
+                                                      h_kv, cap);
   else
-    kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kc, vc, L, Lpad, h_kv, cap);
+    kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kc, vc, L, Lpad,
+                                                     h_kv, cap);
   return hipGetLastError();
 }
 

@@ -104,8 +104,9 @@ def test_rope_rejects(lib):
 
 def test_workspace_sizes(lib):
     # bf16 prefill: cos/sin table + rotated K + transposed V (64-key padded)
+    # + the largest K row norm per 64-key tile
     n = lib.gqa_prefill_workspace_size(1, 4, 4096, 4, 128)
-    assert n == 4096 * 64 * 8 + 2 * 4 * 4 * 4096 * 128 * 2
+    assert n == 4096 * 64 * 8 + 2 * 4 * 4 * 4096 * 128 * 2 + 4 * 4 * 64 * 4
     assert lib.gqa_prefill_workspace_size(1, 0, 10, 4, 128) == 0
     # decode: (m, l, o[d]) per (b, group, 1024-key chunk, head)
     n = lib.gqa_decode_workspace_size(32, 28, 4, 128, 32768)
