@@ -35,11 +35,23 @@ sys.path.insert(0, ROOT)
 METRIC = "GQA prefill TFLOP/s + decode KV-stream GB/s, % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
-# HBM bytes per dispatch measured by rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE,
-# scaled by the copy-kernel calibration); None until measured for the
-# current kernels.
-TRAFFIC_PREFILL_BYTES = None
-TRAFFIC_DECODE_BYTES = None
+# HBM bytes per dispatch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# (KiB per dispatch, each scaled by what the counter reads for a plain 1 GiB
+# device copy: FETCH x 2.00, WRITE x 1.00).  Each figure is valid only for the
+# kernel source it was measured on (sha256 prefix); otherwise it reports null.
+TRAFFIC = {
+    "prefill": ("prefill_bf16.hip", "d8185fd8814ab33a", (137380.4 * 2.0 + 238261.5) * 1024),
+    "decode": ("decode.hip", "453db71308e11c0a", (1058210.9 * 2.0 + 14784.1) * 1024),
+}
+
+
+def traffic_bytes(which):
+    import hashlib
+    src, digest, nbytes = TRAFFIC[which]
+    path = os.path.join(ROOT, "rope_causal_grouped_amd", "csrc", src)
+    with open(path, "rb") as f:
+        cur = hashlib.sha256(f.read()).hexdigest()[:16]
+    return nbytes if cur == digest else None
 
 
 def log(msg):
@@ -182,7 +194,7 @@ def main():
         out["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel",
                            "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": ach / PEAK_BF16_TFLOPS, "kernel_ms": attn_avg,
-                           "traffic": TRAFFIC_PREFILL_BYTES}
+                           "traffic": traffic_bytes("prefill")}
     if run_d:
         kvb = wd.decode_kv_bytes()
         split_avg = split_ms / max(split_n, 1)
@@ -193,7 +205,7 @@ def main():
                "roofline": {"bound": "hbm", "kernel": "decode_split_bf16_kernel",
                             "achieved": dach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": dach / PEAK_HBM_GBS, "kernel_ms": split_avg,
-                            "traffic": TRAFFIC_DECODE_BYTES}}
+                            "traffic": traffic_bytes("decode")}}
         out["decode"] = dec
         if not run_p:
             out["value"], out["unit"] = dec["value"], "GB/s"

@@ -249,7 +249,8 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
     return fail(GQA_ERR_INVALID_ARG,
                 "kv_len=%lld > q_pos+1=%lld: the query may only see keys at or before its position",
                 (long long)kv_len, (long long)(q_pos + 1));
-  if (cap > (INT64_C(1) << 30) || q_pos > (INT64_C(1) << 40) || B > 65535 || h_q > 65535)
+  if (cap > (INT64_C(1) << 30) || q_pos > (INT64_C(1) << 40) || B > 65535 || h_q > 65535 ||
+      gqa::decode_num_splits(cap) > gqa::kDecodeMaxSplitsLds)
     return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
       !aligned16(workspace))

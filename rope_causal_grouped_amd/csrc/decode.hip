@@ -29,7 +29,8 @@ int decode_num_splits(int64_t kv_len) {
 // rows straight from HBM into the A operand), then O^T += V^T P^T with V
 // staged through a wave-private LDS slab to turn key-major rows into the
 // key-contiguous operand.  Heads beyond 16 per group run as extra head
-// blocks (another pass over the chunk).
+// blocks (another pass over the chunk).  The cache is read once, so its
+// loads are non-temporal (they do not displace reused lines in the caches).
 template <int D>
 __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -100,13 +101,13 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
       const int key = min(k0 + blk * 16 + col, kv_len - 1);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        ka[blk][s] = *(const u32x4*)(kbase + key * RS + s * 32 + h4 * 8);
+        ka[blk][s] = __builtin_nontemporal_load((const u32x4*)(kbase + key * RS + s * 32 + h4 * 8));
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int ch = lane + 64 * i;
       const int key = min(k0 + ch / (D / 8), kv_len - 1);
-      va[i] = *(const u32x4*)(vbase + key * RS + (ch % (D / 8)) * 8);
+      va[i] = __builtin_nontemporal_load((const u32x4*)(vbase + key * RS + (ch % (D / 8)) * 8));
     }
     // S^T for 2 x 16 keys
     f32x4 sacc[2];
@@ -286,28 +287,45 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
   }
 }
 
-// Merge the chunk partials of one (b, query head); one thread per dim.
+// Merge the chunk partials of one (b, query head); one thread per dim.  The
+// chunk maxima and sums are staged in LDS once; every thread then issues its
+// per-chunk loads independently.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restrict__ pm,
                                                            const float* __restrict__ pl,
                                                            const float* __restrict__ po,
                                                            void* __restrict__ o, int h_q, int h_kv,
                                                            int g, int d, int n_split) {
+  __shared__ float wsc[kDecodeMaxSplitsLds];
+  __shared__ float red[2];
   const int t = blockIdx.x, b = blockIdx.y;
   const int u = t / g, c = t % g;
   const int64_t base = (((int64_t)b * h_kv + u) * n_split) * g + c;
+  // 1) global max of the chunk maxima (n_split <= kDecodeMaxSplitsLds)
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pm[base + (int64_t)s * g]);
-  float L = 0.f;
-  for (int s = 0; s < n_split; ++s)
-    L = fmaf(__builtin_amdgcn_exp2f(pm[base + (int64_t)s * g] - M), pl[base + (int64_t)s * g], L);
-  const float inv = 1.0f / L;
+  for (int s = threadIdx.x; s < n_split; s += blockDim.x) M = fmaxf(M, pm[base + (int64_t)s * g]);
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], blockDim.x > 64 ? red[1] : -INFINITY);
+  __syncthreads();
+  // 2) chunk weights 2^(m_s - M) and the total sum
+  float Ls = 0.f;
+  for (int s = threadIdx.x; s < n_split; s += blockDim.x) {
+    const float w = __builtin_amdgcn_exp2f(pm[base + (int64_t)s * g] - M);
+    wsc[s] = w;
+    Ls = fmaf(w, pl[base + (int64_t)s * g], Ls);
+  }
+  for (int m = 32; m >= 1; m >>= 1) Ls += __shfl_xor(Ls, m, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = Ls;
+  __syncthreads();
+  const float inv = 1.0f / (red[0] + (blockDim.x > 64 ? red[1] : 0.f));
+  // 3) weighted sum of the chunk outputs
   for (int dim = threadIdx.x; dim < d; dim += blockDim.x) {
     float acc = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const int64_t idx = base + (int64_t)s * g;
-      acc = fmaf(__builtin_amdgcn_exp2f(pm[idx] - M), po[idx * d + dim], acc);
-    }
+#pragma unroll 8
+    for (int s = 0; s < n_split; ++s)
+      acc = fmaf(wsc[s], po[(base + (int64_t)s * g) * d + dim], acc);
     const int64_t oo = ((int64_t)b * h_q + t) * d + dim;
     if constexpr (OUT_BF16)
       ((uint16_t*)o)[oo] = f32_to_bf16_bits(acc * inv);

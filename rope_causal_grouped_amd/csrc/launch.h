@@ -11,6 +11,7 @@ constexpr int kPrefillTileK = 64;      // key padding granule of the prepared K/
 constexpr int kPrefillTileV = 32;      // keys per attention tile; V^T is stored per such tile
 constexpr int kPrefillRowsWG = 128;    // stacked (position, head) rows per workgroup
 constexpr int kDecodeChunk = 1024;     // keys per decode split
+constexpr int kDecodeMaxSplitsLds = 8192;  // chunk weights staged by the merge kernel
 
 hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,
                              double log2_theta, hipStream_t st);
