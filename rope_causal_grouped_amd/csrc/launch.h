@@ -9,7 +9,7 @@ namespace gqa {
 
 constexpr int kPrefillTileK = 64;      // key padding granule of the prepared K/V
 constexpr int kPrefillTileV = 32;      // keys per attention tile; V^T is stored per such tile
-constexpr int kPrefillRowsWG = 128;    // stacked (position, head) rows per workgroup
+constexpr int kPrefillRowsWG = 256;    // stacked (position, head) rows per workgroup
 constexpr int kDecodeChunk = 1024;     // keys per decode split
 constexpr int kDecodeMaxSplitsLds = 8192;  // chunk weights staged by the merge kernel
 

@@ -11,40 +11,41 @@
 // for a fixed (batch b, group u) the rows (position i, head t in the group)
 // form one "stacked" query matrix of L*g rows, ordered position-major; that
 // matrix is contiguous in q (the g heads of one position are adjacent).  A
-// workgroup owns 128 consecutive stacked rows (about 128/g positions, all g
+// workgroup owns 256 consecutive stacked rows (about 256/g positions, all g
 // heads) and streams the K/V tiles of group u through LDS once for all of
 // them: the g-fold K/V reuse GQA offers (same page, closing note of §4.1.3).
-// Its four waves own 32 rows each.  Two workgroups share a CU, so the two
-// waves on each SIMD come from different workgroups, are not tied by a
-// common barrier, and overlap one's matrix-core phase with the other's
-// softmax.
+// Eight waves own 32 rows each, two waves per SIMD.
 //
 // Per 64-key tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (K from LDS as the A operand, the wave's rotated Q rows resident in VGPRs
-// as the B operand), so each lane holds one query row's scores and the row
-// max needs one exchange with lane ^ 32.  The probabilities, rounded to
-// bf16, are already in the B-operand layout of O^T += V^T P^T; V arrives
-// pre-transposed (keys contiguous, in the accumulator's lane order) from the
-// preparation pass, in 32-key sub-tiles.
+// as the B operand), so each lane holds half of one query row's scores.  The
+// probabilities, rounded to bf16, are already in the B-operand layout of
+// O^T += V^T P^T; V arrives pre-transposed (keys contiguous, in the
+// accumulator's lane order) from the preparation pass, in 32-key sub-tiles.
 //
-// K and V^T tiles go from HBM straight into LDS (global_load_lds_dwordx4,
-// no staging registers).  That instruction writes 16 bytes per lane at
-// consecutive LDS addresses, so the tiles are stored unpadded and bank
-// conflicts are avoided instead by XOR-swizzling the 16-byte chunk index of
-// each row with bits of the row index; the operand reads apply the same
-// swizzle.
+// Ping-pong schedule.  Each wave alternates between a matrix phase (P.V of
+// tile i-1, then S^T of tile i) and a vector phase (softmax of tile i).
+// Waves 0-3 and waves 4-7 (one of each on every SIMD) run the two phases in
+// opposite order and every phase ends at a workgroup barrier, so on each
+// SIMD one wave's matrix-core work always runs against the other wave's
+// softmax.  A matrix phase reads 32 operand fragments from LDS; they are
+// issued a few MFMAs ahead of their use so that LDS latency stays hidden.
+// The wave group in its vector phase also streams tiles from HBM straight
+// into LDS (global_load_lds_dwordx4, no staging registers), two phases ahead
+// of their use: K by waves 4-7, V by waves 0-3, each in a three-slot ring.  LDS rows are unpadded; the 16-byte
+// chunk index is XOR-swizzled with the row index, which keeps the operand
+// reads free of bank conflicts.
 //
-// The running max is raised only when a row's max grows by more than 2^8
-// (exp2 units): probabilities then stay <= 256, exact enough in bf16 and far
-// from fp32 overflow, and the O rescale is skipped on almost every tile.
-// Waiting for a tile's max before the exponentials would serialise each
-// tile, so on the common path the probabilities are formed against the
-// running max straight away; that is safe when |q'| * max|k'| over the tile
-// (the preparation pass stores max|k'| per 64-key tile) is within 2^64 of
-// the running max.  The tile max is then taken alongside P.V, and if it
-// grew past the threshold, O and l (which already hold this tile) are
-// rescaled together.  The first tile, the diagonal (masked) tiles and tiles
-// that fail the bound take the max-first path.
+// Softmax without a per-tile max.  |q'| * max|k'| (Cauchy-Schwarz; max over
+// the keys this workgroup visits, from the per-tile norms of the preparation
+// pass) bounds every score of a row.  Once the row's reference m is within
+// 64 (exp2 units) of that bound, probabilities are formed against m directly
+// (<= 2^64, far inside fp32 and bf16 range) and the tile max is not needed;
+// m is raised only if a tile's probability sum passes 2^32, which keeps O
+// and l bounded.  Until then (the first tile at least) the tile max is taken
+// first and m follows it lazily (raised when the max grows by more than 8).
+// m never exceeds the true running max by more than log2(64), so the
+// largest probability cannot underflow.
 
 #include "common.h"
 #include "launch.h"
@@ -55,21 +56,38 @@ namespace {
 
 constexpr int TK = 64;                      // keys per tile
 constexpr int TV = kPrefillTileV;           // keys per prepared V^T sub-tile (32)
-constexpr int NW = 4;                       // waves per workgroup
+constexpr int NW = 8;                       // waves per workgroup
 constexpr int RW = 32;                      // rows per wave
-constexpr float kRescaleThreshold = 8.0f;   // log2 units
-constexpr float kStaleMaxHeadroom = 64.0f;  // log2 units: p <= 2^64 against a stale max
+constexpr int PF = 4;                       // LDS operand reads kept ahead of the MFMAs
+constexpr int kXcds = 8;                    // XCDs (each with its own L2) per MI355X
+constexpr float kRescaleThreshold = 8.0f;   // log2 units, max-first path
+constexpr float kBoundHeadroom = 64.0f;     // log2 units, bound-first path
+constexpr float kSumCap = 4294967296.0f;    // 2^32
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16x8_sum(const bf16x8 v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
+}
 
 }  // namespace
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
-    const float2* __restrict__ cs, void* __restrict__ o, int L,
-    int Lpad, int h_q, int h_kv, int g, int n_rb, int n_bu, float sl2, int causal) {
+    const float2* __restrict__ cs, void* __restrict__ o, int L, int Lpad, int h_q, int h_kv,
+    int g, int n_rb, int n_bu, float sl2, int causal) {
   constexpr int NS = D / 16;                  // 16-dim k-steps of S^T
   constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
+  constexpr int NPV = 4 * NDB;                // P.V MFMAs per tile
+  constexpr int NQK = 2 * NS;                 // S^T MFMAs per tile
+  constexpr int NR = NPV + NQK;               // operand fragments per matrix phase
   constexpr int ROWS = NW * RW;
   // tile geometry in 16-byte chunks
   constexpr int KCPR = D / 8;                 // chunks per K row (16 for d = 128)
@@ -77,18 +95,30 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   constexpr int VCPR = TV / 8;                // chunks per V^T row (4)
   constexpr int VRPB = 16 / VCPR;             // V^T rows per 256 bytes
   constexpr int TILE_CH = TK * D / 8;         // chunks per K (or V^T) tile
-  constexpr int LPW = TILE_CH / 64 / NW;      // direct loads per wave per tile and tensor
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][TK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][TK * D];
+  constexpr int LPG = TILE_CH / 64 / 4;       // direct loads per wave when 4 waves load a tile
+  static_assert(LPG >= 1, "tile too small for the wave count");
+  __shared__ __attribute__((aligned(16))) uint16_t ks[3][TK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[3][TK * D];
+  __shared__ float wred[NW];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int grp = wave >> 2;                  // 0: matrix phase first; 1: vector phase first
   const int hl = lane >> 5, c32 = lane & 31;
 
-  // Heaviest row blocks (latest positions, most keys) are dispatched first.
-  const int id = blockIdx.x;
-  const int rb = n_rb - 1 - id / n_bu;
-  const int bu = id % n_bu;
+  // Work item w = bu * n_rb + (n_rb - 1 - rb).  Workgroups are dispatched
+  // to the eight XCDs round-robin by id, and each XCD has its own L2, so the
+  // ids that land on one XCD get one contiguous range of work items: an XCD
+  // works through the row blocks of one (b, u) at a time and the K/V of
+  // that group stays in its L2.  Within a (b, u), the heaviest row blocks
+  // (latest positions, most keys) go first.
+  const int nwg = (int)gridDim.x;
+  const int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+  const int per = nwg / kXcds, extra = nwg % kXcds;
+  const int w = xcd * per + min(xcd, extra) + j;
+  const int bu = w / n_rb;
+  const int rb = n_rb - 1 - (w - bu * n_rb);
   const int b = bu / h_kv, u = bu % h_kv;
 
   const int rows_total = L * g;
@@ -98,6 +128,68 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
   const int rr = row_valid ? row : rows_total - 1;
   const int pos = rr / g;
   const int head = u * g + (rr - pos * g);
+
+  // ---- key range
+  const int rmax = min(R0 + ROWS - 1, rows_total - 1);
+  const int n_keys = causal ? rmax / g + 1 : L;
+  const int n_tiles = (n_keys + TK - 1) / TK;
+  const int wr0 = min(R0 + wave * RW, rows_total - 1);
+  const int wr1 = min(R0 + wave * RW + RW - 1, rows_total - 1);
+  const int wpos_lo = wr0 / g, wpos_hi = wr1 / g;
+  const int lim = causal ? min(pos, L - 1) : L - 1;   // last key this row may see
+  // tile i has keys this wave may see / needs the element mask
+  auto active = [&](int i) { return !causal || i * TK <= wpos_hi; };
+  auto masked = [&](int i) { return (causal && i * TK + TK - 1 > wpos_lo) || (i * TK + TK > L); };
+
+  // ---- direct HBM -> LDS tile loads by one wave group.  Instruction n of
+  // wave w (of the group) fills LDS chunks [(w*LPG + n)*64, +64); lane l's
+  // chunk P sits at row P / CPR, physical slot P % CPR, and holds logical
+  // chunk slot ^ swizzle(row).  Waves 4-7 load K, waves 0-3 load V.
+  const int wg4 = wave & 3;
+  const uint16_t* src = (grp ? kp : vt) + (int64_t)bu * Lpad * D;
+  int loff[LPG];
+#pragma unroll
+  for (int n = 0; n < LPG; ++n) {
+    const int P = (wg4 * LPG + n) * 64 + lane;
+    if (grp) {
+      const int kr = P / KCPR, kslot = P % KCPR;
+      loff[n] = kr * D + ((kslot ^ ((kr / KRPB) % KCPR)) * 8);
+    } else {
+      const int sub = P / (D * VCPR), rem = P % (D * VCPR);
+      const int vr = rem / VCPR, vslot = rem % VCPR;
+      loff[n] = sub * D * TV + vr * TV + ((vslot ^ ((vr / VRPB) % VCPR)) * 8);
+    }
+  }
+  auto load_tile = [&](uint16_t* ring, int tile) {
+#pragma unroll
+    for (int n = 0; n < LPG; ++n)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(src + (int64_t)tile * TK * D + loff[n]),
+          (void __attribute__((address_space(3)))*)&ring[(wg4 * LPG + n) * 64 * 8], 16, 0, 0);
+  };
+  // wait for this wave's older tile; `newer`: one more tile was issued since
+  auto landed = [&](bool newer) {
+    if (newer) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPG) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  // ---- prologue part 1: K(0) on its way; largest K norm this workgroup
+  // will see (per-tile norms from the preparation pass)
+  const int n = n_tiles;
+  if (grp) {
+    load_tile(ks[0], 0);
+    if (n > 1) load_tile(ks[1], 1);
+  } else {
+    load_tile(vs[0], 0);
+  }
+  {
+    const float* kmax_bu = kmax + (int64_t)bu * (Lpad / TK);
+    float km = 0.f;
+    for (int t = tid; t < n_tiles; t += NW * 64) km = fmaxf(km, kmax_bu[t]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) km = wave_max_xor(km, m);
+    if (lane == 0) wred[wave] = km;
+  }
 
   // ---- Q row: load, rotate at pos, round to bf16 (B operand layout: lane
   // holds dims s*16 + hl*8 + e of its row; RoPE pairs are (s, s + NS/2)).
@@ -121,9 +213,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
       }
     }
   }
-  // |q'| of the row (from the bf16 values the matrix cores see), times the
-  // score scale: |q'| * max|k'| bounds every score of a tile (Cauchy-Schwarz;
-  // the rotation keeps norms), with a small margin for fp32 rounding
+  // |q'| of the row from the bf16 values the matrix cores see, in score
+  // units (scale * log2 e), with a margin for fp32 rounding
   float qcap;
   {
     float ss = 0.f;
@@ -136,53 +227,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
       }
     qcap = sqrtf(sum_xor32(ss)) * sl2 * 1.01f;
   }
-  const float* kmax_bu = kmax + (int64_t)bu * (Lpad / TK);
-
-  // ---- key range
-  const int rmax = min(R0 + ROWS - 1, rows_total - 1);
-  const int n_keys = causal ? rmax / g + 1 : L;
-  const int n_tiles = (n_keys + TK - 1) / TK;
-  const int wr0 = min(R0 + wave * RW, rows_total - 1);
-  const int wr1 = min(R0 + wave * RW + RW - 1, rows_total - 1);
-  const int wpos_lo = wr0 / g, wpos_hi = wr1 / g;
-  const int lim = causal ? min(pos, L - 1) : L - 1;   // last key this row may see
-
-  // ---- direct HBM -> LDS tile loads.  Instruction i of wave w fills LDS
-  // chunks [(w*LPW + i)*64, +64); lane l's chunk P sits at row P / CPR,
-  // physical slot P % CPR, and holds logical chunk slot ^ swizzle(row).
-  const uint16_t* kbase = kp + (int64_t)bu * Lpad * D;
-  const uint16_t* vbase = vt + (int64_t)bu * Lpad * D;
-  int koff[LPW], voff[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int P = (wave * LPW + i) * 64 + lane;
-    const int kr = P / KCPR, kslot = P % KCPR;
-    koff[i] = kr * D + ((kslot ^ ((kr / KRPB) % KCPR)) * 8);
-    const int sub = P / (D * VCPR), rem = P % (D * VCPR);
-    const int vr = rem / VCPR, vslot = rem % VCPR;
-    voff[i] = sub * D * TV + vr * TV + ((vslot ^ ((vr / VRPB) % VCPR)) * 8);
-  }
-  // load n of the 2*LPW direct loads a wave issues per tile (K first, then V)
-  auto issue_one = [&](int n, int tile, int buf) {
-    const int i = n % LPW;
-    const int dst = (wave * LPW + i) * 64 * 8;
-    if (n < LPW)
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(kbase + (int64_t)tile * TK * D + koff[i]),
-          (void __attribute__((address_space(3)))*)&ks[buf][dst], 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(vbase + (int64_t)tile * TK * D + voff[i]),
-          (void __attribute__((address_space(3)))*)&vs[buf][dst], 16, 0, 0);
-  };
-  auto issue_tile = [&](int tile, int buf) {
-#pragma unroll
-    for (int n = 0; n < 2 * LPW; ++n) issue_one(n, tile, buf);
-  };
-  auto tile_landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  // next tile to prefetch; past the last tile the last one is loaded again
-  // into the idle buffer (harmless), which keeps the loop body uniform
-  auto next_tile = [&](int kt) { return min(kt + 1, n_tiles - 1); };
 
   // ---- operand read offsets (elements), swizzled like the stores
   const int kswz = (c32 / KRPB) % KCPR;       // same for key rows c32 and 32 + c32
@@ -200,27 +244,82 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const f32x16 zero16 = {};
+  f32x16 sacc[2];     // scores of the tile between its matrix and vector phases
+  bf16x8 pb[2][2];    // probabilities between the vector and the next matrix phase
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    sacc[kb] = zero16;
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[kb][hs][e] = (__bf16)0.0f;
+  }
 
-  // S^T = K Q^T for two 32-key blocks (independent MFMA chains)
-  auto qk = [&](f32x16 (&sacc)[2], int buf) {
-    const uint16_t* kt0 = ks[buf];
+  // ---- matrix phases.  Fragment j < NPV is V^T block (kb, hs, db) with
+  // j = (kb*2 + hs)*NDB + db; fragment NPV + 2s + c is K rows c*32.. at
+  // k-step s.  All reads and MFMAs sit in one basic block; the scheduling
+  // barriers issue the reads PF fragments ahead of their MFMAs.
+  auto read_v = [&](const uint16_t* vt0, int j) {
+    const int kb = j / (2 * NDB), hs = (j / NDB) % 2, db = j % NDB;
+    return *(const bf16x8*)(vt0 + kb * D * TV + db * 32 * TV + vread[hs]);
+  };
+  auto read_k = [&](const uint16_t* kt0, int j) {
+    const int s = j / 2, c = j % 2;
+    return *(const bf16x8*)(kt0 + c * 32 * D + kread[s]);
+  };
+  auto mma_pv = [&](const bf16x8 a, int j) {
+    const int kb = j / (2 * NDB), hs = (j / NDB) % 2, db = j % NDB;
+    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][hs], oacc[db], 0, 0, 0);
+  };
+  auto mma_qk = [&](const bf16x8 a, int j) {
+    const int s = j / 2, c = j % 2;
+    sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[s], s == 0 ? zero16 : sacc[c], 0, 0,
+                                                      0);
+  };
+  // P.V of tile i-1 and S^T of tile i
+  auto matrix_full = [&](int i) {
+    const uint16_t* vt0 = vs[(i - 1) % 3];
+    const uint16_t* kt0 = ks[i % 3];
+    bf16x8 fr[NR];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 a0 = *(const bf16x8*)(kt0 + kread[s]);
-      const bf16x8 a1 = *(const bf16x8*)(kt0 + 32 * D + kread[s]);
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[s], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[s], sacc[1], 0, 0, 0);
+    for (int j = 0; j < NPV; ++j) fr[j] = read_v(vt0, j);
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) fr[NPV + j] = read_k(kt0, j);
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) mma_pv(fr[j], j);
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) mma_qk(fr[NPV + j], j);
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int j = 0; j < NR - PF; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+    __builtin_amdgcn_sched_barrier(0);   // the MFMAs stay in this phase
   };
-  // row max of a tile's scores (exp2 units)
-  auto tile_max = [&](const f32x16 (&sacc)[2]) {
-    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+  // S^T of tile 0 only
+  auto matrix_qk = [&](int i) {
+    const uint16_t* kt0 = ks[i % 3];
+    bf16x8 fr[NQK];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
-    return max_xor32(mx) * sl2;
+    for (int j = 0; j < NQK; ++j) fr[j] = read_k(kt0, j);
+#pragma unroll
+    for (int j = 0; j < NQK; ++j) mma_qk(fr[j], j);
   };
-  auto rescale = [&](float mx) {
-    const float m_new = fmaxf(m_run, mx);
+  // P.V of the last tile only
+  auto matrix_pv = [&](int i) {
+    const uint16_t* vt0 = vs[(i - 1) % 3];
+    bf16x8 fr[NPV];
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) fr[j] = read_v(vt0, j);
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) mma_pv(fr[j], j);
+  };
+
+  // ---- vector phase i: probabilities of tile i into pb, row sums into l
+  auto rescale = [&](float m_new) {
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
@@ -229,94 +328,130 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
       // keep the accumulators in AGPRs outside this rare branch
       asm volatile("" : "+a"(oacc[db]));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
       asm volatile("" : "+a"(oacc[db]));
     }
   };
-  // probabilities against the running max (bf16, B operand of P.V); returns
-  // their fp32 sum
-  auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
-    float psum = 0.f;
+  auto probs = [&](const f32x16& s0, const f32x16& s1) {
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], sl2, -m_run));
-        pb[kb][i >> 3][i & 7] = (__bf16)p;
-        psum += p;
-      }
-    return psum;
+    for (int e = 0; e < 16; ++e) {
+      pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[e], sl2, -m_run));
+      pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[e], sl2, -m_run));
+    }
+    acc0 = bf16x8_sum(pb[0][0], acc0);
+    acc1 = bf16x8_sum(pb[0][1], acc1);
+    acc0 = bf16x8_sum(pb[1][0], acc0);
+    acc1 = bf16x8_sum(pb[1][1], acc1);
+    return acc0 + acc1;
   };
-  // O^T += V^T P^T: per 16-key step, one MFMA per 32-dim block
-  auto pv = [&](const bf16x8 (&pb)[2][2], int buf) {
-    const uint16_t* vt0 = vs[buf];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 a = *(const bf16x8*)(vt0 + kb * D * TV + db * 32 * TV + vread[hs]);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][hs], oacc[db], 0, 0, 0);
-        }
-  };
-
-  issue_tile(0, 0);
-  tile_landed();
-  __syncthreads();
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    const int k0 = kt * TK;
-    issue_tile(next_tile(kt), buf ^ 1);
-    if (!causal || k0 <= wpos_hi) {
-      const bool masked = (causal && k0 + TK - 1 > wpos_lo) || (k0 + TK > L);
-      // fast path: no mask on this tile and every score provably within the
-      // headroom of the running max, so P can be formed before the tile max
-      const bool fast = !masked && !__builtin_amdgcn_ballot_w64(
-                                       qcap * kmax_bu[kt] > m_run + kStaleMaxHeadroom);
-      f32x16 sacc[2];
+  float crow = 0.f;   // bound on this row's scores, score units (set after the prologue)
+  float m_raise = 0.f;  // raise of m owed by the previous tile's large sum (applied lazily)
+  auto vector_phase = [&](int i) {
+    if (!active(i)) {   // keys beyond this wave's rows: contribute nothing
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      qk(sacc, buf);
-      if (masked) {
+        for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int e = 0; e < 8; ++e) pb[kb][hs][e] = (__bf16)0.0f;
+      return;
+    }
+    f32x16 s0 = sacc[0], s1 = sacc[1];
+    asm volatile("" : "+v"(s0), "+v"(s1));   // scores to VGPRs once
+    if (masked(i)) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + (i >> 2) * 8 + hl * 4 + (i & 3);
-            if (key > lim) sacc[kb][i] = -INFINITY;
-          }
-      }
-      if (!fast) {   // max first
-        const float mx = tile_max(sacc);
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) rescale(mx);
-      }
-      bf16x8 pb[2][2];
-      l_run += probs(sacc, pb);
-      pv(pb, buf);
-      if (fast) {    // the tile max off the critical path; rescale what holds it
-        const float mx = tile_max(sacc);
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold)) rescale(mx);
+      for (int e = 0; e < 16; ++e) {
+        const int key = i * TK + (e >> 2) * 8 + hl * 4 + (e & 3);
+        if (key > lim) s0[e] = -INFINITY;
+        if (key + 32 > lim) s1[e] = -INFINITY;
       }
     }
-    tile_landed();
+    // new reference: the owed raise (O and l already hold the tile that
+    // caused it), or the tile max while the bound is not yet usable
+    float m_new = m_run + m_raise;
+    if (__builtin_amdgcn_ballot_w64(crow > m_run + kBoundHeadroom)) {   // max first
+      float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+      mx = max_xor32(mx) * sl2;
+      if (mx > m_new + kRescaleThreshold) m_new = mx;
+    }
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) rescale(m_new);
+    const float psum = probs(s0, s1);
+    l_run += psum;
+    // probabilities here are <= 2^64; a sum past 2^32 owes a raise of m by
+    // its (integral) log2, taken at the next tile once P.V has added it
+    m_raise = 0.f;
+    if (__builtin_amdgcn_ballot_w64(psum > kSumCap))
+      m_raise = ceilf(__builtin_amdgcn_logf(fmaxf(max_xor32(psum), 1.0f)));
+  };
+
+  // ---- prologue part 2: K(0) resident, bound known
+  if (grp) landed(n > 1);
+  __syncthreads();
+  {
+    float km = wred[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) km = fmaxf(km, wred[w]);
+    crow = qcap * km;
+  }
+
+  // ---- periods t = 0 .. 2 n_tiles + 1, each ending at a barrier.  Even
+  // period 2i: waves 0-3 run matrix phase i, waves 4-7 vector phase i-1 and
+  // issue K(i+2).  Odd period 2i+1: waves 0-3 run vector phase i and issue
+  // V(i+1), waves 4-7 matrix phase i.  Tiles live in three-slot rings
+  // (tile t in slot t % 3) and get two periods to land: the loading waves
+  // wait for K(i+1) and V(i) before the barrier that ends period 2i+1.
+  if (grp == 0) {
+    matrix_qk(0);                           // period 0
+    __syncthreads();
+    if (n > 1) load_tile(vs[1], 1);         // period 1
+    vector_phase(0);
+    landed(n > 1);
+    __syncthreads();
+    for (int i = 1; i < n; ++i) {
+      matrix_full(i);                       // period 2i
+      __syncthreads();
+      if (i + 1 < n) load_tile(vs[(i + 1) % 3], i + 1);   // period 2i+1
+      vector_phase(i);
+      landed(i + 1 < n);
+      __syncthreads();
+    }
+    matrix_pv(n);                           // period 2n
+    __syncthreads();
+    __syncthreads();                        // period 2n+1
+  } else {
+    if (n > 2) load_tile(ks[2], 2);         // period 0
+    __syncthreads();
+    matrix_qk(0);                           // period 1
+    landed(n > 2);
+    __syncthreads();
+    for (int i = 1; i < n; ++i) {
+      if (i + 2 < n) load_tile(ks[(i + 2) % 3], i + 2);   // period 2i
+      vector_phase(i - 1);
+      __syncthreads();
+      matrix_full(i);                       // period 2i+1
+      landed(i + 2 < n);
+      __syncthreads();
+    }
+    vector_phase(n - 1);                    // period 2n
+    __syncthreads();
+    matrix_pv(n);                           // period 2n+1
     __syncthreads();
   }
 
-  // ---- epilogue: O = O / l; lane holds dims db*32 + grp*8 + hl*4 + (0..3)
+  // ---- epilogue: O = O / l; lane holds dims db*32 + gq*8 + hl*4 + (0..3)
   const float inv = 1.0f / sum_xor32(l_run);
   if (row_valid) {
     const int64_t orow = ((int64_t)((int64_t)b * L + pos) * h_q + head) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int dim = db * 32 + grp * 8 + hl * 4;
-        const float y0 = oacc[db][grp * 4 + 0] * inv, y1 = oacc[db][grp * 4 + 1] * inv;
-        const float y2 = oacc[db][grp * 4 + 2] * inv, y3 = oacc[db][grp * 4 + 3] * inv;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int dim = db * 32 + gq * 8 + hl * 4;
+        const float y0 = oacc[db][gq * 4 + 0] * inv, y1 = oacc[db][gq * 4 + 1] * inv;
+        const float y2 = oacc[db][gq * 4 + 2] * inv, y3 = oacc[db][gq * 4 + 3] * inv;
         if constexpr (OUT_BF16) {
           u32x2 w;
           w[0] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
@@ -331,17 +466,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(
 }
 
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
-                               const float* kmax, const float2* cs, void* o, int out_bf16, int64_t B, int64_t L,
-                               int64_t Lpad, int h_q, int h_kv, int d, float scale, int causal,
-                               hipStream_t st) {
+                               const float* kmax, const float2* cs, void* o, int out_bf16,
+                               int64_t B, int64_t L, int64_t Lpad, int h_q, int h_kv, int d,
+                               float scale, int causal, hipStream_t st) {
   const int g = h_q / h_kv;
   const int n_rb = (int)((L * g + kPrefillRowsWG - 1) / kPrefillRowsWG);
   const int n_bu = (int)(B * h_kv);
   const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e): exp(x) = exp2(x log2 e)
   const unsigned grid = (unsigned)((int64_t)n_rb * n_bu);
 #define GQA_LAUNCH(DD, OB)                                                                    \
-  prefill_bf16_kernel<DD, OB><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, cs, o, (int)L, (int)Lpad, \
-                                                        h_q, h_kv, g, n_rb, n_bu, sl2, causal)
+  prefill_bf16_kernel<DD, OB><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, cs, o, (int)L,      \
+                                                        (int)Lpad, h_q, h_kv, g, n_rb, n_bu, \
+                                                        sl2, causal)
   if (d == 128) {
     if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);
   } else {
