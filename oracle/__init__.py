@@ -3,8 +3,13 @@ tests, the smoke check and the benchmark's CPU-baseline leg may use it."""
 
 from .gqa_oracle import (ROPE_THETA, inv_freq, rope, group_size, kv_group,
                          visible, softmax_rows, head_weights, attend, prefill,
-                         prefill_rows, decode, prefill_brute)
+                         prefill_rows, decode, prefill_brute,
+                         per_sequence, chunk_positions, cache_append,
+                         attend_cached, prefill_chunk, decode_ragged,
+                         decode_append)
 
 __all__ = ["ROPE_THETA", "inv_freq", "rope", "group_size", "kv_group",
            "visible", "softmax_rows", "head_weights", "attend", "prefill",
-           "prefill_rows", "decode", "prefill_brute"]
+           "prefill_rows", "decode", "prefill_brute", "per_sequence",
+           "chunk_positions", "cache_append", "attend_cached", "prefill_chunk",
+           "decode_ragged", "decode_append"]

@@ -189,6 +189,122 @@ def decode(q, k_cache, v_cache, kv_len: int, q_pos: int,
     return out
 
 
+# ------------------------------------------- cache append and chunks -----
+#
+# Autoregressive use around the path: every step appends the current K and V
+# of the h_kv groups to the per-layer cache ([csdn] §4.1.3 closing note), a
+# decode step attends to everything cached so far, and a long prompt may be
+# fed in chunks whose queries see the cache plus the chunk itself.
+
+def per_sequence(values, B: int) -> np.ndarray:
+    """One int64 value per sequence: a scalar is shared, an array is ragged."""
+    return np.broadcast_to(np.asarray(values, np.int64), (B,)).copy()
+
+
+def chunk_positions(start: int, n: int) -> np.ndarray:
+    """Positions of the n new rows of a sequence whose first new row sits at
+    ``start`` (the rows already cached occupy positions 0 .. start-1)."""
+    return np.arange(start, start + n)
+
+
+def cache_append(k_cache, v_cache, k_new, v_new, start, length=None,
+                 theta: float = ROPE_THETA):
+    """Append rows to the cache.  k_new/v_new [B, C, h_kv, d] are pre-RoPE;
+    row i < length[b] (default C) of sequence b sits at position
+    p = start[b] + i, its K is rotated at p and stored, with its V, in cache
+    row p.  Returns updated fp64 copies of (k_cache, v_cache)."""
+    kc = np.array(k_cache, np.float64, copy=True)
+    vc = np.array(v_cache, np.float64, copy=True)
+    B, C = np.shape(k_new)[:2]
+    start = per_sequence(start, B)
+    n_new = per_sequence(C if length is None else length, B)
+    for b in range(B):
+        n = int(n_new[b])
+        if n == 0:
+            continue
+        pos = chunk_positions(int(start[b]), n)
+        if pos[0] < 0 or pos[-1] >= kc.shape[1] or n > C:
+            raise ValueError("rows outside the cache")
+        kc[b, pos] = rope(np.asarray(k_new[b, :n], np.float64), pos, theta)
+        vc[b, pos] = np.asarray(v_new[b, :n], np.float64)
+    return kc, vc
+
+
+def attend_cached(q, q_pos, k_cache, v_cache, kv_len: int,
+                  theta: float = ROPE_THETA, scale: float | None = None):
+    """Queries of one sequence at explicit positions against its cache:
+    q [n, h_q, d] pre-RoPE (rotated here at q_pos[n]); cache rows j < kv_len
+    hold the rotated key and the value of position j, visible to a query iff
+    j <= its position.  Returns [n, h_q, d]."""
+    q = np.asarray(q, np.float64)
+    n, h_q, d = q.shape
+    h_kv = np.shape(k_cache)[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qp = np.asarray(q_pos)
+    qr = rope(q, qp, theta)
+    kb = np.asarray(k_cache[:kv_len], np.float64)
+    vb = np.asarray(v_cache[:kv_len], np.float64)
+    vis = visible(qp, np.arange(kv_len))
+    out = np.empty((n, h_q, d), np.float64)
+    for t in range(h_q):
+        u = kv_group(t, h_q, h_kv)
+        out[:, t, :] = attend(qr[:, t, :], kb[:, u, :], vb[:, u, :], scale, vis)
+    return out
+
+
+def prefill_chunk(q, k_cache, v_cache, start, length=None,
+                  theta: float = ROPE_THETA, scale: float | None = None):
+    """Chunked causal prefill against a cache that already holds the chunk's
+    own rows (see cache_append): query i < length[b] of sequence b sits at
+    position start[b] + i and sees cache rows 0 .. start[b] + i.
+    q [B, C, h_q, d]; returns O [B, C, h_q, d] with rows i >= length[b] NaN."""
+    q = np.asarray(q, np.float64)
+    B, C = q.shape[:2]
+    start = per_sequence(start, B)
+    n_new = per_sequence(C if length is None else length, B)
+    out = np.full(q.shape, np.nan)
+    for b in range(B):
+        n = int(n_new[b])
+        if n == 0:
+            continue
+        pos = chunk_positions(int(start[b]), n)
+        out[b, :n] = attend_cached(q[b, :n], pos, k_cache[b], v_cache[b],
+                                   int(pos[-1]) + 1, theta, scale)
+    return out
+
+
+def decode_ragged(q, k_cache, v_cache, kv_len, q_pos,
+                  theta: float = ROPE_THETA, scale: float | None = None):
+    """Decode with one length and one query position per sequence: q [B, h_q,
+    d]; sequence b attends to its cache rows 0 .. kv_len[b]-1 from position
+    q_pos[b] (kv_len[b] <= q_pos[b] + 1).  Returns O [B, h_q, d]."""
+    q = np.asarray(q, np.float64)
+    B = q.shape[0]
+    kv_len = per_sequence(kv_len, B)
+    q_pos = per_sequence(q_pos, B)
+    out = np.empty(q.shape, np.float64)
+    for b in range(B):
+        if not 1 <= kv_len[b] <= min(np.shape(k_cache)[1], q_pos[b] + 1):
+            raise ValueError("kv_len out of range")
+        out[b] = attend_cached(q[b][None], q_pos[b:b + 1], k_cache[b], v_cache[b],
+                               int(kv_len[b]), theta, scale)[0]
+    return out
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, pos,
+                  theta: float = ROPE_THETA, scale: float | None = None):
+    """One autoregressive step: the new token of sequence b sits at position
+    pos[b]; its K (rotated there) and V are appended at cache row pos[b],
+    then its query attends to rows 0 .. pos[b].  q [B, h_q, d], k_new/v_new
+    [B, h_kv, d].  Returns (O [B, h_q, d], k_cache', v_cache')."""
+    B = np.shape(q)[0]
+    pos = per_sequence(pos, B)
+    kc, vc = cache_append(k_cache, v_cache, np.asarray(k_new)[:, None],
+                          np.asarray(v_new)[:, None], pos, 1, theta)
+    return decode_ragged(q, kc, vc, pos + 1, pos, theta, scale), kc, vc
+
+
 # ------------------------------------------------------- brute force ------
 
 def prefill_brute(q, k, v, theta: float = ROPE_THETA, scale: float | None = None,

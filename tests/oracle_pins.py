@@ -280,8 +280,110 @@ def pin_prefill_rows(orc):
     close(orc.prefill_rows(q, k, v, rows), want, 1e-12, "prefill_rows")
 
 
+# ------------------------------------------------ cache, chunks, ragged --
+
+def pin_chunked_prefill_is_prefill(orc):
+    """Feeding a prompt in two chunks through the cache (ragged split points
+    per sequence) gives the rows of the one-shot prefill, and leaves the
+    cache holding the rotated K and the V of every position."""
+    rng = _rng(14)
+    B, L, h_q, h_kv, d = 2, 13, 6, 2, 16
+    q = _rand(rng, B, L, h_q, d)
+    k = _rand(rng, B, L, h_kv, d)
+    v = _rand(rng, B, L, h_kv, d)
+    want = orc.prefill(q, k, v)
+    cap = L + 2
+    kc = np.full((B, cap, h_kv, d), 7.0)   # rows never written must not be read
+    vc = np.full((B, cap, h_kv, d), 7.0)
+    split = np.array([5, 9])
+    C1, C2 = 9, 8
+    q1 = np.zeros((B, C1, h_q, d)); k1 = np.zeros((B, C1, h_kv, d)); v1 = np.zeros_like(k1)
+    q2 = np.zeros((B, C2, h_q, d)); k2 = np.zeros((B, C2, h_kv, d)); v2 = np.zeros_like(k2)
+    for b in range(B):
+        s0 = split[b]
+        q1[b, :s0], k1[b, :s0], v1[b, :s0] = q[b, :s0], k[b, :s0], v[b, :s0]
+        n2 = L - s0
+        q2[b, :n2], k2[b, :n2], v2[b, :n2] = q[b, s0:], k[b, s0:], v[b, s0:]
+    kc, vc = orc.cache_append(kc, vc, k1, v1, 0, split)
+    o1 = orc.prefill_chunk(q1, kc, vc, 0, split)
+    kc, vc = orc.cache_append(kc, vc, k2, v2, split, L - split)
+    o2 = orc.prefill_chunk(q2, kc, vc, split, L - split)
+    for b in range(B):
+        s0 = split[b]
+        close(o1[b, :s0], want[b, :s0], 1e-12, f"first chunk, sequence {b}")
+        close(o2[b, :L - s0], want[b, s0:], 1e-12, f"second chunk, sequence {b}")
+        assert np.isnan(o1[b, s0:]).all() and np.isnan(o2[b, L - s0:]).all()
+    close(kc[:, :L], orc.rope(k, np.arange(L)), 1e-12, "cached K")
+    close(vc[:, :L], v, 0.0, "cached V")
+    close(kc[:, L:], np.full((B, cap - L, h_kv, d), 7.0), 0.0, "rows past the prompt")
+
+
+def pin_decode_append_is_prefill_row(orc):
+    """A decode step that appends its own K, V at position p (ragged p per
+    sequence) returns row p of the prefill over positions 0..p."""
+    rng = _rng(15)
+    B, L, h_q, h_kv, d = 3, 11, 8, 2, 16
+    q = _rand(rng, B, L, h_q, d)
+    k = _rand(rng, B, L, h_kv, d)
+    v = _rand(rng, B, L, h_kv, d)
+    want = orc.prefill(q, k, v)
+    pos = np.array([0, 4, 10])
+    cap = L
+    kc = np.full((B, cap, h_kv, d), -3.0)
+    vc = np.full((B, cap, h_kv, d), -3.0)
+    kr = orc.rope(k, np.arange(L))
+    for b in range(B):
+        kc[b, :pos[b]] = kr[b, :pos[b]]
+        vc[b, :pos[b]] = v[b, :pos[b]]
+    qn = np.stack([q[b, pos[b]] for b in range(B)])
+    kn = np.stack([k[b, pos[b]] for b in range(B)])
+    vn = np.stack([v[b, pos[b]] for b in range(B)])
+    o, kc2, vc2 = orc.decode_append(qn, kn, vn, kc, vc, pos)
+    for b in range(B):
+        close(o[b], want[b, pos[b]], 1e-12, f"sequence {b} at {pos[b]}")
+        close(kc2[b, pos[b]], kr[b, pos[b]], 1e-12, "appended K")
+        close(vc2[b, pos[b]], v[b, pos[b]], 0.0, "appended V")
+        close(kc2[b, pos[b] + 1:], kc[b, pos[b] + 1:], 0.0, "rows after the new one")
+
+
+def pin_cache_append_pair0(orc):
+    """Pair 0 turns by exactly its position in radians (omega_0 = 1): as a
+    complex number, (k'_0 + i k'_{d/2}) = (k_0 + i k_{d/2}) e^{i p}."""
+    rng = _rng(16)
+    B, C, h_kv, d, cap = 2, 3, 2, 8, 40
+    k = _rand(rng, B, C, h_kv, d)
+    v = _rand(rng, B, C, h_kv, d)
+    start = np.array([30, 2])
+    kc, vc = orc.cache_append(np.zeros((B, cap, h_kv, d)), np.zeros((B, cap, h_kv, d)),
+                              k, v, start)
+    for b in range(B):
+        for i in range(C):
+            p = int(start[b]) + i
+            for u in range(h_kv):
+                z = complex(k[b, i, u, 0], k[b, i, u, d // 2]) * cmath.exp(1j * p)
+                assert abs(complex(kc[b, p, u, 0], kc[b, p, u, d // 2]) - z) < 1e-12, (b, i, u)
+
+
+def pin_ragged_decode_is_single(orc):
+    """Each sequence of a ragged decode equals a one-sequence decode with its
+    own kv_len and position."""
+    rng = _rng(17)
+    B, cap, h_q, h_kv, d = 3, 20, 6, 3, 8
+    q = _rand(rng, B, h_q, d)
+    kc = _rand(rng, B, cap, h_kv, d)
+    vc = _rand(rng, B, cap, h_kv, d)
+    kv_len = np.array([1, 20, 7])
+    q_pos = np.array([0, 25, 6])
+    o = orc.decode_ragged(q, kc, vc, kv_len, q_pos)
+    for b in range(B):
+        one = orc.decode(q[b:b + 1], kc[b:b + 1], vc[b:b + 1], int(kv_len[b]), int(q_pos[b]))
+        close(o[b], one[0], 1e-12, f"sequence {b}")
+
+
 ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_rope_half_split_pairing, pin_rope_norm, pin_rope_relative,
             pin_rope_group_law, pin_group_example, pin_repeat_interleave,
             pin_sdpa, pin_brute, pin_softmax_causal, pin_future_invariance,
-            pin_shift_invariance, pin_decode_is_prefill_row, pin_prefill_rows]
+            pin_shift_invariance, pin_decode_is_prefill_row, pin_prefill_rows,
+            pin_chunked_prefill_is_prefill, pin_decode_append_is_prefill_row,
+            pin_cache_append_pair0, pin_ragged_decode_is_single]

@@ -114,10 +114,35 @@ def m_decode_unrotated_query(mod):
     mod.rope = rope
 
 
+def m_chunk_position_shift(mod):
+    mod.chunk_positions = lambda start, n: np.arange(start + 1, start + 1 + n)
+
+
+def m_ragged_first_value(mod):
+    def per_sequence(values, B):
+        a = np.asarray(values, np.int64).reshape(-1)
+        return np.full(B, a[0], np.int64)
+    mod.per_sequence = per_sequence
+
+
+def m_cached_key_unrotated(mod):
+    orig = mod.cache_append
+
+    def cache_append(k_cache, v_cache, k_new, v_new, start, length=None, theta=mod.ROPE_THETA):
+        saved = mod.rope
+        mod.rope = lambda x, positions, theta=theta: np.asarray(x, np.float64)
+        try:
+            return orig(k_cache, v_cache, k_new, v_new, start, length, theta)
+        finally:
+            mod.rope = saved
+    mod.cache_append = cache_append
+
+
 MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
            m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
-           m_transposed_weights, m_softmax_no_norm, m_decode_unrotated_query]
+           m_transposed_weights, m_softmax_no_norm, m_decode_unrotated_query,
+           m_chunk_position_shift, m_ragged_first_value, m_cached_key_unrotated]
 
 
 def failing_pins(mod):
