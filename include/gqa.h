@@ -109,6 +109,72 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                int64_t kv_len, int64_t q_pos, double theta, float scale,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Autoregressive use around the path (walkthrough §4.1.3 closing note: the
+ * per-layer cache keeps only the h_kv groups' K and V, and every step
+ * appends the current token's K, V before attending).  The per-sequence
+ * arrays below are int64 device memory of B entries; the host cannot read
+ * them, so each call takes a host-side bound and the kernels check every
+ * entry against it: a sequence whose entries break the stated conditions
+ * gets NaN output rows and leaves the cache untouched, and no memory
+ * outside the buffers is accessed.
+ */
+
+/* Bytes of workspace gqa_prefill_chunk needs when no sequence ends after
+ * position kend - 1. */
+size_t gqa_prefill_chunk_workspace_size(int in_dtype, int64_t B, int64_t kend,
+                                        int h_kv, int d);
+
+/*
+ * Chunked causal prefill against the cache.  Sequence b brings len[b] new
+ * rows (len NULL: C each) at positions start[b] .. start[b] + len[b] - 1,
+ * laid out in q [B, C, h_q, d] and k/v [B, C, h_kv, d] (pre-RoPE, in_dtype);
+ * the cache [B, cap, h_kv, d] (in_dtype) already holds rows
+ * 0 .. start[b] - 1 (rotated K, as every call here writes it).  The call
+ * 1) rotates the new K rows at their positions and writes them with the new
+ *    V into cache rows start[b] + i,
+ * 2) lets new query i attend to cache rows 0 .. start[b] + i,
+ * and writes o [B, C, h_q, d] (out_dtype) rows i < len[b]; other rows are
+ * not written.  Conditions: 0 <= start[b], 0 <= len[b] <= C,
+ * start[b] + len[b] <= kend <= cap.  Splitting a prompt into chunks gives
+ * the rows of the one-shot gqa_prefill (up to rounding).
+ */
+int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o,
+                      int in_dtype, int out_dtype,
+                      int64_t B, int64_t C, int h_q, int h_kv, int d,
+                      const int64_t* start, const int64_t* len, int64_t kend,
+                      double theta, float scale,
+                      void* k_cache, void* v_cache, int64_t cap,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode with one length and one query position per sequence: q [B, h_q, d]
+ * (pre-RoPE) of sequence b, rotated at q_pos[b], attends to its cache rows
+ * 0 .. kv_len[b] - 1.  Conditions: 1 <= kv_len[b] <= max_kv_len <= cap and
+ * kv_len[b] <= q_pos[b] + 1.  Workspace: gqa_decode_workspace_size(..., cap).
+ */
+int gqa_decode_ragged(const void* q, const void* k_cache, const void* v_cache,
+                      void* o, int in_dtype, int out_dtype,
+                      int64_t B, int h_q, int h_kv, int d, int64_t cap,
+                      const int64_t* kv_len, const int64_t* q_pos,
+                      int64_t max_kv_len, double theta, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One autoregressive step with KV append: the new token of sequence b sits
+ * at position pos[b]; its K (k_new [B, h_kv, d], pre-RoPE, rotated at
+ * pos[b]) and V (v_new [B, h_kv, d]) are written to cache row pos[b], then
+ * its query (q [B, h_q, d], rotated at pos[b]) attends to rows 0 .. pos[b].
+ * Conditions: 0 <= pos[b] <= max_pos < cap.  Workspace as gqa_decode.
+ */
+int gqa_decode_append(const void* q, const void* k_new, const void* v_new,
+                      void* k_cache, void* v_cache, void* o,
+                      int in_dtype, int out_dtype,
+                      int64_t B, int h_q, int h_kv, int d, int64_t cap,
+                      const int64_t* pos, int64_t max_pos,
+                      double theta, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* gqa_last_error(void);
 
@@ -116,10 +182,10 @@ const char* gqa_last_error(void);
 const char* gqa_version(void);
 
 /*
- * Kernel timing for benchmarks.  While enabled, each gqa_prefill records a
- * HIP event pair around its attention kernel (which = 0) and each
- * gqa_decode around its split-K streaming kernel (which = 1), on the
- * caller's stream.  gqa_timing_read waits for the recorded events, returns
+ * Kernel timing for benchmarks.  While enabled, each gqa_prefill and
+ * gqa_prefill_chunk records a HIP event pair around its attention kernel
+ * (which = 0) and each decode call around its split-K streaming kernel
+ * (which = 1), on the caller's stream.  gqa_timing_read waits for the recorded events, returns
  * the summed milliseconds and the launch count for `which`, and clears
  * them.  Not thread-safe; meant for a single benchmarking thread.
  */

@@ -16,7 +16,8 @@ import torch
 
 from ._lib import (GQA_BF16, GQA_F32, GQAError, check, lib)
 
-__all__ = ["rope_apply", "prefill", "decode", "prefill_workspace_size",
+__all__ = ["rope_apply", "prefill", "decode", "prefill_chunk", "decode_ragged",
+           "decode_append", "prefill_workspace_size", "prefill_chunk_workspace_size",
            "decode_workspace_size", "timing_enable", "timing_read", "version",
            "GQAError", "ROPE_THETA"]
 
@@ -123,6 +124,117 @@ def decode(q, k_cache, v_cache, kv_len: int, q_pos: int, *, theta: float = ROPE_
     check(lib().gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _dt(q), _dt(out), B,
                            h_q, h_kv, d, cap, kv_len, q_pos, theta, scale, _ptr(workspace),
                            workspace.numel(), _stream()))
+    return out
+
+
+def _seq_array(x, B: int, device, what: str):
+    """Per-sequence int64 device array of B entries (a tensor or a sequence)."""
+    if x is None:
+        return None
+    t = x if isinstance(x, torch.Tensor) else torch.tensor(list(x), dtype=torch.int64)
+    if t.dtype != torch.int64 or t.numel() != B:
+        raise ValueError(f"{what} must hold B={B} int64 entries")
+    if not t.is_cuda:
+        t = t.to(device)
+    return t.contiguous()
+
+
+def _caches(k_cache, v_cache, B, h_kv, d, dtype):
+    cap = k_cache.shape[1]
+    for c in (k_cache, v_cache):
+        if c.dtype != dtype or c.shape != (B, cap, h_kv, d):
+            raise ValueError("k_cache/v_cache must both be [B, cap, h_kv, d] of the inputs' dtype")
+    return cap
+
+
+def prefill_chunk_workspace_size(dtype: torch.dtype, B: int, kend: int, h_kv: int, d: int) -> int:
+    return lib().gqa_prefill_chunk_workspace_size(_DT[dtype], B, kend, h_kv, d)
+
+
+def prefill_chunk(q, k, v, k_cache, v_cache, start, length=None, *, kend: int | None = None,
+                  theta: float = ROPE_THETA, scale: float | None = None,
+                  out_dtype: torch.dtype = torch.float32, out=None, workspace=None):
+    """Chunked causal prefill.  q [B, C, h_q, d], k/v [B, C, h_kv, d] (pre-RoPE)
+    are the new rows of each sequence, at positions start[b] + i for
+    i < length[b]; they are appended to the caches [B, cap, h_kv, d] and
+    attend to every cached row up to their own position.  kend bounds
+    start[b] + length[b] (default: cap).  Returns o [B, C, h_q, d]; rows
+    i >= length[b] are left as they were in ``out`` (uninitialised if None)."""
+    _dev(q, k, v, k_cache, v_cache, out, workspace)
+    B, C, h_q, d = q.shape
+    h_kv = k.shape[2]
+    if k.shape != (B, C, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k/v must be [B, C, h_kv, d] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    cap = _caches(k_cache, v_cache, B, h_kv, d, q.dtype)
+    kend = cap if kend is None else kend
+    st = _seq_array(start, B, q.device, "start")
+    ln = _seq_array(length, B, q.device, "length")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, C, h_q, d), dtype=out_dtype, device=q.device)
+    need = lib().gqa_prefill_chunk_workspace_size(_dt(q), B, kend, h_kv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    check(lib().gqa_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dt(q), _dt(out), B, C,
+                                  h_q, h_kv, d, _ptr(st), _ptr(ln), kend, theta, scale,
+                                  _ptr(k_cache), _ptr(v_cache), cap, _ptr(workspace),
+                                  workspace.numel(), _stream()))
+    return out
+
+
+def _decode_common(q, k_cache, v_cache, out, out_dtype, workspace, scale):
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    cap = _caches(k_cache, v_cache, B, h_kv, d, q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        need = lib().gqa_decode_workspace_size(B, h_q, h_kv, d, cap)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    return B, h_q, h_kv, d, cap, scale, out, workspace
+
+
+def decode_ragged(q, k_cache, v_cache, kv_len, q_pos, *, max_kv_len: int | None = None,
+                  theta: float = ROPE_THETA, scale: float | None = None,
+                  out_dtype: torch.dtype = torch.float32, out=None, workspace=None):
+    """Decode with per-sequence kv_len[b] and q_pos[b] (int64, B entries);
+    max_kv_len bounds kv_len (default: cap)."""
+    _dev(q, k_cache, v_cache, out, workspace)
+    B, h_q, h_kv, d, cap, scale, out, workspace = _decode_common(
+        q, k_cache, v_cache, out, out_dtype, workspace, scale)
+    kl = _seq_array(kv_len, B, q.device, "kv_len")
+    qp = _seq_array(q_pos, B, q.device, "q_pos")
+    max_kv_len = cap if max_kv_len is None else max_kv_len
+    check(lib().gqa_decode_ragged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _dt(q),
+                                  _dt(out), B, h_q, h_kv, d, cap, _ptr(kl), _ptr(qp), max_kv_len,
+                                  theta, scale, _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, pos, *, max_pos: int | None = None,
+                  theta: float = ROPE_THETA, scale: float | None = None,
+                  out_dtype: torch.dtype = torch.float32, out=None, workspace=None):
+    """One step with KV append: k_new/v_new [B, h_kv, d] (pre-RoPE) go to cache
+    row pos[b], then q [B, h_q, d] at pos[b] attends to rows 0..pos[b].
+    max_pos bounds pos (default: cap - 1)."""
+    _dev(q, k_new, v_new, k_cache, v_cache, out, workspace)
+    B, h_q, h_kv, d, cap, scale, out, workspace = _decode_common(
+        q, k_cache, v_cache, out, out_dtype, workspace, scale)
+    if k_new.shape != (B, h_kv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, h_kv, d]")
+    if not (q.dtype == k_new.dtype == v_new.dtype):
+        raise TypeError("q, k_new and v_new must share one dtype")
+    ps = _seq_array(pos, B, q.device, "pos")
+    max_pos = cap - 1 if max_pos is None else max_pos
+    check(lib().gqa_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(out), _dt(q), _dt(out), B, h_q, h_kv, d,
+                                  cap, _ptr(ps), max_pos, theta, scale, _ptr(workspace),
+                                  workspace.numel(), _stream()))
     return out
 
 

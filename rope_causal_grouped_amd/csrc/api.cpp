@@ -202,19 +202,22 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     float* kmax = (float*)(wsb + ws.kmax_off);
     e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, cs, kp, vt, kmax,
                                     (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad, h_kv, d,
-                                    cap, st);
+                                    cap, L, nullptr, nullptr, L, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     if (ev.first) (void)hipEventRecord(ev.first, st);
     e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, cs, o, out_dtype == GQA_BF16, B, L,
-                                 Lpad, h_q, h_kv, d, scale, causal, st);
+                                 Lpad, h_q, h_kv, d, scale, causal, nullptr, nullptr, L, st);
   } else {
     float* kp = (float*)(wsb + ws.kp_off);
     e = gqa::launch_kv_prepare_f32((const float*)k, (const float*)v, cs, kp, (float*)k_cache,
                                    (float*)v_cache, B, L, h_kv, d, cap, st);
     if (e != hipSuccess) return hip_fail(e, "K preparation launch");
     if (ev.first) (void)hipEventRecord(ev.first, st);
+    const gqa::KvStrides ksd{(int64_t)h_kv * L * d, L * d, d};          // [B][h_kv][L][d]
+    const gqa::KvStrides vsd{L * h_kv * d, d, (int64_t)h_kv * d};       // [B, L, h_kv, d]
     e = gqa::launch_prefill_f32((const float*)q, kp, (const float*)v, cs, o,
-                                out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, st);
+                                out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, ksd, vsd,
+                                nullptr, nullptr, L, st);
   }
   if (ev.second) {
     (void)hipEventRecord(ev.second, st);
@@ -264,11 +267,187 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   if (g_timing.on) ev = g_timing.take();
   hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
                                     out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, kv_len, q_pos,
-                                    std::log2(theta), scale, (float*)(wsb + ws.m_off),
+                                    nullptr, nullptr, 0, std::log2(theta), scale,
+                                    (float*)(wsb + ws.m_off),
                                     (float*)(wsb + ws.l_off), (float*)(wsb + ws.o_off),
                                     (hipStream_t)stream, ev.first, ev.second);
   if (ev.first) g_timing.rec[1].push_back(ev);
   return e == hipSuccess ? GQA_OK : hip_fail(e, "decode launch");
+}
+
+size_t gqa_prefill_chunk_workspace_size(int in_dtype, int64_t B, int64_t kend, int h_kv, int d) {
+  if (!dtype_ok(in_dtype) || B < 1 || kend < 1 || h_kv < 1 || d < 2) return 0;
+  const PrefillWs w = prefill_ws(in_dtype, B, kend, h_kv, d);
+  return in_dtype == GQA_BF16 ? w.total : w.kp_off;   // fp32 chunks read K from the cache
+}
+
+int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int in_dtype,
+                      int out_dtype, int64_t B, int64_t C, int h_q, int h_kv, int d,
+                      const int64_t* start, const int64_t* len, int64_t kend, double theta,
+                      float scale, void* k_cache, void* v_cache, int64_t cap, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!q || !k || !v || !o || !start || !k_cache || !v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "q, k, v, o, start, k_cache and v_cache must be non-NULL");
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in=%d, out=%d)", in_dtype, out_dtype);
+  if (B < 1 || C < 1) return fail(GQA_ERR_INVALID_ARG, "B and C must be >= 1");
+  if (int rc = check_heads(h_q, h_kv)) return rc;
+  if (int rc = check_d(d)) return rc;
+  if (int rc = check_theta_scale(theta, scale)) return rc;
+  if (kend < 1 || kend > cap)
+    return fail(GQA_ERR_INVALID_ARG, "kend=%lld outside [1, cap=%lld]", (long long)kend,
+                (long long)cap);
+  const int g = h_q / h_kv;
+  if (C * g + gqa::kPrefillRowsWG > INT_MAX || B * h_kv > 65535 || kend > (INT64_C(1) << 24))
+    return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
+  const int64_t n_rb = (C * g + gqa::kPrefillRowsWG - 1) / gqa::kPrefillRowsWG;
+  if (n_rb * B * h_kv > INT_MAX) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(workspace))
+    return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const size_t need = gqa_prefill_chunk_workspace_size(in_dtype, B, kend, h_kv, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  const PrefillWs ws = prefill_ws(in_dtype, B, kend, h_kv, d);
+  float2* cs = (float2*)(wsb + ws.cs_off);
+  const double l2t = std::log2(theta);
+  hipError_t e = gqa::launch_rope_table(cs, kend, d, 0, l2t, st);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  // 1) the chunk's rotated K and its V into the cache rows start[b] + i
+  e = gqa::launch_cache_append(k, v, k_cache, v_cache, in_dtype == GQA_BF16, start, len, B, C,
+                               h_kv, d, cap, kend, l2t, st);
+  if (e != hipSuccess) return hip_fail(e, "cache append launch");
+
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (g_timing.on) ev = g_timing.take();
+  if (in_dtype == GQA_BF16) {
+    // 2) keys 0 .. start[b] + len[b] - 1 of the cache into the attention layout
+    const int64_t Lpad = prefill_lpad(kend);
+    uint16_t* kp = (uint16_t*)(wsb + ws.kp_off);
+    uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
+    float* kmax = (float*)(wsb + ws.kmax_off);
+    e = gqa::launch_kv_prepare_bf16((const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
+                                    kp, vt, kmax, nullptr, nullptr, B, C, Lpad, h_kv, d, cap, cap,
+                                    start, len, kend, st);
+    if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
+    // 3) the chunk's queries against them
+    if (ev.first) (void)hipEventRecord(ev.first, st);
+    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, cs, o, out_dtype == GQA_BF16, B,
+                                 C, Lpad, h_q, h_kv, d, scale, 1, start, len, kend, st);
+  } else {
+    // 2) the chunk's queries against the cache itself
+    const gqa::KvStrides csd{cap * h_kv * d, d, (int64_t)h_kv * d};   // [B, cap, h_kv, d]
+    if (ev.first) (void)hipEventRecord(ev.first, st);
+    e = gqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache, cs,
+                                o, out_dtype == GQA_BF16, B, C, h_q, h_kv, d, scale, 1, csd, csd,
+                                start, len, kend, st);
+  }
+  if (ev.second) {
+    (void)hipEventRecord(ev.second, st);
+    g_timing.rec[0].push_back(ev);
+  }
+  return e == hipSuccess ? GQA_OK : hip_fail(e, "chunked prefill launch");
+}
+
+namespace {
+
+// host checks shared by the ragged decode entry points
+int decode_ragged_check(const void* q, const void* k_cache, const void* v_cache, void* o,
+                        int in_dtype, int out_dtype, int64_t B, int h_q, int h_kv, int d,
+                        int64_t cap, int64_t max_kv_len, double theta, float scale,
+                        void* workspace, size_t workspace_bytes) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in=%d, out=%d)", in_dtype, out_dtype);
+  if (B < 1) return fail(GQA_ERR_INVALID_ARG, "B must be >= 1");
+  if (int rc = check_heads(h_q, h_kv)) return rc;
+  if (int rc = check_d(d)) return rc;
+  if (int rc = check_theta_scale(theta, scale)) return rc;
+  if (cap < 1) return fail(GQA_ERR_INVALID_ARG, "cap must be >= 1");
+  if (max_kv_len < 1 || max_kv_len > cap)
+    return fail(GQA_ERR_INVALID_ARG, "longest sequence %lld outside [1, cap=%lld]",
+                (long long)max_kv_len, (long long)cap);
+  if (cap > (INT64_C(1) << 30) || B > 65535 || h_q > 65535 ||
+      gqa::decode_num_splits(cap) > gqa::kDecodeMaxSplitsLds)
+    return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(workspace))
+    return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const DecodeWs ws = decode_ws(B, h_q, h_kv, d, cap);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                workspace ? workspace_bytes : (size_t)0);
+  return GQA_OK;
+}
+
+// dispatch of a checked ragged decode
+int decode_ragged_launch(const void* q, const void* k_cache, const void* v_cache, void* o,
+                         int in_dtype, int out_dtype, int64_t B, int h_q, int h_kv, int d,
+                         int64_t cap, const int64_t* kvl, const int64_t* qpos, int from_pos,
+                         int64_t max_kv_len, double theta, float scale, void* workspace,
+                         hipStream_t st) {
+  const DecodeWs ws = decode_ws(B, h_q, h_kv, d, cap);
+  char* wsb = (char*)workspace;
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (g_timing.on) ev = g_timing.take();
+  hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
+                                    out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, max_kv_len, 0,
+                                    kvl, qpos, from_pos, std::log2(theta), scale,
+                                    (float*)(wsb + ws.m_off), (float*)(wsb + ws.l_off),
+                                    (float*)(wsb + ws.o_off), st, ev.first, ev.second);
+  if (ev.first) g_timing.rec[1].push_back(ev);
+  return e == hipSuccess ? GQA_OK : hip_fail(e, "decode launch");
+}
+
+}  // namespace
+
+int gqa_decode_ragged(const void* q, const void* k_cache, const void* v_cache, void* o,
+                      int in_dtype, int out_dtype, int64_t B, int h_q, int h_kv, int d,
+                      int64_t cap, const int64_t* kv_len, const int64_t* q_pos,
+                      int64_t max_kv_len, double theta, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!q || !k_cache || !v_cache || !o || !kv_len || !q_pos)
+    return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache, o, kv_len and q_pos must be non-NULL");
+  if (int rc = decode_ragged_check(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d,
+                                   cap, max_kv_len, theta, scale, workspace, workspace_bytes))
+    return rc;
+  return decode_ragged_launch(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap,
+                              kv_len, q_pos, 0, max_kv_len, theta, scale, workspace,
+                              (hipStream_t)stream);
+}
+
+int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, void* o, int in_dtype, int out_dtype, int64_t B, int h_q,
+                      int h_kv, int d, int64_t cap, const int64_t* pos, int64_t max_pos,
+                      double theta, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_err.clear();
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !o || !pos)
+    return fail(GQA_ERR_INVALID_ARG,
+                "q, k_new, v_new, k_cache, v_cache, o and pos must be non-NULL");
+  if (max_pos < 0 || max_pos >= cap)
+    return fail(GQA_ERR_INVALID_ARG, "max_pos=%lld outside [0, cap=%lld)", (long long)max_pos,
+                (long long)cap);
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  // everything the decode checks, before the cache is touched
+  if (int rc = decode_ragged_check(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d,
+                                   cap, max_pos + 1, theta, scale, workspace, workspace_bytes))
+    return rc;
+  hipStream_t st = (hipStream_t)stream;
+  // 1) the new token's rotated K and its V into cache row pos[b]
+  hipError_t e = gqa::launch_cache_append(k_new, v_new, k_cache, v_cache, in_dtype == GQA_BF16,
+                                          pos, nullptr, B, 1, h_kv, d, cap, max_pos + 1,
+                                          std::log2(theta), st);
+  if (e != hipSuccess) return hip_fail(e, "cache append launch");
+  // 2) attend to rows 0 .. pos[b]
+  return decode_ragged_launch(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap,
+                              nullptr, pos, 1, max_pos + 1, theta, scale, workspace, st);
 }
 
 int gqa_timing_enable(int on) {

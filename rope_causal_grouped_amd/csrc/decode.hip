@@ -13,11 +13,39 @@
 //   M = max_s m_s,  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
 // which equals the unsplit softmax exactly (up to rounding).  Maxima are
 // kept in the log2 domain (scores pre-multiplied by scale * log2 e).
+//
+// Ragged batches: with qpos_arr set, sequence b has its own query position
+// qpos_arr[b] and length kvl_arr[b] (or qpos_arr[b] + 1 when the step has
+// just appended its own row); kv_len is then the largest allowed length and
+// sets the number of chunks.  Chunks past a sequence's length leave an empty
+// state (m = -inf, l = 0, o = 0) that the merge weighs with zero.  A
+// sequence whose length or position is out of range has no keys at all and
+// its output becomes NaN.
 
 #include "common.h"
 #include "launch.h"
 
 namespace gqa {
+
+namespace {
+
+// per-sequence (kv_len, q_pos); kv_len = 0 marks an invalid sequence
+struct SeqLen {
+  int kv_len;
+  double q_pos;
+};
+
+__device__ __forceinline__ SeqLen seq_len(int b, int kv_len, double q_pos,
+                                          const int64_t* __restrict__ kvl_arr,
+                                          const int64_t* __restrict__ qpos_arr, int kvl_from_pos) {
+  if (!qpos_arr) return {kv_len, q_pos};
+  const int64_t qp = qpos_arr[b];
+  const int64_t kl = kvl_from_pos ? qp + 1 : kvl_arr[b];
+  const bool ok = kl >= 1 && kl <= kv_len && qp >= kl - 1 && qp <= (INT64_C(1) << 40);
+  return {ok ? (int)kl : 0, (double)qp};
+}
+
+}  // namespace
 
 int decode_num_splits(int64_t kv_len) {
   return (int)((kv_len + kDecodeChunk - 1) / kDecodeChunk);
@@ -35,8 +63,9 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int64_t cap, int kv_len,
-    double q_pos, double log2_theta, float sl2, int n_split) {
+    float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int64_t cap, int kv_len_max,
+    double q_pos_s, double log2_theta, float sl2, int n_split, const int64_t* __restrict__ kvl_arr,
+    const int64_t* __restrict__ qpos_arr, int kvl_from_pos) {
   constexpr int CH = kDecodeChunk;
   constexpr int WK = CH / 4;            // keys per wave
   constexpr int NS = D / 32;            // 32-dim k-steps of S^T
@@ -53,6 +82,22 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h4 = lane >> 4;
   const int c = hb * 16 + col;
+  const SeqLen sq = seq_len(b, kv_len_max, q_pos_s, kvl_arr, qpos_arr, kvl_from_pos);
+  const int kv_len = sq.kv_len;
+  const double q_pos = sq.q_pos;
+  if (split * CH >= kv_len) {   // chunk past this sequence's keys: empty state
+    for (int idx = tid; idx < 16 * D; idx += 256) {
+      const int cc = idx / D, dim = idx % D;
+      if (hb * 16 + cc >= g) continue;
+      const int64_t out = (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16 + cc;
+      po[out * D + dim] = 0.f;
+      if (dim == 0) {
+        pm[out] = -INFINITY;
+        pl[out] = 0.f;
+      }
+    }
+    return;
+  }
 
   // ---- rotated query, B operand: lane holds head `col`, dims s*32 + h4*8 + e
   bf16x8 qb[NS];
@@ -209,8 +254,9 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po, int h_q, int h_kv,
-    int g, int n_hb, int64_t cap, int kv_len, double q_pos, double log2_theta, float scale,
-    int n_split) {
+    int g, int n_hb, int64_t cap, int kv_len_max, double q_pos_s, double log2_theta, float scale,
+    int n_split, const int64_t* __restrict__ kvl_arr, const int64_t* __restrict__ qpos_arr,
+    int kvl_from_pos) {
   constexpr int CH = kDecodeChunk;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float qs[16][D];
@@ -220,6 +266,22 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int nh = min(16, g - hb * 16);
+  const SeqLen sq = seq_len(b, kv_len_max, q_pos_s, kvl_arr, qpos_arr, kvl_from_pos);
+  const int kv_len = sq.kv_len;
+  const double q_pos = sq.q_pos;
+  if (split * CH >= kv_len) {   // chunk past this sequence's keys: empty state
+    for (int idx = tid; idx < 16 * D; idx += 256) {
+      const int cc = idx / D, dim = idx % D;
+      if (cc >= nh) continue;
+      const int64_t out = (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16 + cc;
+      po[out * D + dim] = 0.f;
+      if (dim == 0) {
+        pm[out] = -INFINITY;
+        pl[out] = 0.f;
+      }
+    }
+    return;
+  }
 
   for (int idx = tid; idx < 16 * (D / 2); idx += 256) {
     const int cc = idx / (D / 2), j = idx % (D / 2);
@@ -336,8 +398,9 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restri
 
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, int in_bf16,
                          int out_bf16, int64_t B, int h_q, int h_kv, int d, int64_t cap,
-                         int64_t kv_len, int64_t q_pos, double log2_theta, float scale,
-                         float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
+                         int64_t kv_len, int64_t q_pos, const int64_t* kvl_arr,
+                         const int64_t* qpos_arr, int kvl_from_pos, double log2_theta,
+                         float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end) {
   const int g = h_q / h_kv;
   const int n_hb = (g + 15) / 16;
@@ -349,20 +412,24 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
     if (d == 128)
       decode_split_bf16_kernel<128><<<grid, 256, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
-          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split);
+          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split, kvl_arr,
+          qpos_arr, kvl_from_pos);
     else
       decode_split_bf16_kernel<64><<<grid, 256, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
-          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split);
+          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split, kvl_arr,
+          qpos_arr, kvl_from_pos);
   } else {
     if (d == 128)
       decode_split_f32_kernel<128><<<grid, 256, 0, st>>>(
           (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
-          n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split);
+          n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split, kvl_arr, qpos_arr,
+          kvl_from_pos);
     else
       decode_split_f32_kernel<64><<<grid, 256, 0, st>>>(
           (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
-          n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split);
+          n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split, kvl_arr, qpos_arr,
+          kvl_from_pos);
   }
   hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, st);

@@ -82,7 +82,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float2* __restrict__ cs, void* __restrict__ o, int L, int Lpad, int h_q, int h_kv,
-    int g, int n_rb, int n_bu, float sl2, int causal) {
+    int g, int n_rb, float sl2, int causal, const int64_t* __restrict__ qstart,
+    const int64_t* __restrict__ qlen, int kend) {
   constexpr int NS = D / 16;                  // 16-dim k-steps of S^T
   constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
   constexpr int NPV = 4 * NDB;                // P.V MFMAs per tile
@@ -120,26 +121,50 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int bu = w / n_rb;
   const int rb = n_rb - 1 - (w - bu * n_rb);
   const int b = bu / h_kv, u = bu % h_kv;
-
-  const int rows_total = L * g;
   const int R0 = rb * ROWS;
+
+  // Queries of sequence b: rows i < nq of q[b] (row stride L), at positions
+  // qs + i.  qs = 0, nq = L for a whole prompt; with qstart set this is a
+  // chunk whose keys 0 .. qs + nq - 1 were prepared from the cache (causal
+  // only).  A sequence whose chunk is out of range gets NaN rows.
+  int qs = 0, nq = L;
+  if (qstart) {
+    const int64_t s0 = qstart[b], n = qlen ? qlen[b] : L;
+    if (!(s0 >= 0 && n >= 0 && n <= L && s0 + n <= kend)) {
+      for (int e = tid; e < ROWS * D; e += NW * 64) {
+        const int r = R0 + e / D;
+        if (r < L * g) {
+          const int64_t oo = ((int64_t)((int64_t)b * L + r / g) * h_q + u * g + r % g) * D + e % D;
+          if constexpr (OUT_BF16) ((uint16_t*)o)[oo] = 0x7fc0u;
+          else ((float*)o)[oo] = __builtin_nanf("");
+        }
+      }
+      return;
+    }
+    qs = (int)s0;
+    nq = (int)n;
+  }
+  const int nk = causal ? qs + nq : L;   // keys of the sequence
+  const int rows_total = nq * g;
+  if (R0 >= rows_total) return;          // the whole row block lies past this sequence's rows
   const int row = R0 + wave * RW + c32;
   const bool row_valid = row < rows_total;
   const int rr = row_valid ? row : rows_total - 1;
-  const int pos = rr / g;
-  const int head = u * g + (rr - pos * g);
+  const int pl = rr / g;                 // row of q / o
+  const int pos = qs + pl;               // its position
+  const int head = u * g + (rr - pl * g);
 
   // ---- key range
   const int rmax = min(R0 + ROWS - 1, rows_total - 1);
-  const int n_keys = causal ? rmax / g + 1 : L;
+  const int n_keys = causal ? qs + rmax / g + 1 : L;
   const int n_tiles = (n_keys + TK - 1) / TK;
   const int wr0 = min(R0 + wave * RW, rows_total - 1);
   const int wr1 = min(R0 + wave * RW + RW - 1, rows_total - 1);
-  const int wpos_lo = wr0 / g, wpos_hi = wr1 / g;
-  const int lim = causal ? min(pos, L - 1) : L - 1;   // last key this row may see
+  const int wpos_lo = qs + wr0 / g, wpos_hi = qs + wr1 / g;
+  const int lim = causal ? min(pos, nk - 1) : nk - 1;   // last key this row may see
   // tile i has keys this wave may see / needs the element mask
   auto active = [&](int i) { return !causal || i * TK <= wpos_hi; };
-  auto masked = [&](int i) { return (causal && i * TK + TK - 1 > wpos_lo) || (i * TK + TK > L); };
+  auto masked = [&](int i) { return (causal && i * TK + TK - 1 > wpos_lo) || (i * TK + TK > nk); };
 
   // ---- direct HBM -> LDS tile loads by one wave group.  Instruction n of
   // wave w (of the group) fills LDS chunks [(w*LPG + n)*64, +64); lane l's
@@ -195,7 +220,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // holds dims s*16 + hl*8 + e of its row; RoPE pairs are (s, s + NS/2)).
   bf16x8 qb[NS];
   {
-    const uint16_t* qrow = q + ((int64_t)((int64_t)b * L + pos) * h_q + head) * D;
+    const uint16_t* qrow = q + ((int64_t)((int64_t)b * L + pl) * h_q + head) * D;
     u32x4 raw[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) raw[s] = *(const u32x4*)(qrow + s * 16 + hl * 8);
@@ -444,7 +469,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // ---- epilogue: O = O / l; lane holds dims db*32 + gq*8 + hl*4 + (0..3)
   const float inv = 1.0f / sum_xor32(l_run);
   if (row_valid) {
-    const int64_t orow = ((int64_t)((int64_t)b * L + pos) * h_q + head) * D;
+    const int64_t orow = ((int64_t)((int64_t)b * L + pl) * h_q + head) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -468,7 +493,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
                                const float* kmax, const float2* cs, void* o, int out_bf16,
                                int64_t B, int64_t L, int64_t Lpad, int h_q, int h_kv, int d,
-                               float scale, int causal, hipStream_t st) {
+                               float scale, int causal, const int64_t* qstart,
+                               const int64_t* qlen, int64_t kend, hipStream_t st) {
   const int g = h_q / h_kv;
   const int n_rb = (int)((L * g + kPrefillRowsWG - 1) / kPrefillRowsWG);
   const int n_bu = (int)(B * h_kv);
@@ -476,8 +502,8 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   const unsigned grid = (unsigned)((int64_t)n_rb * n_bu);
 #define GQA_LAUNCH(DD, OB)                                                                    \
   prefill_bf16_kernel<DD, OB><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, cs, o, (int)L,      \
-                                                        (int)Lpad, h_q, h_kv, g, n_rb, n_bu, \
-                                                        sl2, causal)
+                                                        (int)Lpad, h_q, h_kv, g, n_rb, sl2,  \
+                                                        causal, qstart, qlen, (int)kend)
   if (d == 128) {
     if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);
   } else {

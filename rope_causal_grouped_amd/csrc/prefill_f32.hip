@@ -8,7 +8,11 @@
 // one query head; four lanes share a row, each holding a quarter of its dims
 // (dims j and j + d/2 of a RoPE pair stay in one lane).  K' (rotated by the
 // preparation pass) and V tiles of 64 keys are staged in LDS and shared by
-// the 64 rows; the softmax is updated key by key.
+// the 64 rows; the softmax is updated key by key.  Keys and values are read
+// through strides, so they may come from the preparation pass (rotated K,
+// [B][h_kv][L][d]) and the call's V, or straight from a per-layer cache
+// [B, cap, h_kv, d] when a chunk of queries at positions qstart[b] + i
+// attends to everything cached so far.
 
 #include "common.h"
 #include "launch.h"
@@ -19,7 +23,8 @@ template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ v,
     const float2* __restrict__ cs, void* __restrict__ o, int L, int h_q, int h_kv, int g,
-    float scale, int causal) {
+    float scale, int causal, KvStrides ks_, KvStrides vs_, const int64_t* __restrict__ qstart,
+    const int64_t* __restrict__ qlen, int kend) {
   constexpr int TK = 64;
   constexpr int E = D / 8;  // pair count per lane
   __shared__ float ks[TK][D + 4];
@@ -28,14 +33,36 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   const int pbk = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int u = t / g;
   const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
-  const int pos_raw = pbk * TK + row;
-  const bool valid = pos_raw < L;
-  const int pos = valid ? pos_raw : L - 1;
+
+  // queries i < nq of sequence b at positions qs + i; keys 0 .. nk-1
+  int qs = 0, nq = L;
+  if (qstart) {
+    const int64_t s0 = qstart[b], n = qlen ? qlen[b] : L;
+    if (!(s0 >= 0 && n >= 0 && n <= L && s0 + n <= kend)) {   // out of range: NaN rows
+      const int pr = pbk * TK + row;
+      if (pr < L) {
+        const int64_t orow = ((int64_t)((int64_t)b * L + pr) * h_q + t) * D;
+        for (int e = part; e < D; e += 4) {
+          if constexpr (OUT_BF16) ((uint16_t*)o)[orow + e] = 0x7fc0u;
+          else ((float*)o)[orow + e] = __builtin_nanf("");
+        }
+      }
+      return;
+    }
+    qs = (int)s0;
+    nq = (int)n;
+  }
+  if (pbk * TK >= nq) return;
+  const int nk = causal ? qs + nq : L;
+  const int pl_raw = pbk * TK + row;
+  const bool valid = pl_raw < nq;
+  const int pl = valid ? pl_raw : nq - 1;   // row of q / o
+  const int pos = qs + pl;                  // its position
 
   // rotated query slice: qr[e] = dim part*E + e, qr[E + e] = dim D/2 + part*E + e
   float qr[2 * E];
   {
-    const float* src = q + ((int64_t)((int64_t)b * L + pos) * h_q + t) * D;
+    const float* src = q + ((int64_t)((int64_t)b * L + pl) * h_q + t) * D;
     const float2* csr = cs + (int64_t)pos * (D / 2);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -52,9 +79,10 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   for (int e = 0; e < 2 * E; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const int last_row_pos = min(L - 1, pbk * TK + TK - 1);
+  const int last_row_pos = qs + min(nq - 1, pbk * TK + TK - 1);
   const int n_keys = causal ? last_row_pos + 1 : L;
-  const float* kbase = kp + ((int64_t)b * h_kv + u) * (int64_t)L * D;
+  const float* kbase = kp + (int64_t)b * ks_.batch + (int64_t)u * ks_.head;
+  const float* vbase = v + (int64_t)b * vs_.batch + (int64_t)u * vs_.head;
 
   for (int k0 = 0; k0 < n_keys; k0 += TK) {
     __syncthreads();
@@ -62,16 +90,16 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
       const int kk = idx / D, dd = idx % D;
       const int key = k0 + kk;
       float kv = 0.f, vv = 0.f;
-      if (key < L) {
-        kv = kbase[(int64_t)key * D + dd];
-        vv = v[(((int64_t)b * L + key) * h_kv + u) * D + dd];
+      if (key < nk) {
+        kv = kbase[(int64_t)key * ks_.row + dd];
+        vv = vbase[(int64_t)key * vs_.row + dd];
       }
       ks[kk][dd] = kv;
       vs[kk][dd] = vv;
     }
     __syncthreads();
-    const int nk = min(TK, n_keys - k0);
-    for (int jj = 0; jj < nk; ++jj) {
+    const int ntile = min(TK, n_keys - k0);
+    for (int jj = 0; jj < ntile; ++jj) {
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -99,7 +127,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 
   if (valid) {
     const float inv = 1.0f / l;
-    const int64_t orow = ((int64_t)((int64_t)b * L + pos) * h_q + t) * D;
+    const int64_t orow = ((int64_t)((int64_t)b * L + pl) * h_q + t) * D;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = part * E + e;
@@ -116,12 +144,14 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 
 hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, const float2* cs,
                               void* o, int out_bf16, int64_t B, int64_t L, int h_q, int h_kv,
-                              int d, float scale, int causal, hipStream_t st) {
+                              int d, float scale, int causal, KvStrides ks, KvStrides vs,
+                              const int64_t* qstart, const int64_t* qlen, int64_t kend,
+                              hipStream_t st) {
   const int g = h_q / h_kv;
   dim3 grid((unsigned)((L + 63) / 64), (unsigned)h_q, (unsigned)B);
 #define GQA_LAUNCH(DD, OB)                                                                   \
   prefill_f32_kernel<DD, OB><<<grid, 256, 0, st>>>(q, kp, v, cs, o, (int)L, h_q, h_kv, g, scale, \
-                                                   causal)
+                                                   causal, ks, vs, qstart, qlen, (int)kend)
   if (d == 128) {
     if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);
   } else {

@@ -97,13 +97,18 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double 
 //                      the order in which one lane of the 32x32 score
 //                      accumulator holds them.
 // Rows past L are zero.  If kc/vc are set, the rotated K and the V rows are
-// also written to the per-layer cache [B, cap, h_kv, d].
+// also written to the per-layer cache [B, cap, h_kv, d].  The source rows of
+// sequence b start at k + b * src_rows * h_kv * d (src_rows = L for the
+// call's own K/V, cap for a cache).  With kstart set, sequence b has
+// kstart[b] + klen[b] rows (0 if that is not within [0, kend]); with cs NULL
+// the source K is taken as already rotated (a cache).
 template <int D>
 __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float2* __restrict__ cs,
     uint16_t* __restrict__ kp, uint16_t* __restrict__ vt, float* __restrict__ kmax,
     uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t L, int64_t Lpad, int h_kv,
-    int64_t cap) {
+    int64_t cap, int64_t src_rows, const int64_t* __restrict__ kstart,
+    const int64_t* __restrict__ klen, int64_t kend) {
   constexpr int TK = 64;
   constexpr int HALF = D / 2;
   constexpr int PP = HALF / 4;        // RoPE pairs per thread: 4 threads per key row
@@ -113,28 +118,41 @@ __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
   const int tile = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t key0 = (int64_t)tile * TK;
-
-  // ---- K: thread (row tid/4, quarter tid%4) rotates pairs q*PP .. q*PP+PP-1
+  if (kstart) {   // keys of sequence b: rows 0 .. kstart[b] + klen[b] - 1 of the source
+    const int64_t s0 = kstart[b], n = klen ? klen[b] : L;
+    L = (s0 >= 0 && n >= 0 && n <= L && s0 + n <= kend) ? s0 + n : 0;
+  }
   {
     const int kk = tid >> 2, part = tid & 3;
     const int64_t key = key0 + kk;
     uint16_t o1[PP], o2[PP];
     float ss = 0.f;
     if (key < L) {
-      const uint16_t* src = k + (((int64_t)b * L + key) * h_kv + u) * D + part * PP;
+      const uint16_t* src = k + (((int64_t)b * src_rows + key) * h_kv + u) * D + part * PP;
       uint16_t x1[PP], x2[PP];
 #pragma unroll
       for (int c = 0; c < PP / 8; ++c) {
         *(u32x4*)&x1[c * 8] = *(const u32x4*)(src + c * 8);
         *(u32x4*)&x2[c * 8] = *(const u32x4*)(src + HALF + c * 8);
       }
-      const float2* csr = cs + key * HALF + part * PP;
+      if (cs) {   // rotate here; otherwise the source rows are rotated already
+        const float2* csr = cs + key * HALF + part * PP;
+#pragma unroll
+        for (int e = 0; e < PP; ++e) {
+          const float2 r = csr[e];
+          const float a = bf16_bits_to_f32(x1[e]), bb = bf16_bits_to_f32(x2[e]);
+          o1[e] = f32_to_bf16_bits(fmaf(a, r.x, -bb * r.y));
+          o2[e] = f32_to_bf16_bits(fmaf(bb, r.x, a * r.y));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < PP; ++e) {
+          o1[e] = x1[e];
+          o2[e] = x2[e];
+        }
+      }
 #pragma unroll
       for (int e = 0; e < PP; ++e) {
-        const float2 r = csr[e];
-        const float a = bf16_bits_to_f32(x1[e]), bb = bf16_bits_to_f32(x2[e]);
-        o1[e] = f32_to_bf16_bits(fmaf(a, r.x, -bb * r.y));
-        o2[e] = f32_to_bf16_bits(fmaf(bb, r.x, a * r.y));
         const float y1 = bf16_bits_to_f32(o1[e]), y2 = bf16_bits_to_f32(o2[e]);
         ss = fmaf(y1, y1, fmaf(y2, y2, ss));
       }
@@ -170,7 +188,7 @@ __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
     const int64_t key = key0 + kk;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (key < L) {
-      val = *(const u32x4*)(v + (((int64_t)b * L + key) * h_kv + u) * D + c8 * 8);
+      val = *(const u32x4*)(v + (((int64_t)b * src_rows + key) * h_kv + u) * D + c8 * 8);
       if (vc) *(u32x4*)(vc + (((int64_t)b * cap + key) * h_kv + u) * D + c8 * 8) = val;
     }
     *(u32x4*)&vs[kk][c8 * 8] = val;
@@ -240,14 +258,77 @@ __global__ __launch_bounds__(256) void kv_prepare_f32_kernel(
 hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
                                   uint16_t* kp, uint16_t* vt, float* kmax, uint16_t* kc,
                                   uint16_t* vc, int64_t B, int64_t L, int64_t Lpad, int h_kv, int d,
-                                  int64_t cap, hipStream_t st) {
+                                  int64_t cap, int64_t src_rows, const int64_t* kstart,
+                                  const int64_t* klen, int64_t kend, hipStream_t st) {
   dim3 grid((unsigned)(Lpad / 64), (unsigned)h_kv, (unsigned)B);
   if (d == 128)
     kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kc, vc, L, Lpad,
-                                                      h_kv, cap);
+                                                      h_kv, cap, src_rows, kstart, klen, kend);
   else
     kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kc, vc, L, Lpad,
-                                                     h_kv, cap);
+                                                     h_kv, cap, src_rows, kstart, klen, kend);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Cache append (the per-layer cache keeps the h_kv groups' rotated K and V,
+// appended every step: walkthrough §4.1.3 closing note).  New rows
+// k/v[B, C, h_kv, d]; row i < len[b] (len NULL: C) of sequence b sits at
+// position p = start[b] + i: kc[b][p][u] = RoPE(k[b][i][u], p) and
+// vc[b][p][u] = v[b][i][u].  A sequence whose rows would not lie within
+// [0, end) (end <= cap, checked by the caller) is skipped.  One thread per
+// (row, head, pair j): it rotates dims j, j + d/2 and copies them of V.
+template <typename T>
+__global__ __launch_bounds__(256) void cache_append_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ kc, T* __restrict__ vc,
+    const int64_t* __restrict__ start, const int64_t* __restrict__ len, int64_t n_pairs,
+    int64_t C, int h_kv, int d, int64_t cap, int64_t end, double log2_theta) {
+  const int half = d >> 1;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_pairs;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = idx / half;            // (b, i, u)
+    const int j = (int)(idx - row * half);
+    const int u = (int)(row % h_kv);
+    const int64_t bi = row / h_kv;
+    const int64_t i = bi % C, b = bi / C;
+    const int64_t s0 = start[b], n = len ? len[b] : C;
+    if (!(s0 >= 0 && n >= 0 && n <= C && s0 + n <= end) || i >= n) continue;
+    const int64_t p = s0 + i;
+    float c, s;
+    rope_cos_sin((double)p, rope_omega(j, d, log2_theta), c, s);
+    const T* kr = k + row * d;
+    const T* vr = v + row * d;
+    T* kd = kc + ((b * cap + p) * h_kv + u) * d;
+    T* vd = vc + ((b * cap + p) * h_kv + u) * d;
+    if constexpr (sizeof(T) == 2) {
+      const float x1 = bf16_bits_to_f32(kr[j]), x2 = bf16_bits_to_f32(kr[j + half]);
+      kd[j] = f32_to_bf16_bits(fmaf(x1, c, -x2 * s));
+      kd[j + half] = f32_to_bf16_bits(fmaf(x2, c, x1 * s));
+    } else {
+      const float x1 = kr[j], x2 = kr[j + half];
+      kd[j] = fmaf(x1, c, -x2 * s);
+      kd[j + half] = fmaf(x2, c, x1 * s);
+    }
+    vd[j] = vr[j];
+    vd[j + half] = vr[j + half];
+  }
+}
+
+hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc, int bf16,
+                               const int64_t* start, const int64_t* len, int64_t B, int64_t C,
+                               int h_kv, int d, int64_t cap, int64_t end, double log2_theta,
+                               hipStream_t st) {
+  const int64_t n_pairs = B * C * h_kv * (d / 2);
+  const int64_t want = (n_pairs + 255) / 256;
+  const int grid = (int)(want < 65536 ? want : 65536);
+  if (bf16)
+    cache_append_kernel<uint16_t><<<grid, 256, 0, st>>>(
+        (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kc, (uint16_t*)vc, start, len, n_pairs,
+        C, h_kv, d, cap, end, log2_theta);
+  else
+    cache_append_kernel<float><<<grid, 256, 0, st>>>((const float*)k, (const float*)v, (float*)kc,
+                                                     (float*)vc, start, len, n_pairs, C, h_kv, d,
+                                                     cap, end, log2_theta);
   return hipGetLastError();
 }
 

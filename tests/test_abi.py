@@ -112,3 +112,86 @@ def test_workspace_sizes(lib):
     n = lib.gqa_decode_workspace_size(32, 28, 4, 128, 32768)
     assert n == 32 * 4 * 32 * 7 * (2 + 128) * 4
     assert lib.gqa_decode_workspace_size(1, 28, 3, 128, 10) == 0
+
+
+def chunk_call(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, in_dt=1, out_dt=0, B=2, C=64, h_q=28, h_kv=4, d=128,
+             start=FAKE, len=None, kend=512, theta=1e6, scale=0.088, kc=FAKE, vc=FAKE, cap=512,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gqa_prefill_chunk(a["q"], a["k"], a["v"], a["o"], a["in_dt"], a["out_dt"], a["B"],
+                                 a["C"], a["h_q"], a["h_kv"], a["d"], a["start"], a["len"],
+                                 a["kend"], a["theta"], a["scale"], a["kc"], a["vc"], a["cap"],
+                                 a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(start=None), _lib.GQA_ERR_INVALID_ARG),          # positions are required
+    (dict(kc=None), _lib.GQA_ERR_INVALID_ARG),             # chunks need the cache
+    (dict(C=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(kend=513), _lib.GQA_ERR_INVALID_ARG),            # beyond cap
+    (dict(kend=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(h_q=4, h_kv=28), _lib.GQA_ERR_INVALID_ARG),
+    (dict(d=96), _lib.GQA_ERR_UNSUPPORTED),
+    (dict(kc=FAKE + 8), _lib.GQA_ERR_INVALID_ARG),         # misaligned
+    (dict(wsb=64), _lib.GQA_ERR_WORKSPACE),
+])
+def test_prefill_chunk_rejects(lib, kw, code):
+    assert chunk_call(lib, **kw) == code
+    assert lib.gqa_last_error()
+
+
+def ragged_call(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, in_dt=1, out_dt=0, B=2, h_q=28, h_kv=4, d=128,
+             cap=64, kvl=FAKE, qpos=FAKE, max_kv=64, theta=1e6, scale=0.088, ws=FAKE,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gqa_decode_ragged(a["q"], a["kc"], a["vc"], a["o"], a["in_dt"], a["out_dt"],
+                                 a["B"], a["h_q"], a["h_kv"], a["d"], a["cap"], a["kvl"],
+                                 a["qpos"], a["max_kv"], a["theta"], a["scale"], a["ws"],
+                                 a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kvl=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(max_kv=65), _lib.GQA_ERR_INVALID_ARG),           # longer than the cache
+    (dict(max_kv=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(out_dt=3), _lib.GQA_ERR_INVALID_ARG),
+    (dict(wsb=0), _lib.GQA_ERR_WORKSPACE),
+])
+def test_decode_ragged_rejects(lib, kw, code):
+    assert ragged_call(lib, **kw) == code
+    assert lib.gqa_last_error()
+
+
+def append_call(lib, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, o=FAKE, in_dt=1, out_dt=0, B=2, h_q=28,
+             h_kv=4, d=128, cap=64, pos=FAKE, max_pos=63, theta=1e6, scale=0.088, ws=FAKE,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gqa_decode_append(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["o"], a["in_dt"],
+                                 a["out_dt"], a["B"], a["h_q"], a["h_kv"], a["d"], a["cap"],
+                                 a["pos"], a["max_pos"], a["theta"], a["scale"], a["ws"],
+                                 a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pos=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(kn=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(max_pos=64), _lib.GQA_ERR_INVALID_ARG),          # row 64 is outside a 64-row cache
+    (dict(max_pos=-1), _lib.GQA_ERR_INVALID_ARG),
+    (dict(out_dt=5), _lib.GQA_ERR_INVALID_ARG),            # checked before the cache is touched
+    (dict(h_q=30), _lib.GQA_ERR_INVALID_ARG),
+    (dict(vn=FAKE + 2), _lib.GQA_ERR_INVALID_ARG),
+    (dict(wsb=8), _lib.GQA_ERR_WORKSPACE),
+])
+def test_decode_append_rejects(lib, kw, code):
+    assert append_call(lib, **kw) == code
+    assert lib.gqa_last_error()
+
+
+def test_chunk_workspace_sizes(lib):
+    # bf16: the one-shot layout sized for kend keys; fp32: only the cos/sin table
+    assert (lib.gqa_prefill_chunk_workspace_size(1, 4, 4096, 4, 128)
+            == lib.gqa_prefill_workspace_size(1, 4, 4096, 4, 128))
+    assert lib.gqa_prefill_chunk_workspace_size(0, 1, 1000, 2, 64) == 1000 * 32 * 8

@@ -1,0 +1,221 @@
+"""GPU parity of the autoregressive entry points: KV append at decode,
+ragged per-sequence lengths and positions, and chunked prefill against the
+cache, through the C ABI, against the fp64 oracle.
+
+Inputs are seeded N(0, 1) (bf16-rounded where the dtype is bf16).  The
+cache rows that exist before a call are the oracle's rotated K (rounded to
+the cache dtype) and the V rows, so both sides start from the same bytes.
+
+Tolerances as for the one-shot calls: fp32 max-abs <= 1e-4; bf16 max-abs
+<= 2e-2 and relative L2 <= 1e-2.  A K row the library rotates and rounds to
+bf16 is within half an ulp of the exact rotation plus the fp32 rotation's
+own absolute error.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rope_causal_grouped_amd as gqa
+from synthetic import Workload, gen_prefill
+from tests.test_gpu_parity import assert_parity, dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+def inputs(B, L, h_q, h_kv, d, dtype, seed):
+    w = Workload("t", "test", "prefill", B, L, h_q, h_kv, d,
+                 "bf16" if dtype == torch.bfloat16 else "f32", seed, 1.0)
+    return gen_prefill(w)
+
+
+def rounded(x, dtype):
+    """x as the cache dtype stores it (bf16: round to nearest even)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dtype).double().numpy()
+
+
+def prefilled_cache(k, v, n_rows, cap, dtype, fill=3.0):
+    """Cache [B, cap, h_kv, d] whose rows < n_rows[b] hold the rotated K and
+    the V of positions 0 .. n_rows[b]-1; later rows hold `fill`."""
+    B, _, h_kv, d = k.shape
+    kc = np.full((B, cap, h_kv, d), fill)
+    vc = np.full((B, cap, h_kv, d), fill)
+    kr = oracle.rope(k, np.arange(k.shape[1]))
+    for b in range(B):
+        n = int(n_rows[b])
+        kc[b, :n] = kr[b, :n]
+        vc[b, :n] = v[b, :n]
+    return rounded(kc, dtype), rounded(vc, dtype)
+
+
+def assert_rotated_rows(got, want, dtype, what):
+    if np.size(got) == 0:
+        return
+    if dtype == torch.float32:
+        assert np.max(np.abs(got - want)) <= 1e-5, what
+    else:
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-5), what
+
+
+# ------------------------------------------------------------ decode -----
+
+@pytest.mark.parametrize("dtype,heads", [(torch.bfloat16, (28, 4, 128)),
+                                         (torch.bfloat16, (40, 2, 128)),
+                                         (torch.float32, (14, 2, 64))],
+                         ids=["bf16_28_4", "bf16_g20", "f32_14_2"])
+def test_decode_append_ragged(dtype, heads):
+    h_q, h_kv, d = heads
+    pos = np.array([0, 1, 1023, 1024, 2500])
+    B, cap = len(pos), 2600
+    note(f"decode_append {dtype} {heads} pos={pos.tolist()}")
+    q, k, v = inputs(B, cap, h_q, h_kv, d, dtype, 31)
+    kc, vc = prefilled_cache(k, v, pos, cap, dtype)
+    qn = np.stack([q[b, pos[b]] for b in range(B)])
+    kn = np.stack([k[b, pos[b]] for b in range(B)])
+    vn = np.stack([v[b, pos[b]] for b in range(B)])
+    kcd, vcd = dev(kc, dtype), dev(vc, dtype)
+    o = gqa.decode_append(dev(qn, dtype), dev(kn, dtype), dev(vn, dtype), kcd, vcd,
+                          torch.tensor(pos, dtype=torch.int64), max_pos=int(pos.max()))
+    torch.cuda.synchronize()
+    want, kc_want, vc_want = oracle.decode_append(qn, kn, vn, kc, vc, pos)
+    assert_parity(host(o), want, dtype, "decode_append")
+    kc_got, vc_got = host(kcd), host(vcd)
+    for b in range(B):
+        p = int(pos[b])
+        assert_rotated_rows(kc_got[b, p], kc_want[b, p], dtype, f"appended K row {b}")
+        assert np.array_equal(vc_got[b, p], rounded(vn[b], dtype)), f"appended V row {b}"
+    keep = np.ones((B, cap), bool)
+    keep[np.arange(B), pos] = False
+    assert np.array_equal(kc_got[keep], kc[keep]) and np.array_equal(vc_got[keep], vc[keep]), \
+        "rows other than pos[b] changed"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_ragged(dtype):
+    h_q, h_kv, d = (28, 4, 128) if dtype == torch.bfloat16 else (14, 2, 64)
+    kv_len = np.array([1, 1024, 1025, 3000, 77])
+    q_pos = np.array([0, 1023, 5000, 2999, 200])
+    B, cap = len(kv_len), 3000
+    note(f"decode_ragged {dtype} kv_len={kv_len.tolist()}")
+    q, k, v = inputs(B, cap, h_q, h_kv, d, dtype, 32)
+    kc, vc = prefilled_cache(k, v, np.full(B, cap), cap, dtype)
+    o = gqa.decode_ragged(dev(q[:, 0], dtype), dev(kc, dtype), dev(vc, dtype),
+                          torch.tensor(kv_len), torch.tensor(q_pos), max_kv_len=cap)
+    torch.cuda.synchronize()
+    assert_parity(host(o), oracle.decode_ragged(q[:, 0], kc, vc, kv_len, q_pos), dtype,
+                  "decode_ragged")
+
+
+def test_decode_ragged_matches_scalar_decode():
+    """A ragged call whose sequences share one length equals gqa_decode."""
+    B, cap, h_q, h_kv, d = 4, 1500, 28, 4, 128
+    q, k, v = inputs(B, cap, h_q, h_kv, d, torch.bfloat16, 33)
+    kc, vc = prefilled_cache(k, v, np.full(B, cap), cap, torch.bfloat16)
+    qd, kcd, vcd = dev(q[:, 0], torch.bfloat16), dev(kc, torch.bfloat16), dev(vc, torch.bfloat16)
+    a = gqa.decode(qd, kcd, vcd, 1300, 1400)
+    b = gqa.decode_ragged(qd, kcd, vcd, [1300] * B, [1400] * B)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_invalid_sequence_is_nan():
+    """Entries that break the stated conditions give NaN rows for that
+    sequence only, and an appending step then leaves its cache rows alone."""
+    B, cap, h_q, h_kv, d = 3, 512, 28, 4, 128
+    q, k, v = inputs(B, cap, h_q, h_kv, d, torch.bfloat16, 34)
+    kc, vc = prefilled_cache(k, v, np.full(B, 300), cap, torch.bfloat16)
+    kcd, vcd = dev(kc, torch.bfloat16), dev(vc, torch.bfloat16)
+    qd = dev(q[:, 0], torch.bfloat16)
+    # kv_len beyond max_kv_len, kv_len after the query's position
+    o = gqa.decode_ragged(qd, kcd, vcd, [100, 400, 50], [99, 500, 10], max_kv_len=300)
+    pos = np.array([299, 511, -1])   # valid, beyond max_pos, negative
+    kn, vn = dev(k[:, 0], torch.bfloat16), dev(v[:, 0], torch.bfloat16)
+    oa = gqa.decode_append(qd, kn, vn, kcd, vcd, torch.tensor(pos), max_pos=400)
+    torch.cuda.synchronize()
+    o, oa = host(o), host(oa)
+    assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))
+    assert np.all(np.isfinite(oa[0])) and np.all(np.isnan(oa[1])) and np.all(np.isnan(oa[2]))
+    kc_got = host(kcd)
+    assert np.array_equal(kc_got[1:], kc[1:]), "an invalid sequence's cache was written"
+    assert not np.array_equal(kc_got[0, 299], kc[0, 299])
+
+
+# ----------------------------------------------------- chunked prefill ---
+
+@pytest.mark.parametrize("dtype,heads", [(torch.bfloat16, (28, 4, 128)),
+                                         (torch.bfloat16, (16, 2, 64)),
+                                         (torch.float32, (14, 2, 64))],
+                         ids=["bf16_28_4", "bf16_d64_g8", "f32_14_2"])
+def test_prefill_chunk_ragged(dtype, heads):
+    h_q, h_kv, d = heads
+    start = np.array([0, 300, 1000, 64])
+    length = np.array([200, 1, 137, 0])
+    B, C, cap = len(start), 200, 1400
+    note(f"prefill_chunk {dtype} {heads} start={start.tolist()} len={length.tolist()}")
+    q, k, v = inputs(B, cap, h_q, h_kv, d, dtype, 35)
+    kc, vc = prefilled_cache(k, v, start, cap, dtype)
+    qc = np.zeros((B, C, h_q, d)); kn = np.zeros((B, C, h_kv, d)); vn = np.zeros_like(kn)
+    for b in range(B):
+        s0, n = int(start[b]), int(length[b])
+        qc[b, :n], kn[b, :n], vn[b, :n] = q[b, s0:s0 + n], k[b, s0:s0 + n], v[b, s0:s0 + n]
+    kcd, vcd = dev(kc, dtype), dev(vc, dtype)
+    out = torch.full((B, C, h_q, d), 5.0, device="cuda")
+    gqa.prefill_chunk(dev(qc, dtype), dev(kn, dtype), dev(vn, dtype), kcd, vcd,
+                      torch.tensor(start), torch.tensor(length), kend=1200, out=out)
+    torch.cuda.synchronize()
+    kc_want, vc_want = oracle.cache_append(kc, vc, kn, vn, start, length)
+    want = oracle.prefill_chunk(qc, kc_want, vc_want, start, length)
+    got = host(out)
+    rows = np.zeros((B, C), bool)
+    for b in range(B):
+        rows[b, :length[b]] = True
+    assert_parity(got[rows], want[rows], dtype, "prefill_chunk rows")
+    assert np.all(got[~rows] == 5.0), "rows past len[b] were written"
+    kc_got = host(kcd)
+    for b in range(B):
+        s0, n = int(start[b]), int(length[b])
+        assert_rotated_rows(kc_got[b, s0:s0 + n], kc_want[b, s0:s0 + n], dtype, f"K rows {b}")
+        assert np.array_equal(kc_got[b, :s0], kc[b, :s0])
+        assert np.array_equal(kc_got[b, s0 + n:], kc[b, s0 + n:])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_chunks_equal_one_shot_prefill(dtype):
+    """Three chunks through the cache give the rows and the cache of one
+    gqa_prefill call over the whole prompt."""
+    B, L, h_q, h_kv, d = 2, 700, 28, 4, 128
+    if dtype == torch.float32:
+        h_q, h_kv, d = 14, 2, 64
+    note(f"chunks vs one-shot {dtype}")
+    q, k, v = inputs(B, L, h_q, h_kv, d, dtype, 36)
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    cap = 768
+    kc1 = torch.zeros((B, cap, h_kv, d), dtype=dtype, device="cuda")
+    vc1 = torch.zeros_like(kc1)
+    one = gqa.prefill(qd, kd, vd, k_cache=kc1, v_cache=vc1)
+    kc2 = torch.zeros_like(kc1)
+    vc2 = torch.zeros_like(kc1)
+    parts = []
+    for s0, n in ((0, 256), (256, 256), (512, 188)):
+        parts.append(gqa.prefill_chunk(qd[:, s0:s0 + n].contiguous(), kd[:, s0:s0 + n].contiguous(),
+                                       vd[:, s0:s0 + n].contiguous(), kc2, vc2, [s0] * B,
+                                       kend=L))
+    torch.cuda.synchronize()
+    chunked = torch.cat(parts, dim=1)
+    assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2), "caches differ"
+    assert_parity(host(chunked), host(one), dtype, "chunked vs one-shot")
+    assert_parity(host(chunked), oracle.prefill(q, k, v), dtype, "chunked vs oracle")
+
+
+def test_prefill_chunk_invalid_sequence_is_nan():
+    B, C, h_q, h_kv, d, cap = 2, 64, 28, 4, 128, 256
+    q, k, v = inputs(B, C, h_q, h_kv, d, torch.bfloat16, 37)
+    kc = torch.zeros((B, cap, h_kv, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    o = gqa.prefill_chunk(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16),
+                          kc, vc, [0, 150], kend=200)   # 150 + 64 > 200
+    torch.cuda.synchronize()
+    o = host(o)
+    assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1]))
+    assert torch.count_nonzero(kc[1]) == 0 and torch.count_nonzero(kc[0, :C]) > 0
