@@ -7,6 +7,11 @@ One step = one pass of the whole hot path over resident synthetic inputs:
     RoPE theta 1e6): RoPE table, K/V preparation, attention;
   * gqa_decode on the Qwen2-7B-shaped decode workload (B=32 sequences, a
     32768-position bf16 cache, one new token at position 32768).
+After the timed steps, the autoregressive entry points are measured on the
+same shapes (reported under "next", outside the step): the last 1024-row
+chunk of the prefill workload through gqa_prefill_chunk against a cache that
+holds the first 3072 rows, and one gqa_decode_append step for 32 sequences
+at ragged positions 32767 - 256 b of a 32768-row cache.
 `value` is the prefill rate in TFLOP/s over the causal pairs only
 (4 * B * h_q * d * L(L+1)/2 flop per call) measured around the whole call;
 the decode rate (K/V cache bytes read once per KV group / call time) is
@@ -63,8 +68,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--only", choices=["prefill", "decode"], default=None,
-                   help="run one half of the step (for profiling)")
+    p.add_argument("--only", choices=["prefill", "decode", "next"], default=None,
+                   help="run one part only (for profiling)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
@@ -92,6 +97,114 @@ def cpu_baseline(w):
                       f"{w.name}; {flops / 1e9:.1f} causal GFLOP in {dt:.2f} s (fp64 NumPy)"}
 
 
+def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
+    """Chunked prefill and appending decode on the prefill / decode shapes
+    (``pre``/``dec``: the step's resident inputs, reused when present)."""
+    from synthetic import gen_decode_cache_b, gen_decode_query, gen_prefill
+    K = args.steps
+    res = {}
+    # -- chunked prefill: rows 3072..4095 of the prefill workload, cache holds 0..3071
+    s0, C = wp.L - 1024, 1024
+    if pre is None:
+        q, k, v = gen_prefill(wp)
+        pre = tuple(torch.from_numpy(x).to(dev, torch.bfloat16) for x in (q, k, v))
+        del q, k, v
+    qd, kd, vd = pre
+    kc = torch.zeros((wp.B, wp.L, wp.h_kv, wp.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    ws = torch.empty(gqa.prefill_chunk_workspace_size(torch.bfloat16, wp.B, wp.L, wp.h_kv, wp.d),
+                     dtype=torch.uint8, device=dev)
+    for a in range(0, s0, C):   # fill the cache chunk by chunk (untimed)
+        gqa.prefill_chunk(qd[:, a:a + C].contiguous(), kd[:, a:a + C].contiguous(),
+                          vd[:, a:a + C].contiguous(), kc, vc, [a] * wp.B, kend=wp.L,
+                          workspace=ws)
+    qc, kn, vn = (x[:, s0:].contiguous() for x in (qd, kd, vd))
+    start = torch.full((wp.B,), s0, dtype=torch.int64, device=dev)
+    oc = torch.empty((wp.B, C, wp.h_q, wp.d), dtype=torch.float32, device=dev)
+
+    def chunk():
+        gqa.prefill_chunk(qc, kn, vn, kc, vc, start, kend=wp.L, out=oc, workspace=ws)
+
+    for _ in range(args.warmup):
+        chunk()
+    torch.cuda.synchronize()
+    gqa.timing_read(0)
+    gqa.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        chunk()
+    e1.record()
+    torch.cuda.synchronize()
+    gqa.timing_enable(False)
+    call_ms = e0.elapsed_time(e1) / K
+    attn_ms, attn_n = gqa.timing_read(0)
+    attn_avg = attn_ms / max(attn_n, 1)
+    pos = np.arange(s0, wp.L, dtype=np.float64)
+    flops = 4.0 * wp.B * wp.h_q * wp.d * float(np.sum(pos + 1))
+    ach = flops / (attn_avg * 1e-3) / 1e12
+    res["prefill_chunk"] = {
+        "workload": f"{wp.name} last chunk: B{wp.B} rows {s0}..{wp.L - 1} ({C} per sequence) "
+                    f"against {s0} cached rows, h_q{wp.h_q} h_kv{wp.h_kv} d{wp.d} bf16",
+        "value": flops / (call_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "call_ms": call_ms,
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": ach,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                     "kernel_ms": attn_avg, "traffic": None}}
+    del pre, qd, kd, vd, qc, kn, vn, kc, vc, ws, oc
+    log(f"[bench] chunked prefill: {call_ms:.3f} ms per call")
+
+    # -- appending decode: 32 sequences at ragged positions of a 32768-row cache
+    cap = wd.L
+    pos = np.array([cap - 1 - 256 * b for b in range(wd.B)], dtype=np.int64)
+    if dec is None:
+        qh = torch.from_numpy(gen_decode_query(wd)).to(dev, torch.bfloat16)
+        kc = torch.empty((wd.B, cap, wd.h_kv, wd.d), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        for b in range(wd.B):
+            kb, vb = gen_decode_cache_b(wd, b)
+            kc[b].copy_(torch.from_numpy(kb))
+            vc[b].copy_(torch.from_numpy(vb))
+    else:
+        qh, kc, vc = dec
+    posd = torch.from_numpy(pos).to(dev)
+    rows = torch.arange(wd.B, device=dev)
+    kn = kc[rows, posd].clone()   # the new tokens' K and V (rewritten in place every step)
+    vn = vc[rows, posd].clone()
+    od = torch.empty((wd.B, wd.h_q, wd.d), dtype=torch.float32, device=dev)
+    wsd = torch.empty(gqa.decode_workspace_size(wd.B, wd.h_q, wd.h_kv, wd.d, cap),
+                      dtype=torch.uint8, device=dev)
+
+    def app():
+        gqa.decode_append(qh, kn, vn, kc, vc, posd, max_pos=int(pos.max()), out=od,
+                          workspace=wsd)
+
+    for _ in range(args.warmup):
+        app()
+    torch.cuda.synchronize()
+    gqa.timing_read(1)
+    gqa.timing_enable(True)
+    e0.record()
+    for _ in range(K):
+        app()
+    e1.record()
+    torch.cuda.synchronize()
+    gqa.timing_enable(False)
+    call_ms = e0.elapsed_time(e1) / K
+    split_ms, split_n = gqa.timing_read(1)
+    split_avg = split_ms / max(split_n, 1)
+    kvb = float(np.sum(pos + 1)) * wd.h_kv * wd.d * 2 * 2
+    dach = kvb / (split_avg * 1e-3) / 1e9
+    res["decode_append"] = {
+        "workload": f"{wd.name} with append: B{wd.B} positions {int(pos.min())}..{int(pos.max())} "
+                    f"(step 256) of a {cap}-row cache, h_q{wd.h_q} h_kv{wd.h_kv} d{wd.d} bf16",
+        "value": kvb / (call_ms * 1e-3) / 1e9, "unit": "GB/s", "call_ms": call_ms,
+        "roofline": {"bound": "hbm", "kernel": "decode_split_bf16_kernel", "achieved": dach,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
+                     "kernel_ms": split_avg, "traffic": None}}
+    log(f"[bench] appending decode: {call_ms:.3f} ms per call")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -108,6 +221,7 @@ def main():
     torch.cuda.set_device(dev)
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
+    run_n = args.only in (None, "next")
 
     # ---- inputs resident in HBM
     if run_p:
@@ -167,6 +281,11 @@ def main():
     split_ms, split_n = gqa.timing_read(1)
     log(f"[bench] timed {K} steps: {total_ms:.2f} ms total")
 
+    if run_n:
+        out_next = measure_next(args, torch, gqa, dev, wp, wd,
+                                (qd, kd, vd) if run_p else None,
+                                (qh, kc, vc) if run_d else None)
+
     if args.calib_copy_mb:
         n = args.calib_copy_mb * 2**20 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -212,6 +331,14 @@ def main():
             out["config"] = {"workload": dec["workload"], "global_batch": wd.B,
                              "seq_len": wd.L, "parallelism": "single-gpu"}
             out["roofline"] = dec["roofline"]
+    if run_n:
+        out["next"] = out_next
+        if not (run_p or run_d):
+            nx = out_next["prefill_chunk"]
+            out["value"], out["unit"] = nx["value"], nx["unit"]
+            out["config"] = {"workload": nx["workload"], "global_batch": wp.B,
+                             "seq_len": wp.L, "parallelism": "single-gpu"}
+            out["roofline"] = nx["roofline"]
     if run_p and not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wp)
