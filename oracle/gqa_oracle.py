@@ -305,6 +305,41 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, pos,
     return decode_ragged(q, kc, vc, pos + 1, pos, theta, scale), kc, vc
 
 
+# ------------------------------------------------ QKV projection epilogue -
+
+def qkv_sections(h_q: int, h_kv: int, d: int):
+    """Column ranges of Q, K and V in the packed projection output
+    [..., (h_q + 2 h_kv) d]: the h_q query heads, then the h_kv key heads,
+    then the h_kv value heads, each head's d columns contiguous."""
+    return ((0, h_q * d), (h_q * d, (h_q + h_kv) * d),
+            ((h_q + h_kv) * d, (h_q + 2 * h_kv) * d))
+
+
+def qkv_epilogue(qkv, bias, k_cache, v_cache, h_q: int, h_kv: int, start,
+                 length=None, theta: float = ROPE_THETA):
+    """The step before attention in a Qwen2 layer: each projection adds its
+    bias and the flat output is cut into heads ([csdn] §4.1.3 steps 1-2;
+    §4.2: Qwen2 keeps the QKV bias), K is rotated at its position (step 3),
+    and the K, V of the h_kv groups go to the cache (closing note of
+    §4.1.3).  qkv [B, C, (h_q + 2 h_kv) d] is the packed projection
+    output without bias, bias [(h_q + 2 h_kv) d]; token i < length[b] of
+    sequence b sits at position start[b] + i.  Returns (q [B, C, h_q, d] with
+    bias, not rotated -- rows past length[b] NaN --, k_cache', v_cache')."""
+    x = np.asarray(qkv, np.float64) + np.asarray(bias, np.float64)
+    B, C, _ = x.shape
+    d = x.shape[-1] // (h_q + 2 * h_kv)
+    (q0, q1), (k0, k1), (v0, v1) = qkv_sections(h_q, h_kv, d)
+    q = x[..., q0:q1].reshape(B, C, h_q, d)
+    k = x[..., k0:k1].reshape(B, C, h_kv, d)
+    v = x[..., v0:v1].reshape(B, C, h_kv, d)
+    kc, vc = cache_append(k_cache, v_cache, k, v, start, length, theta)
+    n_new = per_sequence(C if length is None else length, B)
+    q_out = np.full(q.shape, np.nan)
+    for b in range(B):
+        q_out[b, :n_new[b]] = q[b, :n_new[b]]
+    return q_out, kc, vc
+
+
 # ------------------------------------------------------- brute force ------
 
 def prefill_brute(q, k, v, theta: float = ROPE_THETA, scale: float | None = None,

@@ -380,10 +380,68 @@ def pin_ragged_decode_is_single(orc):
         close(o[b], one[0], 1e-12, f"sequence {b}")
 
 
+# ----------------------------------------------------- QKV epilogue -----
+
+def _layout_code(section, head, dim):
+    """A distinct value for every (section, head, dim) of the packed output."""
+    return 100.0 * section + head + dim / 1000.0
+
+
+def pin_qkv_layout(orc):
+    """The packed projection output holds the h_q query heads, then the h_kv
+    key heads, then the h_kv value heads, each head's d columns contiguous;
+    the bias adds column by column.  At position 0 the rotation is the
+    identity, so the cached K row shows the layout too."""
+    B, h_q, h_kv, d = 2, 6, 2, 8
+    width = (h_q + 2 * h_kv) * d
+    qkv = np.zeros((B, 1, width))
+    for col in range(width):
+        if col < h_q * d:
+            sec, rem = 0, col
+        elif col < (h_q + h_kv) * d:
+            sec, rem = 1, col - h_q * d
+        else:
+            sec, rem = 2, col - (h_q + h_kv) * d
+        qkv[:, 0, col] = _layout_code(sec, rem // d, rem % d)
+    bias = np.arange(width) * 1e-6
+    cap = 3
+    q, kc, vc = orc.qkv_epilogue(qkv, bias, np.zeros((B, cap, h_kv, d)),
+                                 np.zeros((B, cap, h_kv, d)), h_q, h_kv, 0)
+    for b in range(B):
+        for t in range(h_q):
+            for j in range(d):
+                want = _layout_code(0, t, j) + (t * d + j) * 1e-6
+                assert abs(q[b, 0, t, j] - want) < 1e-12, ("q", b, t, j)
+        for u in range(h_kv):
+            for j in range(d):
+                kw = _layout_code(1, u, j) + (h_q * d + u * d + j) * 1e-6
+                vw = _layout_code(2, u, j) + ((h_q + h_kv) * d + u * d + j) * 1e-6
+                assert abs(kc[b, 0, u, j] - kw) < 1e-12, ("k", b, u, j)
+                assert abs(vc[b, 0, u, j] - vw) < 1e-12, ("v", b, u, j)
+
+
+def pin_qkv_epilogue_then_attention(orc):
+    """Epilogue, then a chunk attending to the cache it filled, equals the
+    one-shot prefill of the biased projections."""
+    rng = _rng(18)
+    B, L, h_q, h_kv, d = 2, 9, 4, 2, 8
+    width = (h_q + 2 * h_kv) * d
+    qkv = _rand(rng, B, L, width)
+    bias = _rand(rng, width)
+    x = qkv + bias
+    q = x[..., :h_q * d].reshape(B, L, h_q, d)
+    k = x[..., h_q * d:(h_q + h_kv) * d].reshape(B, L, h_kv, d)
+    v = x[..., (h_q + h_kv) * d:].reshape(B, L, h_kv, d)
+    qe, kc, vc = orc.qkv_epilogue(qkv, bias, np.zeros((B, L, h_kv, d)),
+                                  np.zeros((B, L, h_kv, d)), h_q, h_kv, 0)
+    close(orc.prefill_chunk(qe, kc, vc, 0), orc.prefill(q, k, v), 1e-12, "epilogue + chunk")
+
+
 ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_rope_half_split_pairing, pin_rope_norm, pin_rope_relative,
             pin_rope_group_law, pin_group_example, pin_repeat_interleave,
             pin_sdpa, pin_brute, pin_softmax_causal, pin_future_invariance,
             pin_shift_invariance, pin_decode_is_prefill_row, pin_prefill_rows,
             pin_chunked_prefill_is_prefill, pin_decode_append_is_prefill_row,
-            pin_cache_append_pair0, pin_ragged_decode_is_single]
+            pin_cache_append_pair0, pin_ragged_decode_is_single, pin_qkv_layout,
+            pin_qkv_epilogue_then_attention]

@@ -138,11 +138,42 @@ def m_cached_key_unrotated(mod):
     mod.cache_append = cache_append
 
 
+def m_qkv_k_v_swapped(mod):
+    orig = mod.qkv_sections
+
+    def qkv_sections(h_q, h_kv, d):
+        q, k, v = orig(h_q, h_kv, d)
+        return q, v, k
+    mod.qkv_sections = qkv_sections
+
+
+def m_qkv_bias_dropped(mod):
+    orig = mod.qkv_epilogue
+    mod.qkv_epilogue = lambda qkv, bias, *a, **kw: orig(qkv, np.zeros_like(bias), *a, **kw)
+
+
+def m_qkv_heads_transposed(mod):
+    orig = mod.qkv_epilogue
+
+    def qkv_epilogue(qkv, bias, k_cache, v_cache, h_q, h_kv, start, length=None,
+                     theta=mod.ROPE_THETA):
+        x = np.asarray(qkv, np.float64)
+        B, C, width = x.shape
+        d = width // (h_q + 2 * h_kv)
+        perm = []
+        for lo, n in ((0, h_q), (h_q * d, h_kv), ((h_q + h_kv) * d, h_kv)):
+            perm += [lo + j * n + h for h in range(n) for j in range(d)]   # dim-major heads
+        return orig(x[..., perm], np.asarray(bias)[perm], k_cache, v_cache, h_q, h_kv, start,
+                    length, theta)
+    mod.qkv_epilogue = qkv_epilogue
+
+
 MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
            m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
            m_transposed_weights, m_softmax_no_norm, m_decode_unrotated_query,
-           m_chunk_position_shift, m_ragged_first_value, m_cached_key_unrotated]
+           m_chunk_position_shift, m_ragged_first_value, m_cached_key_unrotated,
+           m_qkv_k_v_swapped, m_qkv_bias_dropped, m_qkv_heads_transposed]
 
 
 def failing_pins(mod):
