@@ -10,8 +10,9 @@ One step = one pass of the whole hot path over resident synthetic inputs:
 After the timed steps, the autoregressive entry points are measured on the
 same shapes (reported under "next", outside the step): the last 1024-row
 chunk of the prefill workload through gqa_prefill_chunk against a cache that
-holds the first 3072 rows, and one gqa_decode_append step for 32 sequences
-at ragged positions 32767 - 256 b of a 32768-row cache.
+holds the first 3072 rows, one gqa_decode_append step for 32 sequences at
+ragged positions 32767 - 256 b of a 32768-row cache, and gqa_qkv_epilogue
+over the packed projection output of the prefill workload's 4 x 4096 tokens.
 `value` is the prefill rate in TFLOP/s over the causal pairs only
 (4 * B * h_q * d * L(L+1)/2 flop per call) measured around the whole call;
 the decode rate (K/V cache bytes read once per KV group / call time) is
@@ -202,6 +203,41 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
                      "kernel_ms": split_avg, "traffic": None}}
     log(f"[bench] appending decode: {call_ms:.3f} ms per call")
+    del kn, vn, od, wsd
+
+    # -- QKV epilogue on the prefill shape: packed projection output of all
+    #    4096 tokens -> rotated Q, rotated K and V in a 4096-row cache
+    width = (wp.h_q + 2 * wp.h_kv) * wp.d
+    g = torch.Generator(device=dev).manual_seed(wp.seed)
+    xq = torch.randn((wp.B, wp.L, width), generator=g, device=dev).to(torch.bfloat16)
+    bq = torch.randn((width,), generator=g, device=dev).to(torch.bfloat16)
+    kc = torch.empty((wp.B, wp.L, wp.h_kv, wp.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    qo = torch.empty((wp.B, wp.L, wp.h_q, wp.d), dtype=torch.bfloat16, device=dev)
+    start = torch.zeros((wp.B,), dtype=torch.int64, device=dev)
+
+    def epi():
+        gqa.qkv_epilogue(xq, bq, kc, vc, wp.h_q, start, q_out=qo)
+
+    for _ in range(args.warmup):
+        epi()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        epi()
+    e1.record()
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / K
+    nbytes = 2.0 * wp.B * wp.L * (width + wp.h_q * wp.d + 2 * wp.h_kv * wp.d) + 2 * width
+    rate = nbytes / (call_ms * 1e-3) / 1e9
+    res["qkv_epilogue"] = {
+        "workload": f"{wp.name} projections: B{wp.B} L{wp.L} packed ({wp.h_q}+2x{wp.h_kv}) "
+                    f"x {wp.d} bf16 + bias -> rotated Q, rotated K and V into the cache",
+        "value": rate, "unit": "GB/s", "call_ms": call_ms,
+        "roofline": {"bound": "hbm", "kernel": "qkv_epilogue_kernel", "achieved": rate,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": rate / PEAK_HBM_GBS,
+                     "kernel_ms": call_ms, "traffic": None}}
+    log(f"[bench] QKV epilogue: {call_ms:.3f} ms per call")
     return res
 
 

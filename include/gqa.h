@@ -137,13 +137,16 @@ size_t gqa_prefill_chunk_workspace_size(int in_dtype, int64_t B, int64_t kend,
  * and writes o [B, C, h_q, d] (out_dtype) rows i < len[b]; other rows are
  * not written.  Conditions: 0 <= start[b], 0 <= len[b] <= C,
  * start[b] + len[b] <= kend <= cap.  Splitting a prompt into chunks gives
- * the rows of the one-shot gqa_prefill (up to rounding).
+ * the rows of the one-shot gqa_prefill (up to rounding).  k and v may both
+ * be NULL when the cache already holds the chunk's rows (as written by
+ * gqa_qkv_epilogue); step 1 is then skipped.  q_rotated != 0: q holds
+ * queries rotated already (gqa_qkv_epilogue's q_out), used as given.
  */
 int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o,
                       int in_dtype, int out_dtype,
                       int64_t B, int64_t C, int h_q, int h_kv, int d,
                       const int64_t* start, const int64_t* len, int64_t kend,
-                      double theta, float scale,
+                      double theta, float scale, int q_rotated,
                       void* k_cache, void* v_cache, int64_t cap,
                       void* workspace, size_t workspace_bytes, void* stream);
 
@@ -151,13 +154,15 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o,
  * Decode with one length and one query position per sequence: q [B, h_q, d]
  * (pre-RoPE) of sequence b, rotated at q_pos[b], attends to its cache rows
  * 0 .. kv_len[b] - 1.  Conditions: 1 <= kv_len[b] <= max_kv_len <= cap and
- * kv_len[b] <= q_pos[b] + 1.  Workspace: gqa_decode_workspace_size(..., cap).
+ * kv_len[b] <= q_pos[b] + 1.  q_rotated != 0: q is rotated already
+ * (gqa_qkv_epilogue's q_out) and used as given.  Workspace:
+ * gqa_decode_workspace_size(..., cap).
  */
 int gqa_decode_ragged(const void* q, const void* k_cache, const void* v_cache,
                       void* o, int in_dtype, int out_dtype,
                       int64_t B, int h_q, int h_kv, int d, int64_t cap,
                       const int64_t* kv_len, const int64_t* q_pos,
-                      int64_t max_kv_len, double theta, float scale,
+                      int64_t max_kv_len, double theta, float scale, int q_rotated,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -174,6 +179,29 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new,
                       const int64_t* pos, int64_t max_pos,
                       double theta, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The step before attention (walkthrough §4.1.3 steps 1-3 and §4.2: the
+ * Q, K, V projections keep their bias; the flat outputs are cut into heads;
+ * K is rotated at its position; the h_kv groups' K and V go to the cache).
+ * qkv [B, C, (h_q + 2 h_kv) d] is the packed projection output without
+ * bias: columns [0, h_q d) are the query heads, then h_kv key heads, then
+ * h_kv value heads, each head's d columns contiguous; bias
+ * [(h_q + 2 h_kv) d] (NULL: none).  Token i < len[b] (len NULL: C) of
+ * sequence b sits at position p = start[b] + i:
+ *   q_out [B, C, h_q, d] row i = RoPE(its query heads + bias, p),
+ *   cache row p = RoPE(K + bias, p) and V + bias.
+ * All tensors in `dtype`; sums and rotations in fp32, rounded once.
+ * Conditions: 0 <= start[b], 0 <= len[b] <= C, start[b] + len[b] <= kend
+ * <= cap; a sequence that breaks them is skipped (q_out rows and cache
+ * untouched).  Follow with gqa_prefill_chunk(k = v = NULL, q_rotated = 1)
+ * or gqa_decode_ragged(q_rotated = 1).
+ */
+int gqa_qkv_epilogue(const void* qkv, const void* bias, void* q_out,
+                     void* k_cache, void* v_cache, int dtype,
+                     int64_t B, int64_t C, int h_q, int h_kv, int d, int64_t cap,
+                     const int64_t* start, const int64_t* len, int64_t kend,
+                     double theta, void* stream);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* gqa_last_error(void);

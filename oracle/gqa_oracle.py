@@ -231,18 +231,20 @@ def cache_append(k_cache, v_cache, k_new, v_new, start, length=None,
 
 
 def attend_cached(q, q_pos, k_cache, v_cache, kv_len: int,
-                  theta: float = ROPE_THETA, scale: float | None = None):
+                  theta: float = ROPE_THETA, scale: float | None = None,
+                  q_rotated: bool = False):
     """Queries of one sequence at explicit positions against its cache:
-    q [n, h_q, d] pre-RoPE (rotated here at q_pos[n]); cache rows j < kv_len
-    hold the rotated key and the value of position j, visible to a query iff
-    j <= its position.  Returns [n, h_q, d]."""
+    q [n, h_q, d] pre-RoPE (rotated here at q_pos[n]; already rotated if
+    q_rotated); cache rows j < kv_len hold the rotated key and the value of
+    position j, visible to a query iff j <= its position.  Returns
+    [n, h_q, d]."""
     q = np.asarray(q, np.float64)
     n, h_q, d = q.shape
     h_kv = np.shape(k_cache)[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     qp = np.asarray(q_pos)
-    qr = rope(q, qp, theta)
+    qr = q if q_rotated else rope(q, qp, theta)
     kb = np.asarray(k_cache[:kv_len], np.float64)
     vb = np.asarray(v_cache[:kv_len], np.float64)
     vis = visible(qp, np.arange(kv_len))
@@ -254,7 +256,8 @@ def attend_cached(q, q_pos, k_cache, v_cache, kv_len: int,
 
 
 def prefill_chunk(q, k_cache, v_cache, start, length=None,
-                  theta: float = ROPE_THETA, scale: float | None = None):
+                  theta: float = ROPE_THETA, scale: float | None = None,
+                  q_rotated: bool = False):
     """Chunked causal prefill against a cache that already holds the chunk's
     own rows (see cache_append): query i < length[b] of sequence b sits at
     position start[b] + i and sees cache rows 0 .. start[b] + i.
@@ -270,12 +273,13 @@ def prefill_chunk(q, k_cache, v_cache, start, length=None,
             continue
         pos = chunk_positions(int(start[b]), n)
         out[b, :n] = attend_cached(q[b, :n], pos, k_cache[b], v_cache[b],
-                                   int(pos[-1]) + 1, theta, scale)
+                                   int(pos[-1]) + 1, theta, scale, q_rotated)
     return out
 
 
 def decode_ragged(q, k_cache, v_cache, kv_len, q_pos,
-                  theta: float = ROPE_THETA, scale: float | None = None):
+                  theta: float = ROPE_THETA, scale: float | None = None,
+                  q_rotated: bool = False):
     """Decode with one length and one query position per sequence: q [B, h_q,
     d]; sequence b attends to its cache rows 0 .. kv_len[b]-1 from position
     q_pos[b] (kv_len[b] <= q_pos[b] + 1).  Returns O [B, h_q, d]."""
@@ -288,7 +292,7 @@ def decode_ragged(q, k_cache, v_cache, kv_len, q_pos,
         if not 1 <= kv_len[b] <= min(np.shape(k_cache)[1], q_pos[b] + 1):
             raise ValueError("kv_len out of range")
         out[b] = attend_cached(q[b][None], q_pos[b:b + 1], k_cache[b], v_cache[b],
-                               int(kv_len[b]), theta, scale)[0]
+                               int(kv_len[b]), theta, scale, q_rotated)[0]
     return out
 
 
@@ -319,12 +323,13 @@ def qkv_epilogue(qkv, bias, k_cache, v_cache, h_q: int, h_kv: int, start,
                  length=None, theta: float = ROPE_THETA):
     """The step before attention in a Qwen2 layer: each projection adds its
     bias and the flat output is cut into heads ([csdn] §4.1.3 steps 1-2;
-    §4.2: Qwen2 keeps the QKV bias), K is rotated at its position (step 3),
-    and the K, V of the h_kv groups go to the cache (closing note of
-    §4.1.3).  qkv [B, C, (h_q + 2 h_kv) d] is the packed projection
+    §4.2: Qwen2 keeps the QKV bias), Q and K are rotated at their position
+    (step 3), and the K, V of the h_kv groups go to the cache (closing note
+    of §4.1.3).  qkv [B, C, (h_q + 2 h_kv) d] is the packed projection
     output without bias, bias [(h_q + 2 h_kv) d]; token i < length[b] of
-    sequence b sits at position start[b] + i.  Returns (q [B, C, h_q, d] with
-    bias, not rotated -- rows past length[b] NaN --, k_cache', v_cache')."""
+    sequence b sits at position start[b] + i.  Returns (q [B, C, h_q, d]
+    with bias and rotated -- rows past length[b] NaN --, k_cache',
+    v_cache')."""
     x = np.asarray(qkv, np.float64) + np.asarray(bias, np.float64)
     B, C, _ = x.shape
     d = x.shape[-1] // (h_q + 2 * h_kv)
@@ -335,8 +340,11 @@ def qkv_epilogue(qkv, bias, k_cache, v_cache, h_q: int, h_kv: int, start,
     kc, vc = cache_append(k_cache, v_cache, k, v, start, length, theta)
     n_new = per_sequence(C if length is None else length, B)
     q_out = np.full(q.shape, np.nan)
+    start = per_sequence(start, B)
     for b in range(B):
-        q_out[b, :n_new[b]] = q[b, :n_new[b]]
+        n = int(n_new[b])
+        if n:
+            q_out[b, :n] = rope(q[b, :n], chunk_positions(int(start[b]), n), theta)
     return q_out, kc, vc
 
 

@@ -17,7 +17,7 @@ import torch
 from ._lib import (GQA_BF16, GQA_F32, GQAError, check, lib)
 
 __all__ = ["rope_apply", "prefill", "decode", "prefill_chunk", "decode_ragged",
-           "decode_append", "prefill_workspace_size", "prefill_chunk_workspace_size",
+           "decode_append", "qkv_epilogue", "prefill_workspace_size", "prefill_chunk_workspace_size",
            "decode_workspace_size", "timing_enable", "timing_read", "version",
            "GQAError", "ROPE_THETA"]
 
@@ -152,21 +152,26 @@ def prefill_chunk_workspace_size(dtype: torch.dtype, B: int, kend: int, h_kv: in
 
 
 def prefill_chunk(q, k, v, k_cache, v_cache, start, length=None, *, kend: int | None = None,
-                  theta: float = ROPE_THETA, scale: float | None = None,
+                  theta: float = ROPE_THETA, scale: float | None = None, q_rotated: bool = False,
                   out_dtype: torch.dtype = torch.float32, out=None, workspace=None):
     """Chunked causal prefill.  q [B, C, h_q, d], k/v [B, C, h_kv, d] (pre-RoPE)
     are the new rows of each sequence, at positions start[b] + i for
     i < length[b]; they are appended to the caches [B, cap, h_kv, d] and
-    attend to every cached row up to their own position.  kend bounds
+    attend to every cached row up to their own position (k = v = None: the
+    caches already hold these rows, e.g. from qkv_epilogue; q_rotated: q is
+    rotated already, as qkv_epilogue returns it).  kend bounds
     start[b] + length[b] (default: cap).  Returns o [B, C, h_q, d]; rows
     i >= length[b] are left as they were in ``out`` (uninitialised if None)."""
     _dev(q, k, v, k_cache, v_cache, out, workspace)
     B, C, h_q, d = q.shape
-    h_kv = k.shape[2]
-    if k.shape != (B, C, h_kv, d) or v.shape != k.shape:
-        raise ValueError("k/v must be [B, C, h_kv, d] matching q")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k and v must share one dtype")
+    h_kv = k_cache.shape[2]
+    if (k is None) != (v is None):
+        raise ValueError("k and v must both be given or both be None")
+    if k is not None:
+        if k.shape != (B, C, h_kv, d) or v.shape != k.shape:
+            raise ValueError("k/v must be [B, C, h_kv, d] matching q and the caches")
+        if not (q.dtype == k.dtype == v.dtype):
+            raise TypeError("q, k and v must share one dtype")
     cap = _caches(k_cache, v_cache, B, h_kv, d, q.dtype)
     kend = cap if kend is None else kend
     st = _seq_array(start, B, q.device, "start")
@@ -180,9 +185,37 @@ def prefill_chunk(q, k, v, k_cache, v_cache, start, length=None, *, kend: int | 
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     check(lib().gqa_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dt(q), _dt(out), B, C,
                                   h_q, h_kv, d, _ptr(st), _ptr(ln), kend, theta, scale,
-                                  _ptr(k_cache), _ptr(v_cache), cap, _ptr(workspace),
+                                  int(q_rotated), _ptr(k_cache), _ptr(v_cache), cap,
+                                  _ptr(workspace),
                                   workspace.numel(), _stream()))
     return out
+
+
+def qkv_epilogue(qkv, bias, k_cache, v_cache, h_q: int, start, length=None, *,
+                 kend: int | None = None, theta: float = ROPE_THETA, q_out=None):
+    """Bias, head split and rotation of the packed projection output
+    qkv [B, C, (h_q + 2 h_kv) d] (query heads, then key heads, then value
+    heads); bias [(h_q + 2 h_kv) d] or None.  Writes the rotated K and the V
+    of token i < length[b] into cache row start[b] + i and returns its
+    rotated queries [B, C, h_q, d] (for prefill_chunk / decode_ragged with
+    q_rotated=True)."""
+    _dev(qkv, bias, k_cache, v_cache, q_out)
+    B, C, width = qkv.shape
+    h_kv, d = k_cache.shape[2], k_cache.shape[3]
+    if width != (h_q + 2 * h_kv) * d:
+        raise ValueError(f"qkv width {width} != (h_q + 2 h_kv) d = {(h_q + 2 * h_kv) * d}")
+    if bias is not None and (bias.shape != (width,) or bias.dtype != qkv.dtype):
+        raise ValueError("bias must be [(h_q + 2 h_kv) d] of qkv's dtype")
+    cap = _caches(k_cache, v_cache, B, h_kv, d, qkv.dtype)
+    kend = cap if kend is None else kend
+    st = _seq_array(start, B, qkv.device, "start")
+    ln = _seq_array(length, B, qkv.device, "length")
+    if q_out is None:
+        q_out = torch.empty((B, C, h_q, d), dtype=qkv.dtype, device=qkv.device)
+    check(lib().gqa_qkv_epilogue(_ptr(qkv), _ptr(bias), _ptr(q_out), _ptr(k_cache),
+                                 _ptr(v_cache), _dt(qkv), B, C, h_q, h_kv, d, cap, _ptr(st),
+                                 _ptr(ln), kend, theta, _stream()))
+    return q_out
 
 
 def _decode_common(q, k_cache, v_cache, out, out_dtype, workspace, scale):
@@ -200,10 +233,10 @@ def _decode_common(q, k_cache, v_cache, out, out_dtype, workspace, scale):
 
 
 def decode_ragged(q, k_cache, v_cache, kv_len, q_pos, *, max_kv_len: int | None = None,
-                  theta: float = ROPE_THETA, scale: float | None = None,
+                  theta: float = ROPE_THETA, scale: float | None = None, q_rotated: bool = False,
                   out_dtype: torch.dtype = torch.float32, out=None, workspace=None):
     """Decode with per-sequence kv_len[b] and q_pos[b] (int64, B entries);
-    max_kv_len bounds kv_len (default: cap)."""
+    max_kv_len bounds kv_len (default: cap); q_rotated: q is rotated already."""
     _dev(q, k_cache, v_cache, out, workspace)
     B, h_q, h_kv, d, cap, scale, out, workspace = _decode_common(
         q, k_cache, v_cache, out, out_dtype, workspace, scale)
@@ -212,7 +245,8 @@ def decode_ragged(q, k_cache, v_cache, kv_len, q_pos, *, max_kv_len: int | None 
     max_kv_len = cap if max_kv_len is None else max_kv_len
     check(lib().gqa_decode_ragged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _dt(q),
                                   _dt(out), B, h_q, h_kv, d, cap, _ptr(kl), _ptr(qp), max_kv_len,
-                                  theta, scale, _ptr(workspace), workspace.numel(), _stream()))
+                                  theta, scale, int(q_rotated), _ptr(workspace),
+                                  workspace.numel(), _stream()))
     return out
 
 

@@ -267,7 +267,7 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   if (g_timing.on) ev = g_timing.take();
   hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
                                     out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, kv_len, q_pos,
-                                    nullptr, nullptr, 0, std::log2(theta), scale,
+                                    nullptr, nullptr, 0, 0, std::log2(theta), scale,
                                     (float*)(wsb + ws.m_off),
                                     (float*)(wsb + ws.l_off), (float*)(wsb + ws.o_off),
                                     (hipStream_t)stream, ev.first, ev.second);
@@ -284,11 +284,13 @@ size_t gqa_prefill_chunk_workspace_size(int in_dtype, int64_t B, int64_t kend, i
 int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int in_dtype,
                       int out_dtype, int64_t B, int64_t C, int h_q, int h_kv, int d,
                       const int64_t* start, const int64_t* len, int64_t kend, double theta,
-                      float scale, void* k_cache, void* v_cache, int64_t cap, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      float scale, int q_rotated, void* k_cache, void* v_cache, int64_t cap,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
-  if (!q || !k || !v || !o || !start || !k_cache || !v_cache)
-    return fail(GQA_ERR_INVALID_ARG, "q, k, v, o, start, k_cache and v_cache must be non-NULL");
+  if (!q || !o || !start || !k_cache || !v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "q, o, start, k_cache and v_cache must be non-NULL");
+  if ((k == nullptr) != (v == nullptr))
+    return fail(GQA_ERR_INVALID_ARG, "k and v must both be set or both be NULL");
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
     return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in=%d, out=%d)", in_dtype, out_dtype);
   if (B < 1 || C < 1) return fail(GQA_ERR_INVALID_ARG, "B and C must be >= 1");
@@ -319,9 +321,12 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
   hipError_t e = gqa::launch_rope_table(cs, kend, d, 0, l2t, st);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   // 1) the chunk's rotated K and its V into the cache rows start[b] + i
-  e = gqa::launch_cache_append(k, v, k_cache, v_cache, in_dtype == GQA_BF16, start, len, B, C,
-                               h_kv, d, cap, kend, l2t, st);
-  if (e != hipSuccess) return hip_fail(e, "cache append launch");
+  //    (k, v NULL: an earlier call, e.g. gqa_qkv_epilogue, put them there)
+  if (k) {
+    e = gqa::launch_cache_append(k, v, k_cache, v_cache, in_dtype == GQA_BF16, start, len, B, C,
+                                 h_kv, d, cap, kend, l2t, st);
+    if (e != hipSuccess) return hip_fail(e, "cache append launch");
+  }
 
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   if (g_timing.on) ev = g_timing.take();
@@ -337,15 +342,16 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     // 3) the chunk's queries against them
     if (ev.first) (void)hipEventRecord(ev.first, st);
-    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, cs, o, out_dtype == GQA_BF16, B,
-                                 C, Lpad, h_q, h_kv, d, scale, 1, start, len, kend, st);
+    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, q_rotated ? nullptr : cs, o,
+                                 out_dtype == GQA_BF16, B, C, Lpad, h_q, h_kv, d, scale, 1, start,
+                                 len, kend, st);
   } else {
     // 2) the chunk's queries against the cache itself
     const gqa::KvStrides csd{cap * h_kv * d, d, (int64_t)h_kv * d};   // [B, cap, h_kv, d]
     if (ev.first) (void)hipEventRecord(ev.first, st);
-    e = gqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache, cs,
-                                o, out_dtype == GQA_BF16, B, C, h_q, h_kv, d, scale, 1, csd, csd,
-                                start, len, kend, st);
+    e = gqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache,
+                                q_rotated ? nullptr : cs, o, out_dtype == GQA_BF16, B, C, h_q,
+                                h_kv, d, scale, 1, csd, csd, start, len, kend, st);
   }
   if (ev.second) {
     (void)hipEventRecord(ev.second, st);
@@ -388,15 +394,15 @@ int decode_ragged_check(const void* q, const void* k_cache, const void* v_cache,
 int decode_ragged_launch(const void* q, const void* k_cache, const void* v_cache, void* o,
                          int in_dtype, int out_dtype, int64_t B, int h_q, int h_kv, int d,
                          int64_t cap, const int64_t* kvl, const int64_t* qpos, int from_pos,
-                         int64_t max_kv_len, double theta, float scale, void* workspace,
-                         hipStream_t st) {
+                         int q_rotated, int64_t max_kv_len, double theta, float scale,
+                         void* workspace, hipStream_t st) {
   const DecodeWs ws = decode_ws(B, h_q, h_kv, d, cap);
   char* wsb = (char*)workspace;
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   if (g_timing.on) ev = g_timing.take();
   hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
                                     out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, max_kv_len, 0,
-                                    kvl, qpos, from_pos, std::log2(theta), scale,
+                                    kvl, qpos, from_pos, q_rotated, std::log2(theta), scale,
                                     (float*)(wsb + ws.m_off), (float*)(wsb + ws.l_off),
                                     (float*)(wsb + ws.o_off), st, ev.first, ev.second);
   if (ev.first) g_timing.rec[1].push_back(ev);
@@ -408,8 +414,8 @@ int decode_ragged_launch(const void* q, const void* k_cache, const void* v_cache
 int gqa_decode_ragged(const void* q, const void* k_cache, const void* v_cache, void* o,
                       int in_dtype, int out_dtype, int64_t B, int h_q, int h_kv, int d,
                       int64_t cap, const int64_t* kv_len, const int64_t* q_pos,
-                      int64_t max_kv_len, double theta, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      int64_t max_kv_len, double theta, float scale, int q_rotated,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (!q || !k_cache || !v_cache || !o || !kv_len || !q_pos)
     return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache, o, kv_len and q_pos must be non-NULL");
@@ -417,8 +423,8 @@ int gqa_decode_ragged(const void* q, const void* k_cache, const void* v_cache, v
                                    cap, max_kv_len, theta, scale, workspace, workspace_bytes))
     return rc;
   return decode_ragged_launch(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap,
-                              kv_len, q_pos, 0, max_kv_len, theta, scale, workspace,
-                              (hipStream_t)stream);
+                              kv_len, q_pos, 0, q_rotated != 0, max_kv_len, theta, scale,
+                              workspace, (hipStream_t)stream);
 }
 
 int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
@@ -447,7 +453,33 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
   if (e != hipSuccess) return hip_fail(e, "cache append launch");
   // 2) attend to rows 0 .. pos[b]
   return decode_ragged_launch(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap,
-                              nullptr, pos, 1, max_pos + 1, theta, scale, workspace, st);
+                              nullptr, pos, 1, 0, max_pos + 1, theta, scale, workspace, st);
+}
+
+int gqa_qkv_epilogue(const void* qkv, const void* bias, void* q_out, void* k_cache,
+                     void* v_cache, int dtype, int64_t B, int64_t C, int h_q, int h_kv, int d,
+                     int64_t cap, const int64_t* start, const int64_t* len, int64_t kend,
+                     double theta, void* stream) {
+  g_err.clear();
+  if (!qkv || !q_out || !k_cache || !v_cache || !start)
+    return fail(GQA_ERR_INVALID_ARG, "qkv, q_out, k_cache, v_cache and start must be non-NULL");
+  if (!dtype_ok(dtype)) return fail(GQA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (B < 1 || C < 1) return fail(GQA_ERR_INVALID_ARG, "B and C must be >= 1");
+  if (int rc = check_heads(h_q, h_kv)) return rc;
+  if (int rc = check_d(d)) return rc;
+  if (int rc = check_theta_scale(theta, 1.0f)) return rc;
+  if (kend < 1 || kend > cap)
+    return fail(GQA_ERR_INVALID_ARG, "kend=%lld outside [1, cap=%lld]", (long long)kend,
+                (long long)cap);
+  if (kend > (INT64_C(1) << 40) || B * C > (INT64_C(1) << 32))
+    return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernel's index range");
+  if (!aligned16(qkv) || !aligned16(bias) || !aligned16(q_out) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  hipError_t e = gqa::launch_qkv_epilogue(qkv, bias, q_out, k_cache, v_cache, dtype == GQA_BF16,
+                                          start, len, B, C, h_q, h_kv, d, cap, kend,
+                                          std::log2(theta), (hipStream_t)stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e, "QKV epilogue launch");
 }
 
 int gqa_timing_enable(int on) {

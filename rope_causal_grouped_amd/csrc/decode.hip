@@ -20,7 +20,8 @@
 // sets the number of chunks.  Chunks past a sequence's length leave an empty
 // state (m = -inf, l = 0, o = 0) that the merge weighs with zero.  A
 // sequence whose length or position is out of range has no keys at all and
-// its output becomes NaN.
+// its output becomes NaN.  With q_rotated set the query arrives rotated
+// already (gqa_qkv_epilogue writes it so) and is used as given.
 
 #include "common.h"
 #include "launch.h"
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
     float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int64_t cap, int kv_len_max,
     double q_pos_s, double log2_theta, float sl2, int n_split, const int64_t* __restrict__ kvl_arr,
-    const int64_t* __restrict__ qpos_arr, int kvl_from_pos) {
+    const int64_t* __restrict__ qpos_arr, int kvl_from_pos, int q_rotated) {
   constexpr int CH = kDecodeChunk;
   constexpr int WK = CH / 4;            // keys per wave
   constexpr int NS = D / 32;            // 32-dim k-steps of S^T
@@ -114,8 +115,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = s * 32 + h4 * 8 + e;
-        float cs_c, cs_s;
-        rope_cos_sin(q_pos, rope_omega(j, D, log2_theta), cs_c, cs_s);
+        float cs_c = 1.f, cs_s = 0.f;   // q_rotated: the query is used as given
+        if (!q_rotated) rope_cos_sin(q_pos, rope_omega(j, D, log2_theta), cs_c, cs_s);
         const float x1 = (e & 1) ? __uint_as_float(r1[e >> 1] & 0xffff0000u)
                                  : __uint_as_float(r1[e >> 1] << 16);
         const float x2 = (e & 1) ? __uint_as_float(r2[e >> 1] & 0xffff0000u)
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po, int h_q, int h_kv,
     int g, int n_hb, int64_t cap, int kv_len_max, double q_pos_s, double log2_theta, float scale,
     int n_split, const int64_t* __restrict__ kvl_arr, const int64_t* __restrict__ qpos_arr,
-    int kvl_from_pos) {
+    int kvl_from_pos, int q_rotated) {
   constexpr int CH = kDecodeChunk;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float qs[16][D];
@@ -288,8 +289,8 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     float y1 = 0.f, y2 = 0.f;
     if (cc < nh) {
       const float* qrow = q + ((int64_t)b * h_q + (int64_t)u * g + hb * 16 + cc) * D;
-      float c, s;
-      rope_cos_sin(q_pos, rope_omega(j, D, log2_theta), c, s);
+      float c = 1.f, s = 0.f;   // q_rotated: the query is used as given
+      if (!q_rotated) rope_cos_sin(q_pos, rope_omega(j, D, log2_theta), c, s);
       y1 = fmaf(qrow[j], c, -qrow[j + D / 2] * s);
       y2 = fmaf(qrow[j + D / 2], c, qrow[j] * s);
     }
@@ -399,7 +400,8 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restri
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, int in_bf16,
                          int out_bf16, int64_t B, int h_q, int h_kv, int d, int64_t cap,
                          int64_t kv_len, int64_t q_pos, const int64_t* kvl_arr,
-                         const int64_t* qpos_arr, int kvl_from_pos, double log2_theta,
+                         const int64_t* qpos_arr, int kvl_from_pos, int q_rotated,
+                         double log2_theta,
                          float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end) {
   const int g = h_q / h_kv;
@@ -413,23 +415,23 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
       decode_split_bf16_kernel<128><<<grid, 256, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
           h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split, kvl_arr,
-          qpos_arr, kvl_from_pos);
+          qpos_arr, kvl_from_pos, q_rotated);
     else
       decode_split_bf16_kernel<64><<<grid, 256, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
           h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split, kvl_arr,
-          qpos_arr, kvl_from_pos);
+          qpos_arr, kvl_from_pos, q_rotated);
   } else {
     if (d == 128)
       decode_split_f32_kernel<128><<<grid, 256, 0, st>>>(
           (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
           n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split, kvl_arr, qpos_arr,
-          kvl_from_pos);
+          kvl_from_pos, q_rotated);
     else
       decode_split_f32_kernel<64><<<grid, 256, 0, st>>>(
           (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
           n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split, kvl_arr, qpos_arr,
-          kvl_from_pos);
+          kvl_from_pos, q_rotated);
   }
   hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, st);

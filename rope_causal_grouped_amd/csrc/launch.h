@@ -34,6 +34,11 @@ hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc,
                                int h_kv, int d, int64_t cap, int64_t end, double log2_theta,
                                hipStream_t st);
 
+hipError_t launch_qkv_epilogue(const void* x, const void* bias, void* q_out, void* kc, void* vc,
+                               int bf16, const int64_t* start, const int64_t* len, int64_t B,
+                               int64_t C, int h_q, int h_kv, int d, int64_t cap, int64_t end,
+                               double log2_theta, hipStream_t st);
+
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
                                const float* kmax, const float2* cs, void* o, int out_bf16,
                                int64_t B, int64_t L, int64_t Lpad, int h_q, int h_kv, int d,
@@ -57,7 +62,8 @@ int decode_num_splits(int64_t kv_len);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, int in_bf16,
                          int out_bf16, int64_t B, int h_q, int h_kv, int d, int64_t cap,
                          int64_t kv_len, int64_t q_pos, const int64_t* kvl_arr,
-                         const int64_t* qpos_arr, int kvl_from_pos, double log2_theta,
+                         const int64_t* qpos_arr, int kvl_from_pos, int q_rotated,
+                         double log2_theta,
                          float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end);
 

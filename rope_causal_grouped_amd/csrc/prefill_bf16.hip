@@ -224,12 +224,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     u32x4 raw[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) raw[s] = *(const u32x4*)(qrow + s * 16 + hl * 8);
-    const float2* csr = cs + (int64_t)pos * (D / 2) + hl * 8;
+    const float2* csr = cs + (int64_t)pos * (D / 2) + hl * 8;   // (cs NULL: q is rotated)
 #pragma unroll
     for (int s = 0; s < NS / 2; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float2 r2 = csr[s * 16 + e];
+        const float2 r2 = cs ? csr[s * 16 + e] : make_float2(1.f, 0.f);   // NULL: rotated
         const uint32_t w1 = raw[s][e >> 1], w2 = raw[s + NS / 2][e >> 1];
         const float x1 = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
         const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     for (int e = 0; e < E; ++e) {
       const int j = part * E + e;
       const float x1 = src[j], x2 = src[j + D / 2];
-      const float2 r2 = csr[j];
+      const float2 r2 = cs ? csr[j] : make_float2(1.f, 0.f);   // cs NULL: q is rotated
       qr[e] = fmaf(x1, r2.x, -x2 * r2.y);
       qr[E + e] = fmaf(x2, r2.x, x1 * r2.y);
     }

@@ -343,4 +343,137 @@ hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* c
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// QKV projection epilogue (walkthrough §4.1.3 steps 1-3 and §4.2: each
+// projection adds its bias, the flat output is cut into heads, Q and K are
+// rotated at their position; the closing note of §4.1.3: the h_kv groups' K
+// and V go to the cache).  x[B, C, (h_q + 2 h_kv) d] is the packed
+// projection output (query heads, then key heads, then value heads); token
+// i < len[b] of sequence b sits at position p = start[b] + i:
+//   q_out[b][i][t] = RoPE(x_Q(t) + bias_Q(t), p),
+//   kc[b][p][u]    = RoPE(x_K(u) + bias_K(u), p),  vc[b][p][u] = x_V(u) + bias_V(u).
+// A workgroup takes kEpiTokens tokens: their cos/sin (one per pair, shared by
+// all h_q + h_kv heads) go to LDS first; then one item per pair of Q or K
+// chunks (dims c.. and d/2 + c..) that one rotation couples, or per 16-byte
+// chunk of a V head.  Sums and rotations in fp32, one rounding to the
+// storage type.  Sequences outside [0, end) are skipped.
+constexpr int kEpiTokens = 4;
+
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_epilogue_kernel(
+    const T* __restrict__ x, const T* __restrict__ bias, T* __restrict__ q_out,
+    T* __restrict__ kc, T* __restrict__ vc, const int64_t* __restrict__ start,
+    const int64_t* __restrict__ len, int64_t n_rows, int64_t C, int h_q, int h_kv, int d,
+    int64_t cap, int64_t end, double log2_theta) {
+  constexpr int E = 16 / sizeof(T);             // elements per 16-byte chunk
+  __shared__ float2 csl[kEpiTokens][64];        // (cos, sin) per token and pair (d <= 128)
+  const int cpr = d / E;                        // chunks per head row
+  const int half = d / 2;
+  const int nq = h_q * (cpr / 2), nk = h_kv * (cpr / 2), nv = h_kv * cpr;
+  const int per_row = nq + nk + nv;
+  const int width = (h_q + 2 * h_kv) * d;
+  const int64_t row0 = (int64_t)blockIdx.x * kEpiTokens;
+  // position of token `tok` of this workgroup, or -1 if it is not written
+  auto token_pos = [&](int tok) -> int64_t {
+    const int64_t row = row0 + tok;
+    if (row >= n_rows) return -1;
+    const int64_t b = row / C, i = row % C;
+    const int64_t s0 = start[b], n = len ? len[b] : C;
+    if (!(s0 >= 0 && n >= 0 && n <= C && s0 + n <= end) || i >= n) return -1;
+    return s0 + i;
+  };
+  for (int idx = threadIdx.x; idx < kEpiTokens * half; idx += blockDim.x) {
+    const int tok = idx / half, j = idx % half;
+    const int64_t p = token_pos(tok);
+    float c = 1.f, sn = 0.f;
+    if (p >= 0) rope_cos_sin((double)p, rope_omega(j, d, log2_theta), c, sn);
+    csl[tok][j] = make_float2(c, sn);
+  }
+  __syncthreads();
+  auto load = [&](const T* p, float* f) {
+    const u32x4 w = *(const u32x4*)p;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = bf16_bits_to_f32((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(w[e]);
+    }
+  };
+  auto store = [&](T* p, const float* f) {
+    u32x4 w;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)f32_to_bf16_bits(f[2 * e]) | ((uint32_t)f32_to_bf16_bits(f[2 * e + 1]) << 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(f[e]);
+    }
+    *(u32x4*)p = w;
+  };
+  auto add_bias = [&](float* f, int col) {
+    if (!bias) return;
+    float bf[E];
+    load(bias + col, bf);
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] += bf[e];
+  };
+  for (int it = threadIdx.x; it < kEpiTokens * per_row; it += blockDim.x) {
+    const int tok = it / per_row, r = it % per_row;
+    const int64_t p = token_pos(tok);
+    if (p < 0) continue;
+    const int64_t row = row0 + tok;
+    const int64_t b = row / C;
+    const T* xr = x + row * width;
+    float f[E];
+    if (r < nq + nk) {                          // Q or K: chunk c of both halves of a head
+      const bool is_q = r < nq;
+      const int hh = is_q ? r / (cpr / 2) : (r - nq) / (cpr / 2);
+      const int c = (is_q ? r : r - nq) % (cpr / 2);
+      const int col1 = (is_q ? hh : h_q + hh) * d + c * E, col2 = col1 + half;
+      float g[E];
+      load(xr + col1, f);
+      add_bias(f, col1);
+      load(xr + col2, g);
+      add_bias(g, col2);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float2 cs = csl[tok][c * E + e];
+        const float y1 = fmaf(f[e], cs.x, -g[e] * cs.y);
+        const float y2 = fmaf(g[e], cs.x, f[e] * cs.y);
+        f[e] = y1;
+        g[e] = y2;
+      }
+      T* dst = is_q ? q_out + (row * h_q + hh) * d : kc + ((b * cap + p) * h_kv + hh) * d;
+      store(dst + c * E, f);
+      store(dst + half + c * E, g);
+    } else {                                    // V chunk
+      const int u = (r - nq - nk) / cpr, c = (r - nq - nk) % cpr;
+      const int col = (h_q + h_kv + u) * d + c * E;
+      load(xr + col, f);
+      add_bias(f, col);
+      store(vc + ((b * cap + p) * h_kv + u) * d + c * E, f);
+    }
+  }
+}
+
+hipError_t launch_qkv_epilogue(const void* x, const void* bias, void* q_out, void* kc, void* vc,
+                               int bf16, const int64_t* start, const int64_t* len, int64_t B,
+                               int64_t C, int h_q, int h_kv, int d, int64_t cap, int64_t end,
+                               double log2_theta, hipStream_t st) {
+  const int64_t n_rows = B * C;
+  const unsigned grid = (unsigned)((n_rows + kEpiTokens - 1) / kEpiTokens);
+  if (bf16)
+    qkv_epilogue_kernel<uint16_t><<<grid, 256, 0, st>>>(
+        (const uint16_t*)x, (const uint16_t*)bias, (uint16_t*)q_out, (uint16_t*)kc, (uint16_t*)vc,
+        start, len, n_rows, C, h_q, h_kv, d, cap, end, log2_theta);
+  else
+    qkv_epilogue_kernel<float><<<grid, 256, 0, st>>>((const float*)x, (const float*)bias,
+                                                     (float*)q_out, (float*)kc, (float*)vc, start,
+                                                     len, n_rows, C, h_q, h_kv, d, cap, end,
+                                                     log2_theta);
+  return hipGetLastError();
+}
+
 }  // namespace gqa

@@ -421,8 +421,8 @@ def pin_qkv_layout(orc):
 
 
 def pin_qkv_epilogue_then_attention(orc):
-    """Epilogue, then a chunk attending to the cache it filled, equals the
-    one-shot prefill of the biased projections."""
+    """Epilogue (which rotates Q and K), then a chunk attending to the cache
+    it filled, equals the one-shot prefill of the biased projections."""
     rng = _rng(18)
     B, L, h_q, h_kv, d = 2, 9, 4, 2, 8
     width = (h_q + 2 * h_kv) * d
@@ -434,7 +434,8 @@ def pin_qkv_epilogue_then_attention(orc):
     v = x[..., (h_q + h_kv) * d:].reshape(B, L, h_kv, d)
     qe, kc, vc = orc.qkv_epilogue(qkv, bias, np.zeros((B, L, h_kv, d)),
                                   np.zeros((B, L, h_kv, d)), h_q, h_kv, 0)
-    close(orc.prefill_chunk(qe, kc, vc, 0), orc.prefill(q, k, v), 1e-12, "epilogue + chunk")
+    close(orc.prefill_chunk(qe, kc, vc, 0, q_rotated=True), orc.prefill(q, k, v), 1e-12,
+          "epilogue + chunk")
 
 
 ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,

@@ -121,8 +121,8 @@ def chunk_call(lib, **kw):
     a.update(kw)
     return lib.gqa_prefill_chunk(a["q"], a["k"], a["v"], a["o"], a["in_dt"], a["out_dt"], a["B"],
                                  a["C"], a["h_q"], a["h_kv"], a["d"], a["start"], a["len"],
-                                 a["kend"], a["theta"], a["scale"], a["kc"], a["vc"], a["cap"],
-                                 a["ws"], a["wsb"], a["stream"])
+                                 a["kend"], a["theta"], a["scale"], 0, a["kc"], a["vc"],
+                                 a["cap"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -135,6 +135,7 @@ def chunk_call(lib, **kw):
     (dict(d=96), _lib.GQA_ERR_UNSUPPORTED),
     (dict(kc=FAKE + 8), _lib.GQA_ERR_INVALID_ARG),         # misaligned
     (dict(wsb=64), _lib.GQA_ERR_WORKSPACE),
+    (dict(k=None), _lib.GQA_ERR_INVALID_ARG),              # k and v: both or neither
 ])
 def test_prefill_chunk_rejects(lib, kw, code):
     assert chunk_call(lib, **kw) == code
@@ -148,7 +149,7 @@ def ragged_call(lib, **kw):
     a.update(kw)
     return lib.gqa_decode_ragged(a["q"], a["kc"], a["vc"], a["o"], a["in_dt"], a["out_dt"],
                                  a["B"], a["h_q"], a["h_kv"], a["d"], a["cap"], a["kvl"],
-                                 a["qpos"], a["max_kv"], a["theta"], a["scale"], a["ws"],
+                                 a["qpos"], a["max_kv"], a["theta"], a["scale"], 0, a["ws"],
                                  a["wsb"], a["stream"])
 
 
@@ -195,3 +196,28 @@ def test_chunk_workspace_sizes(lib):
     assert (lib.gqa_prefill_chunk_workspace_size(1, 4, 4096, 4, 128)
             == lib.gqa_prefill_workspace_size(1, 4, 4096, 4, 128))
     assert lib.gqa_prefill_chunk_workspace_size(0, 1, 1000, 2, 64) == 1000 * 32 * 8
+
+
+def epilogue_call(lib, **kw):
+    a = dict(qkv=FAKE, bias=None, q_out=FAKE, kc=FAKE, vc=FAKE, dt=1, B=2, C=16, h_q=28, h_kv=4,
+             d=128, cap=64, start=FAKE, len=None, kend=64, theta=1e6, stream=None)
+    a.update(kw)
+    return lib.gqa_qkv_epilogue(a["qkv"], a["bias"], a["q_out"], a["kc"], a["vc"], a["dt"],
+                                a["B"], a["C"], a["h_q"], a["h_kv"], a["d"], a["cap"],
+                                a["start"], a["len"], a["kend"], a["theta"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qkv=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(start=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(vc=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(kend=65), _lib.GQA_ERR_INVALID_ARG),
+    (dict(h_q=4, h_kv=28), _lib.GQA_ERR_INVALID_ARG),
+    (dict(d=96), _lib.GQA_ERR_UNSUPPORTED),
+    (dict(bias=FAKE + 4), _lib.GQA_ERR_INVALID_ARG),       # misaligned bias
+    (dict(dt=2), _lib.GQA_ERR_INVALID_ARG),
+    (dict(theta=0.5), _lib.GQA_ERR_INVALID_ARG),
+])
+def test_qkv_epilogue_rejects(lib, kw, code):
+    assert epilogue_call(lib, **kw) == code
+    assert lib.gqa_last_error()

@@ -219,3 +219,67 @@ def test_prefill_chunk_invalid_sequence_is_nan():
     o = host(o)
     assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1]))
     assert torch.count_nonzero(kc[1]) == 0 and torch.count_nonzero(kc[0, :C]) > 0
+
+
+# ------------------------------------------------------ QKV epilogue -----
+
+def packed(B, C, h_q, h_kv, d, dtype, seed):
+    """Packed projection output [B, C, (h_q + 2 h_kv) d] and a bias vector."""
+    rng = np.random.default_rng([seed, 9])
+    width = (h_q + 2 * h_kv) * d
+    x = rounded(rng.standard_normal((B, C, width), dtype=np.float32), dtype)
+    bias = rounded(0.5 * rng.standard_normal(width, dtype=np.float32), dtype)
+    return x, bias
+
+
+@pytest.mark.parametrize("dtype,heads", [(torch.bfloat16, (28, 4, 128)),
+                                         (torch.float32, (14, 2, 64))],
+                         ids=["bf16_28_4", "f32_14_2"])
+def test_qkv_epilogue(dtype, heads):
+    h_q, h_kv, d = heads
+    B, C, cap = 3, 100, 700
+    start, length = np.array([0, 500, 37]), np.array([100, 50, 0])
+    note(f"qkv_epilogue {dtype} {heads}")
+    x, bias = packed(B, C, h_q, h_kv, d, dtype, 40)
+    kc0 = np.full((B, cap, h_kv, d), 2.0)
+    vc0 = np.full((B, cap, h_kv, d), -2.0)
+    kcd, vcd = dev(kc0, dtype), dev(vc0, dtype)
+    q_out = torch.full((B, C, h_q, d), 9.0, dtype=dtype, device="cuda")
+    gqa.qkv_epilogue(dev(x, dtype), dev(bias, dtype), kcd, vcd, h_q, torch.tensor(start),
+                     torch.tensor(length), kend=650, q_out=q_out)
+    torch.cuda.synchronize()
+    q_want, kc_want, vc_want = oracle.qkv_epilogue(x, bias, kc0, vc0, h_q, h_kv, start, length)
+    qg, kg, vg = host(q_out), host(kcd), host(vcd)
+    for b in range(B):
+        s0, n = int(start[b]), int(length[b])
+        assert_rotated_rows(qg[b, :n], q_want[b, :n], dtype, f"q rows {b}")
+        assert np.all(qg[b, n:] == 9.0), "q rows past len[b] were written"
+        assert_rotated_rows(kg[b, s0:s0 + n], kc_want[b, s0:s0 + n], dtype, f"K rows {b}")
+        assert_rotated_rows(vg[b, s0:s0 + n], vc_want[b, s0:s0 + n], dtype, f"V rows {b}")
+        assert np.all(kg[b, :s0] == 2.0) and np.all(kg[b, s0 + n:] == 2.0)
+        assert np.all(vg[b, :s0] == -2.0) and np.all(vg[b, s0 + n:] == -2.0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_epilogue_then_attention(dtype):
+    """Prompt: epilogue, then a chunk that attends to the rows it cached;
+    next token: epilogue at position L, then a ragged decode over L + 1 rows."""
+    h_q, h_kv, d = (28, 4, 128) if dtype == torch.bfloat16 else (14, 2, 64)
+    B, L, cap = 2, 333, 400
+    note(f"epilogue + attention {dtype}")
+    x, bias = packed(B, L + 1, h_q, h_kv, d, dtype, 41)
+    kcd = torch.zeros((B, cap, h_kv, d), dtype=dtype, device="cuda")
+    vcd = torch.zeros_like(kcd)
+    xd, bd = dev(x, dtype), dev(bias, dtype)
+    qp = gqa.qkv_epilogue(xd[:, :L].contiguous(), bd, kcd, vcd, h_q, [0] * B)
+    o = gqa.prefill_chunk(qp, None, None, kcd, vcd, [0] * B, kend=L, q_rotated=True)
+    qn = gqa.qkv_epilogue(xd[:, L:].contiguous(), bd, kcd, vcd, h_q, [L] * B)
+    od = gqa.decode_ragged(qn[:, 0].contiguous(), kcd, vcd, [L + 1] * B, [L] * B,
+                           q_rotated=True)
+    torch.cuda.synchronize()
+    z = np.zeros((B, cap, h_kv, d))
+    q_all, kc, vc = oracle.qkv_epilogue(x, bias, z, z, h_q, h_kv, 0)
+    assert_parity(host(o), oracle.prefill_chunk(q_all[:, :L], kc, vc, 0, q_rotated=True), dtype,
+                  "epilogue + chunk")
+    assert_parity(host(od), oracle.decode_ragged(q_all[:, L], kc, vc, L + 1, L, q_rotated=True),
+                  dtype, "epilogue + decode")
