@@ -6,10 +6,12 @@ from .gqa_oracle import (ROPE_THETA, inv_freq, rope, group_size, kv_group,
                          prefill_rows, decode, prefill_brute,
                          per_sequence, chunk_positions, cache_append,
                          attend_cached, prefill_chunk, decode_ragged,
-                         decode_append, qkv_sections, qkv_epilogue)
+                         decode_append, qkv_sections, qkv_epilogue,
+                         paged_rows, decode_paged, paged_append)
 
 __all__ = ["ROPE_THETA", "inv_freq", "rope", "group_size", "kv_group",
            "visible", "softmax_rows", "head_weights", "attend", "prefill",
            "prefill_rows", "decode", "prefill_brute", "per_sequence",
            "chunk_positions", "cache_append", "attend_cached", "prefill_chunk",
-           "decode_ragged", "decode_append", "qkv_sections", "qkv_epilogue"]
+           "decode_ragged", "decode_append", "qkv_sections", "qkv_epilogue",
+           "paged_rows", "decode_paged", "paged_append"]

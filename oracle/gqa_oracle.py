@@ -309,6 +309,59 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, pos,
     return decode_ragged(q, kc, vc, pos + 1, pos, theta, scale), kc, vc
 
 
+# --------------------------------------------------------- paged cache ---
+#
+# A paged cache keeps K (and V) in a pool of fixed-size pages instead of one
+# contiguous [cap] range per sequence; PagedAttention manages its memory in
+# blocks per KV head ([evo] §2, GQA's effect on inference).  Here a page
+# holds page_size consecutive positions of every KV head:
+# pool [num_pages, h_kv, page_size, d]; block_table[b][n] is the page that
+# holds positions n*page_size .. (n+1)*page_size - 1 of sequence b.
+
+def paged_rows(pool, block_table, b: int, n_rows: int, page_size: int):
+    """Rows 0 .. n_rows-1 of sequence b, gathered from the pool in
+    position order: [n_rows, h_kv, d]."""
+    pos = np.arange(n_rows)
+    pages = np.asarray(block_table)[b][pos // page_size]
+    return np.asarray(pool, np.float64)[pages, :, pos % page_size, :]
+
+
+def decode_paged(q, k_pool, v_pool, block_table, page_size: int, kv_len, q_pos,
+                 theta: float = ROPE_THETA, scale: float | None = None,
+                 q_rotated: bool = False):
+    """decode_ragged over a paged cache: sequence b's position j lives in
+    page block_table[b][j // page_size], row j % page_size."""
+    q = np.asarray(q, np.float64)
+    B = q.shape[0]
+    kv_len = per_sequence(kv_len, B)
+    q_pos = per_sequence(q_pos, B)
+    out = np.empty(q.shape, np.float64)
+    for b in range(B):
+        n = int(kv_len[b])
+        kb = paged_rows(k_pool, block_table, b, n, page_size)
+        vb = paged_rows(v_pool, block_table, b, n, page_size)
+        out[b] = decode_ragged(q[b:b + 1], kb[None], vb[None], n, int(q_pos[b]), theta,
+                               scale, q_rotated)[0]
+    return out
+
+
+def paged_append(k_pool, v_pool, k_new, v_new, block_table, page_size: int, pos,
+                 theta: float = ROPE_THETA):
+    """Write the new token of each sequence (k_new/v_new [B, h_kv, d],
+    pre-RoPE) at its position pos[b] of the paged cache, K rotated there.
+    Returns updated fp64 copies of both pools."""
+    kp = np.array(k_pool, np.float64, copy=True)
+    vp = np.array(v_pool, np.float64, copy=True)
+    B = np.shape(k_new)[0]
+    pos = per_sequence(pos, B)
+    for b in range(B):
+        p = int(pos[b])
+        page = int(np.asarray(block_table)[b][p // page_size])
+        kp[page, :, p % page_size, :] = rope(np.asarray(k_new[b], np.float64)[None], [p], theta)[0]
+        vp[page, :, p % page_size, :] = np.asarray(v_new[b], np.float64)
+    return kp, vp
+
+
 # ------------------------------------------------ QKV projection epilogue -
 
 def qkv_sections(h_q: int, h_kv: int, d: int):

@@ -438,6 +438,56 @@ def pin_qkv_epilogue_then_attention(orc):
           "epilogue + chunk")
 
 
+# ------------------------------------------------------- paged cache ----
+
+def _scatter_to_pages(kc, page_size, n_pages, rng):
+    """Scatter a contiguous cache [B, cap, h_kv, d] into a pool under a random
+    block table; unused pages hold a poison value."""
+    B, cap, h_kv, d = kc.shape
+    per_seq = cap // page_size
+    perm = rng.permutation(n_pages)[:B * per_seq].reshape(B, per_seq)
+    pool = np.full((n_pages, h_kv, page_size, d), 1e6)
+    for b in range(B):
+        for n in range(per_seq):
+            pool[perm[b, n]] = np.transpose(kc[b, n * page_size:(n + 1) * page_size], (1, 0, 2))
+    return pool, perm
+
+
+def pin_paged_decode_is_contiguous(orc):
+    """A paged cache holding the same rows under a shuffled block table gives
+    the contiguous ragged decode; pages outside the table (poisoned) and
+    rows past kv_len are never read."""
+    rng = _rng(19)
+    B, cap, h_q, h_kv, d, ps = 3, 24, 6, 2, 8, 4
+    q = _rand(rng, B, h_q, d)
+    kc = _rand(rng, B, cap, h_kv, d)
+    vc = _rand(rng, B, cap, h_kv, d)
+    kp, bt = _scatter_to_pages(kc, ps, 25, np.random.default_rng(5))
+    vp, _ = _scatter_to_pages(vc, ps, 25, np.random.default_rng(5))
+    kv_len, q_pos = np.array([1, 13, 24]), np.array([0, 20, 23])
+    close(orc.decode_paged(q, kp, vp, bt, ps, kv_len, q_pos),
+          orc.decode_ragged(q, kc, vc, kv_len, q_pos), 1e-12, "paged vs contiguous")
+
+
+def pin_paged_append_is_contiguous(orc):
+    """Appending into pages then decoding equals the contiguous appending step."""
+    rng = _rng(20)
+    B, cap, h_q, h_kv, d, ps = 2, 16, 4, 2, 8, 8
+    q = _rand(rng, B, h_q, d)
+    kn = _rand(rng, B, h_kv, d)
+    vn = _rand(rng, B, h_kv, d)
+    kc = _rand(rng, B, cap, h_kv, d)
+    vc = _rand(rng, B, cap, h_kv, d)
+    pos = np.array([9, 0])
+    want, kc2, vc2 = orc.decode_append(q, kn, vn, kc, vc, pos)
+    kp, bt = _scatter_to_pages(kc, ps, 7, np.random.default_rng(6))
+    vp, _ = _scatter_to_pages(vc, ps, 7, np.random.default_rng(6))
+    kp2, vp2 = orc.paged_append(kp, vp, kn, vn, bt, ps, pos)
+    close(orc.decode_paged(q, kp2, vp2, bt, ps, pos + 1, pos), want, 1e-12, "paged append")
+    for b in range(B):
+        close(orc.paged_rows(kp2, bt, b, cap, ps), kc2[b], 1e-12, "pool after append")
+
+
 ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_rope_half_split_pairing, pin_rope_norm, pin_rope_relative,
             pin_rope_group_law, pin_group_example, pin_repeat_interleave,
@@ -445,4 +495,5 @@ ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_shift_invariance, pin_decode_is_prefill_row, pin_prefill_rows,
             pin_chunked_prefill_is_prefill, pin_decode_append_is_prefill_row,
             pin_cache_append_pair0, pin_ragged_decode_is_single, pin_qkv_layout,
-            pin_qkv_epilogue_then_attention]
+            pin_qkv_epilogue_then_attention, pin_paged_decode_is_contiguous,
+            pin_paged_append_is_contiguous]

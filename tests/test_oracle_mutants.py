@@ -168,12 +168,34 @@ def m_qkv_heads_transposed(mod):
     mod.qkv_epilogue = qkv_epilogue
 
 
+def m_paged_row_major_page(mod):
+    def paged_rows(pool, block_table, b, n_rows, page_size):
+        pos = np.arange(n_rows)
+        pages = np.asarray(block_table)[b][pos // page_size]
+        pool = np.asarray(pool, np.float64)
+        flat = pool.reshape(pool.shape[0], -1, pool.shape[-1])      # page as [ps*h_kv] token-major
+        h_kv = pool.shape[1]
+        return np.stack([flat[pages, (pos % page_size) * h_kv + u] for u in range(h_kv)], axis=1)
+    mod.paged_rows = paged_rows
+
+
+def m_paged_page_of_next_block(mod):
+    orig = mod.paged_rows
+
+    def paged_rows(pool, block_table, b, n_rows, page_size):
+        bt = np.asarray(block_table)
+        shifted = np.concatenate([bt[:, 1:], bt[:, -1:]], axis=1)
+        return orig(pool, shifted, b, n_rows, page_size)
+    mod.paged_rows = paged_rows
+
+
 MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
            m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
            m_transposed_weights, m_softmax_no_norm, m_decode_unrotated_query,
            m_chunk_position_shift, m_ragged_first_value, m_cached_key_unrotated,
-           m_qkv_k_v_swapped, m_qkv_bias_dropped, m_qkv_heads_transposed]
+           m_qkv_k_v_swapped, m_qkv_bias_dropped, m_qkv_heads_transposed,
+           m_paged_row_major_page, m_paged_page_of_next_block]
 
 
 def failing_pins(mod):
