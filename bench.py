@@ -11,8 +11,10 @@ After the timed steps, the autoregressive entry points are measured on the
 same shapes (reported under "next", outside the step): the last 1024-row
 chunk of the prefill workload through gqa_prefill_chunk against a cache that
 holds the first 3072 rows, one gqa_decode_append step for 32 sequences at
-ragged positions 32767 - 256 b of a 32768-row cache, and gqa_qkv_epilogue
-over the packed projection output of the prefill workload's 4 x 4096 tokens.
+ragged positions 32767 - 256 b of a 32768-row cache, gqa_decode_paged on
+the decode workload's cache cut into 16-position pages under a shuffled
+block table, and gqa_qkv_epilogue over the packed projection output of the
+prefill workload's 4 x 4096 tokens.
 `value` is the prefill rate in TFLOP/s over the causal pairs only
 (4 * B * h_q * d * L(L+1)/2 flop per call) measured around the whole call;
 the decode rate (K/V cache bytes read once per KV group / call time) is
@@ -203,7 +205,55 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
                      "kernel_ms": split_avg, "traffic": None}}
     log(f"[bench] appending decode: {call_ms:.3f} ms per call")
-    del kn, vn, od, wsd
+    del kn, vn
+
+    # -- paged decode: the same 32768-row caches cut into 16-position pages,
+    #    scattered over the pool by a shuffled block table
+    ps = 16
+    n_pg = cap // ps
+    perm = torch.randperm(wd.B * n_pg, generator=torch.Generator().manual_seed(wd.seed))
+    permd = perm.to(dev)
+    pools = []
+    for c in (kc, vc):
+        pool = c.view(wd.B, n_pg, ps, wd.h_kv, wd.d).permute(0, 1, 3, 2, 4).reshape(
+            wd.B * n_pg, wd.h_kv, ps, wd.d)
+        shuf = torch.empty(pool.shape, dtype=pool.dtype, device=dev)
+        shuf[permd] = pool
+        pools.append(shuf)
+        del pool
+    del kc, vc
+    bt = permd.view(wd.B, n_pg).to(torch.int32)
+    qpos = torch.full((wd.B,), wd.q_pos, dtype=torch.int64, device=dev)
+    kvl = torch.full((wd.B,), cap, dtype=torch.int64, device=dev)
+
+    def paged():
+        gqa.decode_paged(qh, pools[0], pools[1], bt, qpos, kvl, out=od, workspace=wsd)
+
+    for _ in range(args.warmup):
+        paged()
+    torch.cuda.synchronize()
+    gqa.timing_read(1)
+    gqa.timing_enable(True)
+    e0.record()
+    for _ in range(K):
+        paged()
+    e1.record()
+    torch.cuda.synchronize()
+    gqa.timing_enable(False)
+    call_ms = e0.elapsed_time(e1) / K
+    split_ms, split_n = gqa.timing_read(1)
+    split_avg = split_ms / max(split_n, 1)
+    kvb = wd.decode_kv_bytes()
+    dach = kvb / (split_avg * 1e-3) / 1e9
+    res["decode_paged"] = {
+        "workload": f"{wd.name} over a paged cache: B{wd.B} x {cap} positions in {ps}-position "
+                    f"pages (shuffled block table), h_q{wd.h_q} h_kv{wd.h_kv} d{wd.d} bf16",
+        "value": kvb / (call_ms * 1e-3) / 1e9, "unit": "GB/s", "call_ms": call_ms,
+        "roofline": {"bound": "hbm", "kernel": "decode_split_bf16_kernel", "achieved": dach,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
+                     "kernel_ms": split_avg, "traffic": None}}
+    log(f"[bench] paged decode: {call_ms:.3f} ms per call")
+    del pools, bt, od, wsd
 
     # -- QKV epilogue on the prefill shape: packed projection output of all
     #    4096 tokens -> rotated Q, rotated K and V in a 4096-row cache

@@ -203,6 +203,37 @@ int gqa_qkv_epilogue(const void* qkv, const void* bias, void* q_out,
                      const int64_t* start, const int64_t* len, int64_t kend,
                      double theta, void* stream);
 
+/*
+ * Decode over a paged cache.  K and V live in page pools
+ * k_pool/v_pool [num_pages, h_kv, page_size, d] (in_dtype): a page holds
+ * page_size consecutive positions of every KV head (PagedAttention manages
+ * memory in blocks per KV head, "从 Qwen 1 到 Qwen 2 架构演进到底改了什么"
+ * (nxmr.cn) §2).  block_table [B][max_pages] (int32, device): position j of
+ * sequence b is row j % page_size of page block_table[b][j / page_size];
+ * q_pos [B] (int64, device) is each query's position.
+ *   k_new = v_new = NULL: sequence b attends to positions 0 .. kv_len[b]-1
+ *     (kv_len [B] int64 device array, kv_len[b] <= q_pos[b] + 1);
+ *   k_new, v_new [B, h_kv, d] set (kv_len NULL): one step with append --
+ *     the new token's K (rotated at q_pos[b]) and V are written at position
+ *     q_pos[b] first, then it attends to 0 .. q_pos[b].
+ * page_size is a power of two; max_kv_len bounds every length and
+ * max_kv_len <= max_pages * page_size.  A sequence whose length, position
+ * or page ids are out of range gets NaN output (and no cache write).
+ * q_rotated as for gqa_decode_ragged.  o [B, h_q, d] in out_dtype.
+ */
+size_t gqa_decode_paged_workspace_size(int64_t B, int h_q, int h_kv, int d,
+                                       int64_t max_kv_len);
+
+int gqa_decode_paged(const void* q, const void* k_new, const void* v_new,
+                     void* k_pool, void* v_pool, void* o,
+                     int in_dtype, int out_dtype,
+                     int64_t B, int h_q, int h_kv, int d,
+                     int page_size, int64_t num_pages,
+                     const int32_t* block_table, int64_t max_pages,
+                     const int64_t* kv_len, const int64_t* q_pos,
+                     int64_t max_kv_len, double theta, float scale, int q_rotated,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* gqa_last_error(void);
 
@@ -212,8 +243,8 @@ const char* gqa_version(void);
 /*
  * Kernel timing for benchmarks.  While enabled, each gqa_prefill and
  * gqa_prefill_chunk records a HIP event pair around its attention kernel
- * (which = 0) and each decode call around its split-K streaming kernel
- * (which = 1), on the caller's stream.  gqa_timing_read waits for the recorded events, returns
+ * (which = 0) and each decode call (contiguous or paged) around its split-K
+ * streaming kernel (which = 1), on the caller's stream.  gqa_timing_read waits for the recorded events, returns
  * the summed milliseconds and the launch count for `which`, and clears
  * them.  Not thread-safe; meant for a single benchmarking thread.
  */

@@ -17,7 +17,7 @@ import torch
 from ._lib import (GQA_BF16, GQA_F32, GQAError, check, lib)
 
 __all__ = ["rope_apply", "prefill", "decode", "prefill_chunk", "decode_ragged",
-           "decode_append", "qkv_epilogue", "prefill_workspace_size", "prefill_chunk_workspace_size",
+           "decode_append", "qkv_epilogue", "decode_paged", "decode_paged_workspace_size", "prefill_workspace_size", "prefill_chunk_workspace_size",
            "decode_workspace_size", "timing_enable", "timing_read", "version",
            "GQAError", "ROPE_THETA"]
 
@@ -269,6 +269,51 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, pos, *, max_pos: int | None
                                   _ptr(v_cache), _ptr(out), _dt(q), _dt(out), B, h_q, h_kv, d,
                                   cap, _ptr(ps), max_pos, theta, scale, _ptr(workspace),
                                   workspace.numel(), _stream()))
+    return out
+
+
+def decode_paged_workspace_size(B: int, h_q: int, h_kv: int, d: int, max_kv_len: int) -> int:
+    return lib().gqa_decode_paged_workspace_size(B, h_q, h_kv, d, max_kv_len)
+
+
+def decode_paged(q, k_pool, v_pool, block_table, q_pos, kv_len=None, *, k_new=None, v_new=None,
+                 max_kv_len: int | None = None, theta: float = ROPE_THETA,
+                 scale: float | None = None, q_rotated: bool = False,
+                 out_dtype: torch.dtype = torch.float32, out=None, workspace=None):
+    """Decode over page pools [num_pages, h_kv, page_size, d] through
+    block_table [B, max_pages] (int32).  Without k_new/v_new, sequence b
+    attends to positions 0..kv_len[b]-1; with them (kv_len None) the new
+    token is first written at q_pos[b].  max_kv_len defaults to
+    max_pages * page_size."""
+    _dev(q, k_pool, v_pool, block_table, k_new, v_new, out, workspace)
+    B, h_q, d = q.shape
+    num_pages, h_kv, page_size = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if k_pool.shape != (num_pages, h_kv, page_size, d) or v_pool.shape != k_pool.shape:
+        raise ValueError("pools must be [num_pages, h_kv, page_size, d] matching q")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q and the pools must share one dtype")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    max_pages = block_table.shape[1]
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    if k_new is not None and (k_new.shape != (B, h_kv, d) or v_new.shape != k_new.shape):
+        raise ValueError("k_new/v_new must be [B, h_kv, d]")
+    qp = _seq_array(q_pos, B, q.device, "q_pos")
+    kl = _seq_array(kv_len, B, q.device, "kv_len")
+    max_kv_len = max_pages * page_size if max_kv_len is None else max_kv_len
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        need = lib().gqa_decode_paged_workspace_size(B, h_q, h_kv, d, max_kv_len)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    check(lib().gqa_decode_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(out), _dt(q), _dt(out), B, h_q, h_kv, d, page_size,
+                                 num_pages, _ptr(block_table), max_pages, _ptr(kl), _ptr(qp),
+                                 max_kv_len, theta, scale, int(q_rotated), _ptr(workspace),
+                                 workspace.numel(), _stream()))
     return out
 
 

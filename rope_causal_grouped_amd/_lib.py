@@ -38,6 +38,9 @@ SIGNATURES = {
                                _I64, _D, _F, _P, _SZ, _P]),
     "gqa_qkv_epilogue": (_I, [_P, _P, _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _I64, _P, _P, _I64,
                               _D, _P]),
+    "gqa_decode_paged_workspace_size": (_SZ, [_I64, _I, _I, _I, _I64]),
+    "gqa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I64, _I, _I, _I, _I, _I64, _P,
+                              _I64, _P, _P, _I64, _D, _F, _I, _P, _SZ, _P]),
     "gqa_last_error": (ctypes.c_char_p, []),
     "gqa_version": (ctypes.c_char_p, []),
     "gqa_timing_enable": (_I, [_I]),

@@ -267,7 +267,8 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   if (g_timing.on) ev = g_timing.take();
   hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
                                     out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, kv_len, q_pos,
-                                    nullptr, nullptr, 0, 0, std::log2(theta), scale,
+                                    nullptr, nullptr, 0, 0, nullptr, 0, 0, 0, std::log2(theta),
+                                    scale,
                                     (float*)(wsb + ws.m_off),
                                     (float*)(wsb + ws.l_off), (float*)(wsb + ws.o_off),
                                     (hipStream_t)stream, ev.first, ev.second);
@@ -395,14 +396,16 @@ int decode_ragged_launch(const void* q, const void* k_cache, const void* v_cache
                          int in_dtype, int out_dtype, int64_t B, int h_q, int h_kv, int d,
                          int64_t cap, const int64_t* kvl, const int64_t* qpos, int from_pos,
                          int q_rotated, int64_t max_kv_len, double theta, float scale,
-                         void* workspace, hipStream_t st) {
+                         void* workspace, hipStream_t st, const int32_t* bt = nullptr,
+                         int ps_log2 = 0, int64_t max_pages = 0, int64_t num_pages = 0) {
   const DecodeWs ws = decode_ws(B, h_q, h_kv, d, cap);
   char* wsb = (char*)workspace;
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   if (g_timing.on) ev = g_timing.take();
   hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
                                     out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, max_kv_len, 0,
-                                    kvl, qpos, from_pos, q_rotated, std::log2(theta), scale,
+                                    kvl, qpos, from_pos, q_rotated, bt, ps_log2, max_pages,
+                                    num_pages, std::log2(theta), scale,
                                     (float*)(wsb + ws.m_off), (float*)(wsb + ws.l_off),
                                     (float*)(wsb + ws.o_off), st, ev.first, ev.second);
   if (ev.first) g_timing.rec[1].push_back(ev);
@@ -454,6 +457,59 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
   // 2) attend to rows 0 .. pos[b]
   return decode_ragged_launch(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap,
                               nullptr, pos, 1, 0, max_pos + 1, theta, scale, workspace, st);
+}
+
+size_t gqa_decode_paged_workspace_size(int64_t B, int h_q, int h_kv, int d,
+                                       int64_t max_kv_len) {
+  return gqa_decode_workspace_size(B, h_q, h_kv, d, max_kv_len);
+}
+
+int gqa_decode_paged(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                     void* v_pool, void* o, int in_dtype, int out_dtype, int64_t B, int h_q,
+                     int h_kv, int d, int page_size, int64_t num_pages,
+                     const int32_t* block_table, int64_t max_pages, const int64_t* kv_len,
+                     const int64_t* q_pos, int64_t max_kv_len, double theta, float scale,
+                     int q_rotated, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!q || !k_pool || !v_pool || !o || !block_table || !q_pos)
+    return fail(GQA_ERR_INVALID_ARG,
+                "q, k_pool, v_pool, o, block_table and q_pos must be non-NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(GQA_ERR_INVALID_ARG, "k_new and v_new must both be set or both be NULL");
+  const bool append = k_new != nullptr;
+  if (append == (kv_len != nullptr))
+    return fail(GQA_ERR_INVALID_ARG,
+                "give kv_len without k_new/v_new, or k_new/v_new (kv_len = q_pos + 1) alone");
+  if (page_size < 1 || page_size > (1 << 20) || (page_size & (page_size - 1)))
+    return fail(GQA_ERR_INVALID_ARG, "page_size=%d must be a power of two in [1, 2^20]",
+                page_size);
+  if (num_pages < 1 || num_pages > INT_MAX || max_pages < 1)
+    return fail(GQA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1 (num_pages < 2^31)");
+  if (max_kv_len > max_pages * page_size)
+    return fail(GQA_ERR_INVALID_ARG, "max_kv_len=%lld exceeds max_pages * page_size = %lld",
+                (long long)max_kv_len, (long long)(max_pages * page_size));
+  if (append && !(aligned16(k_new) && aligned16(v_new)))
+    return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  // the shared checks and the workspace layout see max_kv_len as the cache length
+  if (int rc = decode_ragged_check(q, k_pool, v_pool, o, in_dtype, out_dtype, B, h_q, h_kv, d,
+                                   max_kv_len, max_kv_len, theta, scale, workspace,
+                                   workspace_bytes))
+    return rc;
+  const int64_t reach = max_pages * page_size;
+  hipStream_t st = (hipStream_t)stream;
+  int ps_log2 = 0;
+  while ((1 << ps_log2) < page_size) ++ps_log2;
+  if (append) {   // the new token's rotated K and its V at position q_pos[b]
+    hipError_t e = gqa::launch_cache_append(k_new, v_new, k_pool, v_pool, in_dtype == GQA_BF16,
+                                            q_pos, nullptr, B, 1, h_kv, d, reach, max_kv_len,
+                                            std::log2(theta), st, block_table, ps_log2,
+                                            max_pages, num_pages);
+    if (e != hipSuccess) return hip_fail(e, "paged append launch");
+  }
+  return decode_ragged_launch(q, k_pool, v_pool, o, in_dtype, out_dtype, B, h_q, h_kv, d,
+                              max_kv_len, kv_len, q_pos, append ? 1 : 0, q_rotated != 0,
+                              max_kv_len, theta, scale, workspace, st, block_table, ps_log2,
+                              max_pages, num_pages);
 }
 
 int gqa_qkv_epilogue(const void* qkv, const void* bias, void* q_out, void* k_cache,

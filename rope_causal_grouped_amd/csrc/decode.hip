@@ -22,6 +22,13 @@
 // sequence whose length or position is out of range has no keys at all and
 // its output becomes NaN.  With q_rotated set the query arrives rotated
 // already (gqa_qkv_epilogue writes it so) and is used as given.
+//
+// Paged cache: with a block table, position j of sequence b lives in page
+// bt[b][j >> ps_log2], row j & (page_size - 1), of the pools
+// [num_pages, h_kv, page_size, d] (blocks of page_size positions per KV head,
+// as PagedAttention manages memory per KV head: "从 Qwen 1 到 Qwen 2 ..."
+// (nxmr.cn) §2).  A workgroup reads its chunk's page ids into LDS once; a
+// chunk whose ids fall outside the pool makes the sequence's output NaN.
 
 #include "common.h"
 #include "launch.h"
@@ -29,6 +36,13 @@
 namespace gqa {
 
 namespace {
+
+// K/V row addressing: contiguous [B, cap, h_kv, d] or paged pools
+struct KvRows {
+  const int32_t* bt;     // block table [B][max_pages], NULL: contiguous cache
+  int ps_log2;           // log2(page_size)
+  int64_t max_pages, num_pages, cap;
+};
 
 // per-sequence (kv_len, q_pos); kv_len = 0 marks an invalid sequence
 struct SeqLen {
@@ -44,6 +58,50 @@ __device__ __forceinline__ SeqLen seq_len(int b, int kv_len, double q_pos,
   const int64_t kl = kvl_from_pos ? qp + 1 : kvl_arr[b];
   const bool ok = kl >= 1 && kl <= kv_len && qp >= kl - 1 && qp <= (INT64_C(1) << 40);
   return {ok ? (int)kl : 0, (double)qp};
+}
+
+// Page ids of positions [k0, k1) of sequence b into pg[]; false if any id or
+// table slot is out of range.  Every thread of the workgroup calls it.
+__device__ bool stage_pages(const KvRows& kr, int b, int k0, int k1, int* pg) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  const int64_t first = (int64_t)k0 >> kr.ps_log2;
+  const int n = (int)((((int64_t)k1 - 1) >> kr.ps_log2) - first + 1);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t slot = first + i;
+    int pid = -1;
+    if (slot < kr.max_pages) pid = kr.bt[(int64_t)b * kr.max_pages + slot];
+    if (pid < 0 || pid >= kr.num_pages) {
+      bad = 1;
+      pid = 0;
+    }
+    pg[i] = pid;
+  }
+  __syncthreads();
+  return bad == 0;
+}
+
+// element offset of (sequence b, position key, group u) in the K or V store
+__device__ __forceinline__ int64_t kv_row(const KvRows& kr, const int* pg, int k0, int b, int key,
+                                          int u, int h_kv, int D) {
+  if (!kr.bt) return (((int64_t)b * kr.cap + key) * h_kv + u) * D;
+  const int page = pg[(key >> kr.ps_log2) - (k0 >> kr.ps_log2)];
+  const int row = key & ((1 << kr.ps_log2) - 1);
+  return (((int64_t)page * h_kv + u) * ((int64_t)1 << kr.ps_log2) + row) * D;
+}
+
+// partial state of an invalid chunk: the merge turns it into NaN output
+__device__ void write_nan_state(float* pm, float* pl, float* po, int64_t out0, int nh, int D) {
+  for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
+    const int cc = idx / D, dim = idx % D;
+    if (cc >= nh) continue;
+    po[(out0 + cc) * D + dim] = 0.f;
+    if (dim == 0) {
+      pm[out0 + cc] = __builtin_nanf("");
+      pl[out0 + cc] = 0.f;
+    }
+  }
 }
 
 }  // namespace
@@ -66,7 +124,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
     float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int64_t cap, int kv_len_max,
     double q_pos_s, double log2_theta, float sl2, int n_split, const int64_t* __restrict__ kvl_arr,
-    const int64_t* __restrict__ qpos_arr, int kvl_from_pos, int q_rotated) {
+    const int64_t* __restrict__ qpos_arr, int kvl_from_pos, int q_rotated, KvRows kr) {
   constexpr int CH = kDecodeChunk;
   constexpr int WK = CH / 4;            // keys per wave
   constexpr int NS = D / 32;            // 32-dim k-steps of S^T
@@ -76,6 +134,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t vsh[4][32 * VPITCH];
   __shared__ float cm[4][16], cl[4][16];
   __shared__ float co[4][16][D + 1];
+  __shared__ int pg[CH];                // page ids of this chunk (paged cache)
 
   const int split = blockIdx.x;
   const int u = blockIdx.y / n_hb, hb = blockIdx.y % n_hb;
@@ -97,6 +156,12 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
         pl[out] = 0.f;
       }
     }
+    return;
+  }
+  const int chunk0 = split * CH;
+  if (kr.bt && !stage_pages(kr, b, chunk0, min(chunk0 + CH, kv_len), pg)) {
+    write_nan_state(pm, pl, po, (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16,
+                    min(16, g - hb * 16), D);
     return;
   }
 
@@ -127,9 +192,6 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     }
   }
 
-  const int64_t RS = (int64_t)h_kv * D;  // elements between consecutive keys
-  const uint16_t* kbase = kc + ((int64_t)b * cap * h_kv + u) * D;
-  const uint16_t* vbase = vc + ((int64_t)b * cap * h_kv + u) * D;
   const int kw0 = split * CH + wave * WK;
   const int kw1 = min(kw0 + WK, kv_len);
 
@@ -147,13 +209,15 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
       const int key = min(k0 + blk * 16 + col, kv_len - 1);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        ka[blk][s] = __builtin_nontemporal_load((const u32x4*)(kbase + key * RS + s * 32 + h4 * 8));
+        ka[blk][s] = __builtin_nontemporal_load(
+            (const u32x4*)(kc + kv_row(kr, pg, chunk0, b, key, u, h_kv, D) + s * 32 + h4 * 8));
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int ch = lane + 64 * i;
       const int key = min(k0 + ch / (D / 8), kv_len - 1);
-      va[i] = __builtin_nontemporal_load((const u32x4*)(vbase + key * RS + (ch % (D / 8)) * 8));
+      va[i] = __builtin_nontemporal_load(
+          (const u32x4*)(vc + kv_row(kr, pg, chunk0, b, key, u, h_kv, D) + (ch % (D / 8)) * 8));
     }
     // S^T for 2 x 16 keys
     f32x4 sacc[2];
@@ -257,11 +321,12 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po, int h_q, int h_kv,
     int g, int n_hb, int64_t cap, int kv_len_max, double q_pos_s, double log2_theta, float scale,
     int n_split, const int64_t* __restrict__ kvl_arr, const int64_t* __restrict__ qpos_arr,
-    int kvl_from_pos, int q_rotated) {
+    int kvl_from_pos, int q_rotated, KvRows kr) {
   constexpr int CH = kDecodeChunk;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float qs[16][D];
   __shared__ float sc[16][CH];
+  __shared__ int pg[CH];                // page ids of this chunk (paged cache)
   const int split = blockIdx.x;
   const int u = blockIdx.y / n_hb, hb = blockIdx.y % n_hb;
   const int b = blockIdx.z;
@@ -283,6 +348,10 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     }
     return;
   }
+  if (kr.bt && !stage_pages(kr, b, split * CH, min(split * CH + CH, kv_len), pg)) {
+    write_nan_state(pm, pl, po, (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16, nh, D);
+    return;
+  }
 
   for (int idx = tid; idx < 16 * (D / 2); idx += 256) {
     const int cc = idx / (D / 2), j = idx % (D / 2);
@@ -301,11 +370,8 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
 
   const int k0 = split * CH;
   const int nk = min(CH, kv_len - k0);
-  const int64_t RS = (int64_t)h_kv * D;
-  const float* kbase = kc + ((int64_t)b * cap * h_kv + u) * D;
-  const float* vbase = vc + ((int64_t)b * cap * h_kv + u) * D;
   for (int kk = tid; kk < nk; kk += 256) {
-    const float* krow = kbase + (int64_t)(k0 + kk) * RS;
+    const float* krow = kc + kv_row(kr, pg, k0, b, k0 + kk, u, h_kv, D);
     for (int cc = 0; cc < nh; ++cc) {
       float dot = 0.f;
       for (int dd = 0; dd < D; ++dd) dot = fmaf(qs[cc][dd], krow[dd], dot);
@@ -336,7 +402,7 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
     for (int kk = 0; kk < nk; ++kk) {
       const float p = sc[cc][kk];
-      const float* vrow = vbase + (int64_t)(k0 + kk) * RS + sub * DPT;
+      const float* vrow = vc + kv_row(kr, pg, k0, b, k0 + kk, u, h_kv, D) + sub * DPT;
 #pragma unroll
       for (int e = 0; e < DPT; ++e) acc[e] = fmaf(p, vrow[e], acc[e]);
     }
@@ -401,6 +467,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
                          int out_bf16, int64_t B, int h_q, int h_kv, int d, int64_t cap,
                          int64_t kv_len, int64_t q_pos, const int64_t* kvl_arr,
                          const int64_t* qpos_arr, int kvl_from_pos, int q_rotated,
+                         const int32_t* bt, int ps_log2, int64_t max_pages, int64_t num_pages,
                          double log2_theta,
                          float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end) {
@@ -409,29 +476,30 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
   const int n_split = decode_num_splits(kv_len);
   dim3 grid((unsigned)n_split, (unsigned)(h_kv * n_hb), (unsigned)B);
   const float sl2 = scale * 1.4426950408889634f;
+  const KvRows kr{bt, ps_log2, max_pages, num_pages, cap};
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
   if (in_bf16) {
     if (d == 128)
       decode_split_bf16_kernel<128><<<grid, 256, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
           h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split, kvl_arr,
-          qpos_arr, kvl_from_pos, q_rotated);
+          qpos_arr, kvl_from_pos, q_rotated, kr);
     else
       decode_split_bf16_kernel<64><<<grid, 256, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
           h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split, kvl_arr,
-          qpos_arr, kvl_from_pos, q_rotated);
+          qpos_arr, kvl_from_pos, q_rotated, kr);
   } else {
     if (d == 128)
       decode_split_f32_kernel<128><<<grid, 256, 0, st>>>(
           (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
           n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split, kvl_arr, qpos_arr,
-          kvl_from_pos, q_rotated);
+          kvl_from_pos, q_rotated, kr);
     else
       decode_split_f32_kernel<64><<<grid, 256, 0, st>>>(
           (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
           n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split, kvl_arr, qpos_arr,
-          kvl_from_pos, q_rotated);
+          kvl_from_pos, q_rotated, kr);
   }
   hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, st);

@@ -29,10 +29,13 @@ hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* c
                                  float* kc, float* vc, int64_t B, int64_t L, int h_kv, int d,
                                  int64_t cap, hipStream_t st);
 
+// bt != NULL: kc/vc are page pools [num_pages, h_kv, 2^ps_log2, d] addressed
+// through the block table bt [B][max_pages]
 hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc, int bf16,
                                const int64_t* start, const int64_t* len, int64_t B, int64_t C,
                                int h_kv, int d, int64_t cap, int64_t end, double log2_theta,
-                               hipStream_t st);
+                               hipStream_t st, const int32_t* bt = nullptr, int ps_log2 = 0,
+                               int64_t max_pages = 0, int64_t num_pages = 0);
 
 hipError_t launch_qkv_epilogue(const void* x, const void* bias, void* q_out, void* kc, void* vc,
                                int bf16, const int64_t* start, const int64_t* len, int64_t B,
@@ -63,6 +66,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
                          int out_bf16, int64_t B, int h_q, int h_kv, int d, int64_t cap,
                          int64_t kv_len, int64_t q_pos, const int64_t* kvl_arr,
                          const int64_t* qpos_arr, int kvl_from_pos, int q_rotated,
+                         const int32_t* bt, int ps_log2, int64_t max_pages, int64_t num_pages,
                          double log2_theta,
                          float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end);

@@ -276,13 +276,18 @@ hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const fl
 // k/v[B, C, h_kv, d]; row i < len[b] (len NULL: C) of sequence b sits at
 // position p = start[b] + i: kc[b][p][u] = RoPE(k[b][i][u], p) and
 // vc[b][p][u] = v[b][i][u].  A sequence whose rows would not lie within
-// [0, end) (end <= cap, checked by the caller) is skipped.  One thread per
-// (row, head, pair j): it rotates dims j, j + d/2 and copies them of V.
+// [0, end) (end <= cap, checked by the caller) is skipped.  With a block
+// table bt [B][max_pages] the cache is a pair of page pools
+// [num_pages, h_kv, 2^ps_log2, d] and position p goes to page
+// bt[b][p >> ps_log2], row p & (page_size - 1); a row whose page id is out
+// of range is skipped.  One thread per (row, head, pair j): it rotates dims
+// j, j + d/2 and copies them of V.
 template <typename T>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ kc, T* __restrict__ vc,
     const int64_t* __restrict__ start, const int64_t* __restrict__ len, int64_t n_pairs,
-    int64_t C, int h_kv, int d, int64_t cap, int64_t end, double log2_theta) {
+    int64_t C, int h_kv, int d, int64_t cap, int64_t end, double log2_theta,
+    const int32_t* __restrict__ bt, int ps_log2, int64_t max_pages, int64_t num_pages) {
   const int half = d >> 1;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_pairs;
        idx += (int64_t)gridDim.x * blockDim.x) {
@@ -294,12 +299,19 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     const int64_t s0 = start[b], n = len ? len[b] : C;
     if (!(s0 >= 0 && n >= 0 && n <= C && s0 + n <= end) || i >= n) continue;
     const int64_t p = s0 + i;
+    int64_t dst = ((b * cap + p) * h_kv + u) * d;
+    if (bt) {
+      const int64_t slot = p >> ps_log2;
+      const int pid = slot < max_pages ? bt[b * max_pages + slot] : -1;
+      if (pid < 0 || pid >= num_pages) continue;
+      dst = (((int64_t)pid * h_kv + u) * ((int64_t)1 << ps_log2) + (p & ((1 << ps_log2) - 1))) * d;
+    }
     float c, s;
     rope_cos_sin((double)p, rope_omega(j, d, log2_theta), c, s);
     const T* kr = k + row * d;
     const T* vr = v + row * d;
-    T* kd = kc + ((b * cap + p) * h_kv + u) * d;
-    T* vd = vc + ((b * cap + p) * h_kv + u) * d;
+    T* kd = kc + dst;
+    T* vd = vc + dst;
     if constexpr (sizeof(T) == 2) {
       const float x1 = bf16_bits_to_f32(kr[j]), x2 = bf16_bits_to_f32(kr[j + half]);
       kd[j] = f32_to_bf16_bits(fmaf(x1, c, -x2 * s));
@@ -317,18 +329,20 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc, int bf16,
                                const int64_t* start, const int64_t* len, int64_t B, int64_t C,
                                int h_kv, int d, int64_t cap, int64_t end, double log2_theta,
-                               hipStream_t st) {
+                               hipStream_t st, const int32_t* bt, int ps_log2, int64_t max_pages,
+                               int64_t num_pages) {
   const int64_t n_pairs = B * C * h_kv * (d / 2);
   const int64_t want = (n_pairs + 255) / 256;
   const int grid = (int)(want < 65536 ? want : 65536);
   if (bf16)
     cache_append_kernel<uint16_t><<<grid, 256, 0, st>>>(
         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kc, (uint16_t*)vc, start, len, n_pairs,
-        C, h_kv, d, cap, end, log2_theta);
+        C, h_kv, d, cap, end, log2_theta, bt, ps_log2, max_pages, num_pages);
   else
     cache_append_kernel<float><<<grid, 256, 0, st>>>((const float*)k, (const float*)v, (float*)kc,
                                                      (float*)vc, start, len, n_pairs, C, h_kv, d,
-                                                     cap, end, log2_theta);
+                                                     cap, end, log2_theta, bt, ps_log2, max_pages,
+                                                     num_pages);
   return hipGetLastError();
 }
 

@@ -221,3 +221,32 @@ def epilogue_call(lib, **kw):
 def test_qkv_epilogue_rejects(lib, kw, code):
     assert epilogue_call(lib, **kw) == code
     assert lib.gqa_last_error()
+
+
+def paged_call(lib, **kw):
+    a = dict(q=FAKE, kn=None, vn=None, kp=FAKE, vp=FAKE, o=FAKE, in_dt=1, out_dt=0, B=2, h_q=28,
+             h_kv=4, d=128, ps=16, num_pages=64, bt=FAKE, max_pages=8, kvl=FAKE, qpos=FAKE,
+             max_kv=128, theta=1e6, scale=0.088, qrot=0, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gqa_decode_paged(a["q"], a["kn"], a["vn"], a["kp"], a["vp"], a["o"], a["in_dt"],
+                                a["out_dt"], a["B"], a["h_q"], a["h_kv"], a["d"], a["ps"],
+                                a["num_pages"], a["bt"], a["max_pages"], a["kvl"], a["qpos"],
+                                a["max_kv"], a["theta"], a["scale"], a["qrot"], a["ws"], a["wsb"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), _lib.GQA_ERR_INVALID_ARG),
+    (dict(ps=24), _lib.GQA_ERR_INVALID_ARG),               # not a power of two
+    (dict(ps=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(max_kv=129), _lib.GQA_ERR_INVALID_ARG),          # beyond max_pages * page_size
+    (dict(kn=FAKE), _lib.GQA_ERR_INVALID_ARG),             # v_new missing
+    (dict(kn=FAKE, vn=FAKE), _lib.GQA_ERR_INVALID_ARG),    # append mode takes no kv_len
+    (dict(kvl=None), _lib.GQA_ERR_INVALID_ARG),            # neither kv_len nor append
+    (dict(num_pages=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(h_q=30), _lib.GQA_ERR_INVALID_ARG),
+    (dict(wsb=4), _lib.GQA_ERR_WORKSPACE),
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert paged_call(lib, **kw) == code
+    assert lib.gqa_last_error()

@@ -283,3 +283,88 @@ def test_epilogue_then_attention(dtype):
                   "epilogue + chunk")
     assert_parity(host(od), oracle.decode_ragged(q_all[:, L], kc, vc, L + 1, L, q_rotated=True),
                   dtype, "epilogue + decode")
+
+
+# --------------------------------------------------------- paged cache ---
+
+def to_pages(kc, page_size, num_pages, seed, poison=4096.0):
+    """Scatter a contiguous cache [B, cap, h_kv, d] into a page pool under a
+    shuffled block table; unused pages hold `poison` (exact in bf16)."""
+    B, cap, h_kv, d = kc.shape
+    per_seq = -(-cap // page_size)
+    perm = np.random.default_rng(seed).permutation(num_pages)[:B * per_seq].reshape(B, per_seq)
+    pool = np.full((num_pages, h_kv, page_size, d), poison)
+    for b in range(B):
+        for n in range(per_seq):
+            rows = kc[b, n * page_size:(n + 1) * page_size]
+            pool[perm[b, n], :, :rows.shape[0]] = np.transpose(rows, (1, 0, 2))
+    return pool, perm.astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype,page_size", [(torch.bfloat16, 16), (torch.bfloat16, 256),
+                                             (torch.float32, 64)],
+                         ids=["bf16_ps16", "bf16_ps256", "f32_ps64"])
+def test_decode_paged(dtype, page_size):
+    h_q, h_kv, d = (28, 4, 128) if dtype == torch.bfloat16 else (14, 2, 64)
+    kv_len = np.array([1, 1024, 1025, 3000])
+    q_pos = np.array([0, 1500, 1024, 2999])
+    B, cap = len(kv_len), 3072
+    num_pages = B * (cap // page_size) + 7
+    note(f"decode_paged {dtype} page_size={page_size}")
+    q, k, v = inputs(B, cap, h_q, h_kv, d, dtype, 42)
+    kc, vc = prefilled_cache(k, v, np.full(B, cap), cap, dtype)
+    kp, bt = to_pages(kc, page_size, num_pages, 1)
+    vp, _ = to_pages(vc, page_size, num_pages, 1)
+    kpd, vpd, btd = dev(kp, dtype), dev(vp, dtype), torch.from_numpy(bt).cuda()
+    o = gqa.decode_paged(dev(q[:, 0], dtype), kpd, vpd, btd, torch.tensor(q_pos),
+                         torch.tensor(kv_len))
+    oc = gqa.decode_ragged(dev(q[:, 0], dtype), dev(kc, dtype), dev(vc, dtype),
+                           torch.tensor(kv_len), torch.tensor(q_pos))
+    torch.cuda.synchronize()
+    assert_parity(host(o), oracle.decode_paged(q[:, 0], kp, vp, bt, page_size, kv_len, q_pos),
+                  dtype, "decode_paged")
+    assert torch.equal(o, oc), "paged and contiguous decode differ"
+
+
+def test_decode_paged_append():
+    dtype, page_size = torch.bfloat16, 32
+    h_q, h_kv, d = 28, 4, 128
+    pos = np.array([0, 31, 32, 2000])
+    B, cap = len(pos), 2048
+    num_pages = B * (cap // page_size) + 3
+    note("decode_paged append")
+    q, k, v = inputs(B, cap, h_q, h_kv, d, dtype, 43)
+    kc, vc = prefilled_cache(k, v, pos, cap, dtype)
+    kp, bt = to_pages(kc, page_size, num_pages, 2)
+    vp, _ = to_pages(vc, page_size, num_pages, 2)
+    qn = np.stack([q[b, pos[b]] for b in range(B)])
+    kn = np.stack([k[b, pos[b]] for b in range(B)])
+    vn = np.stack([v[b, pos[b]] for b in range(B)])
+    kpd, vpd = dev(kp, dtype), dev(vp, dtype)
+    o = gqa.decode_paged(dev(qn, dtype), kpd, vpd, torch.from_numpy(bt).cuda(), torch.tensor(pos),
+                         k_new=dev(kn, dtype), v_new=dev(vn, dtype), max_kv_len=cap)
+    torch.cuda.synchronize()
+    kp_want, vp_want = oracle.paged_append(kp, vp, kn, vn, bt, page_size, pos)
+    want = oracle.decode_paged(qn, kp_want, vp_want, bt, page_size, pos + 1, pos)
+    assert_parity(host(o), want, dtype, "decode_paged append")
+    kg = host(kpd)
+    for b in range(B):
+        page, row = bt[b, pos[b] // page_size], pos[b] % page_size
+        assert_rotated_rows(kg[page, :, row], kp_want[page, :, row], dtype, f"appended K {b}")
+        kg[page, :, row] = kp[page, :, row]
+    assert np.array_equal(kg, kp), "pool rows other than the new tokens changed"
+
+
+def test_decode_paged_bad_page_is_nan():
+    dtype, page_size = torch.bfloat16, 64
+    B, cap, h_q, h_kv, d = 2, 512, 28, 4, 128
+    q, k, v = inputs(B, cap, h_q, h_kv, d, dtype, 44)
+    kc, vc = prefilled_cache(k, v, np.full(B, cap), cap, dtype)
+    kp, bt = to_pages(kc, page_size, 20, 3)
+    vp, _ = to_pages(vc, page_size, 20, 3)
+    bt[1, 5] = 99    # beyond the pool
+    o = gqa.decode_paged(dev(q[:, 0], dtype), dev(kp, dtype), dev(vp, dtype),
+                         torch.from_numpy(bt).cuda(), [511, 511], [512, 512])
+    torch.cuda.synchronize()
+    o = host(o)
+    assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1]))
