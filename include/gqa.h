@@ -234,6 +234,28 @@ int gqa_decode_paged(const void* q, const void* k_new, const void* v_new,
                      int64_t max_kv_len, double theta, float scale, int q_rotated,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * YaRN context extension of RoPE for every later call on this thread
+ * (like gqa_last_error, the setting is per thread).  Beyond its 32K training
+ * window Qwen2 enables YaRN at inference to reach 128K: each pair's
+ * frequency is scaled as theta_i' = theta_i / s * alpha_i with a ramp
+ * alpha_i over the dimensions ("Qwen-2 详解" (yudonglee.me) §6.2), and the
+ * attention logits are rescaled for length extrapolation (walkthrough §5.3).
+ * The ramp is the YaRN paper's (Peng et al., 2023): with
+ *   D(n) = d ln(original_max_position / (2 pi n)) / (2 ln theta),
+ * pair j keeps its frequency for j <= floor(D(beta_fast)), is divided by
+ * `factor` for j >= ceil(D(beta_slow)), and is blended linearly in j between
+ * (bounds clamped to [0, d-1]); cos and sin are multiplied by
+ * 0.1 ln(factor) + 1, so Q'K'^T grows by its square.  factor = 1 restores
+ * plain RoPE (the default).  Qwen2's long-context setting is factor 4,
+ * original_max_position 32768, beta_fast 32, beta_slow 1.
+ * Requires factor >= 1 and, when factor > 1, original_max_position >= 1 and
+ * beta_fast > beta_slow > 0.  Cached keys must have been written under the
+ * same setting.
+ */
+int gqa_set_rope_yarn(double factor, double original_max_position,
+                      double beta_fast, double beta_slow);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* gqa_last_error(void);
 

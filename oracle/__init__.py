@@ -1,7 +1,8 @@
 """fp64 CPU oracle for causal GQA with RoPE.  TEST INFRASTRUCTURE: only the
 tests, the smoke check and the benchmark's CPU-baseline leg may use it."""
 
-from .gqa_oracle import (ROPE_THETA, inv_freq, rope, group_size, kv_group,
+from .gqa_oracle import (ROPE_THETA, YaRN, base_theta, yarn_ramp, rope_mscale,
+                         inv_freq, rope, group_size, kv_group,
                          visible, softmax_rows, head_weights, attend, prefill,
                          prefill_rows, decode, prefill_brute,
                          per_sequence, chunk_positions, cache_append,
@@ -9,7 +10,8 @@ from .gqa_oracle import (ROPE_THETA, inv_freq, rope, group_size, kv_group,
                          decode_append, qkv_sections, qkv_epilogue,
                          paged_rows, decode_paged, paged_append)
 
-__all__ = ["ROPE_THETA", "inv_freq", "rope", "group_size", "kv_group",
+__all__ = ["ROPE_THETA", "YaRN", "base_theta", "yarn_ramp", "rope_mscale", "inv_freq",
+           "rope", "group_size", "kv_group",
            "visible", "softmax_rows", "head_weights", "attend", "prefill",
            "prefill_rows", "decode", "prefill_brute", "per_sequence",
            "chunk_positions", "cache_append", "attend_cached", "prefill_chunk",

@@ -35,6 +35,7 @@ example, brute-force loops, and the invariants the pages state.
 from __future__ import annotations
 
 import math
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -43,16 +44,69 @@ ROPE_THETA = 1.0e6   # Qwen2's RoPE base: [evo] §2.3/§3.2, [csdn] §5.2, [kn] 
 
 # ---------------------------------------------------------------- RoPE ----
 
-def inv_freq(d: int, theta: float = ROPE_THETA) -> np.ndarray:
+@dataclass(frozen=True)
+class YaRN:
+    """RoPE with YaRN context extension, usable wherever a base theta is.
+
+    The pages: beyond the 32K training window Qwen2 enables YaRN at inference
+    to reach 128K ([yd] §6.2), which scales each pair's frequency as
+    theta'_i = theta_i / s * alpha_i with a per-dimension ramp alpha_i, and
+    rescales the attention logits for length extrapolation ([csdn] §5.3).
+    The ramp is the one of the YaRN paper (Peng et al., 2023): pairs that
+    turn at least beta_fast times over the original context keep their
+    frequency, pairs below beta_slow turns are divided by the factor s, and
+    the blend is linear in the pair index between the two correction
+    dimensions; cos and sin carry the factor 0.1 ln s + 1."""
+    theta: float = ROPE_THETA
+    factor: float = 4.0
+    original_max_position: float = 32768.0
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+
+
+def base_theta(theta) -> float:
+    return theta.theta if isinstance(theta, YaRN) else float(theta)
+
+
+def yarn_ramp(spec: YaRN, d: int) -> np.ndarray:
+    """Blend weight per pair (0: frequency kept, 1: divided by the factor).
+    Pair index of a frequency that turns n times over the original context:
+    D(n) = d ln(L_orig / (2 pi n)) / (2 ln theta); the ramp rises linearly
+    from floor(D(beta_fast)) to ceil(D(beta_slow)) (bounds clamped to
+    [0, d-1])."""
+    def corr_dim(n):
+        return d * math.log(spec.original_max_position / (n * 2.0 * math.pi)) / (
+            2.0 * math.log(spec.theta))
+    lo = max(math.floor(corr_dim(spec.beta_fast)), 0)
+    hi = min(math.ceil(corr_dim(spec.beta_slow)), d - 1)
+    if hi == lo:
+        hi += 0.001
+    j = np.arange(d // 2, dtype=np.float64)
+    return np.clip((j - lo) / (hi - lo), 0.0, 1.0)
+
+
+def rope_mscale(theta) -> float:
+    """Factor on cos and sin: 0.1 ln s + 1 under YaRN with s > 1, else 1."""
+    if isinstance(theta, YaRN) and theta.factor > 1.0:
+        return 0.1 * math.log(theta.factor) + 1.0
+    return 1.0
+
+
+def inv_freq(d: int, theta=ROPE_THETA) -> np.ndarray:
     """omega_j = theta^(-2j/d), j = 0 .. d/2-1 ([ip] §2.3 angle m*base^(-2i/d);
-    [csdn] §5.2: the base generates the inverse frequencies)."""
+    [csdn] §5.2: the base generates the inverse frequencies); under YaRN
+    blended towards omega_j / s by yarn_ramp."""
     if d % 2:
         raise ValueError("RoPE needs an even head size")
     j = np.arange(d // 2, dtype=np.float64)
-    return np.power(np.float64(theta), -2.0 * j / d)
+    w = np.power(np.float64(base_theta(theta)), -2.0 * j / d)
+    if isinstance(theta, YaRN) and theta.factor != 1.0:
+        r = yarn_ramp(theta, d)
+        w = w * (1.0 - r) + (w / theta.factor) * r
+    return w
 
 
-def rope(x: np.ndarray, positions, theta: float = ROPE_THETA) -> np.ndarray:
+def rope(x: np.ndarray, positions, theta=ROPE_THETA) -> np.ndarray:
     """Rotate every row of x[..., L, h, d] at its position ([csdn] §3.5.2 and
     §4.1.3 step 3: rotate Q and K per position and per dimension pair; the
     shape is unchanged).  ``positions`` has shape [L] (or broadcasts to
@@ -62,8 +116,9 @@ def rope(x: np.ndarray, positions, theta: float = ROPE_THETA) -> np.ndarray:
     half = d // 2
     pos = np.asarray(positions, dtype=np.float64)
     ang = pos[..., None] * inv_freq(d, theta)          # [..., L, d/2]
-    c = np.cos(ang)[..., None, :]                      # broadcast over heads
-    s = np.sin(ang)[..., None, :]
+    ms = rope_mscale(theta)
+    c = ms * np.cos(ang)[..., None, :]                 # broadcast over heads
+    s = ms * np.sin(ang)[..., None, :]
     x1 = x[..., :half]
     x2 = x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)

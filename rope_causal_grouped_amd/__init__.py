@@ -17,7 +17,8 @@ import torch
 from ._lib import (GQA_BF16, GQA_F32, GQAError, check, lib)
 
 __all__ = ["rope_apply", "prefill", "decode", "prefill_chunk", "decode_ragged",
-           "decode_append", "qkv_epilogue", "decode_paged", "decode_paged_workspace_size", "prefill_workspace_size", "prefill_chunk_workspace_size",
+           "decode_append", "qkv_epilogue", "decode_paged", "decode_paged_workspace_size",
+           "set_rope_yarn", "prefill_workspace_size", "prefill_chunk_workspace_size",
            "decode_workspace_size", "timing_enable", "timing_read", "version",
            "GQAError", "ROPE_THETA"]
 
@@ -315,6 +316,13 @@ def decode_paged(q, k_pool, v_pool, block_table, q_pos, kv_len=None, *, k_new=No
                                  max_kv_len, theta, scale, int(q_rotated), _ptr(workspace),
                                  workspace.numel(), _stream()))
     return out
+
+
+def set_rope_yarn(factor: float = 1.0, original_max_position: float = 32768.0,
+                  beta_fast: float = 32.0, beta_slow: float = 1.0) -> None:
+    """YaRN-scaled RoPE for every later call on this thread (factor 1: plain
+    RoPE).  Qwen2's long-context setting: factor 4 over 32768 positions."""
+    check(lib().gqa_set_rope_yarn(factor, original_max_position, beta_fast, beta_slow))
 
 
 def timing_enable(on: bool) -> None:

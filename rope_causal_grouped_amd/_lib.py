@@ -41,6 +41,7 @@ SIGNATURES = {
     "gqa_decode_paged_workspace_size": (_SZ, [_I64, _I, _I, _I, _I64]),
     "gqa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I64, _I, _I, _I, _I, _I64, _P,
                               _I64, _P, _P, _I64, _D, _F, _I, _P, _SZ, _P]),
+    "gqa_set_rope_yarn": (_I, [_D, _D, _D, _D]),
     "gqa_last_error": (ctypes.c_char_p, []),
     "gqa_version": (ctypes.c_char_p, []),
     "gqa_timing_enable": (_I, [_I]),

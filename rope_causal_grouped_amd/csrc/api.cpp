@@ -58,10 +58,37 @@ struct Timing {
 };
 Timing g_timing;
 
-struct Shape {
-  int64_t B, L;
-  int h_q, h_kv, d;
+// YaRN context extension of RoPE (gqa_set_rope_yarn), per thread like the
+// error message; factor 1 is plain RoPE.
+struct YarnConfig {
+  double factor = 1.0, original_max_position = 0.0, beta_fast = 32.0, beta_slow = 1.0;
 };
+thread_local YarnConfig g_yarn;
+
+// The call's RoPE parameters: base theta, and the YaRN blend of this thread.
+// Pair j keeps its frequency below the correction dimension of beta_fast
+// rotations over the original context and is divided by the factor above
+// that of beta_slow rotations, linearly in j between; cos and sin carry the
+// attention factor 0.1 ln(factor) + 1.
+gqa::RopeParams rope_params(double theta, int d) {
+  gqa::RopeParams rp{std::log2(theta), 1.0, 0.0, 1.0, 1.0f};
+  const YarnConfig& y = g_yarn;
+  if (y.factor == 1.0) return rp;
+  const double two_ln_theta = 2.0 * std::log(theta);
+  auto corr_dim = [&](double rotations) {
+    return d * std::log(y.original_max_position / (rotations * 2.0 * M_PI)) / two_ln_theta;
+  };
+  double lo = std::floor(corr_dim(y.beta_fast));
+  double hi = std::ceil(corr_dim(y.beta_slow));
+  if (lo < 0.0) lo = 0.0;
+  if (hi > d - 1) hi = d - 1;
+  if (hi == lo) hi += 0.001;
+  rp.inv_factor = 1.0 / y.factor;
+  rp.ramp_lo = lo;
+  rp.ramp_hi = hi;
+  rp.mscale = (float)(0.1 * std::log(y.factor) + 1.0);
+  return rp;
+}
 
 int check_heads(int h_q, int h_kv) {
   if (h_q < 1 || h_kv < 1)
@@ -147,7 +174,7 @@ int gqa_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64
   if (pos0 < 0 || pos0 > (INT64_C(1) << 40)) return fail(GQA_ERR_INVALID_ARG, "pos0 out of range");
   if (int rc = check_theta_scale(theta, 1.0f)) return rc;
   if (!aligned16(x)) return fail(GQA_ERR_INVALID_ARG, "x must be 16-byte aligned");
-  hipError_t e = gqa::launch_rope_apply(x, dtype, B, L, h, d, pos0, std::log2(theta),
+  hipError_t e = gqa::launch_rope_apply(x, dtype, B, L, h, d, pos0, rope_params(theta, d),
                                         (hipStream_t)stream);
   return e == hipSuccess ? GQA_OK : hip_fail(e, "rope_apply launch");
 }
@@ -188,8 +215,8 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)workspace;
   float2* cs = (float2*)(wsb + ws.cs_off);
-  const double l2t = std::log2(theta);
-  hipError_t e = gqa::launch_rope_table(cs, L, d, 0, l2t, st);
+  const gqa::RopeParams rp = rope_params(theta, d);
+  hipError_t e = gqa::launch_rope_table(cs, L, d, 0, rp, st);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
 
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
@@ -267,8 +294,8 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   if (g_timing.on) ev = g_timing.take();
   hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
                                     out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, kv_len, q_pos,
-                                    nullptr, nullptr, 0, 0, nullptr, 0, 0, 0, std::log2(theta),
-                                    scale,
+                                    nullptr, nullptr, 0, 0, nullptr, 0, 0, 0,
+                                    rope_params(theta, d), scale,
                                     (float*)(wsb + ws.m_off),
                                     (float*)(wsb + ws.l_off), (float*)(wsb + ws.o_off),
                                     (hipStream_t)stream, ev.first, ev.second);
@@ -318,14 +345,14 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
   char* wsb = (char*)workspace;
   const PrefillWs ws = prefill_ws(in_dtype, B, kend, h_kv, d);
   float2* cs = (float2*)(wsb + ws.cs_off);
-  const double l2t = std::log2(theta);
-  hipError_t e = gqa::launch_rope_table(cs, kend, d, 0, l2t, st);
+  const gqa::RopeParams rp = rope_params(theta, d);
+  hipError_t e = gqa::launch_rope_table(cs, kend, d, 0, rp, st);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   // 1) the chunk's rotated K and its V into the cache rows start[b] + i
   //    (k, v NULL: an earlier call, e.g. gqa_qkv_epilogue, put them there)
   if (k) {
     e = gqa::launch_cache_append(k, v, k_cache, v_cache, in_dtype == GQA_BF16, start, len, B, C,
-                                 h_kv, d, cap, kend, l2t, st);
+                                 h_kv, d, cap, kend, rp, st);
     if (e != hipSuccess) return hip_fail(e, "cache append launch");
   }
 
@@ -405,7 +432,7 @@ int decode_ragged_launch(const void* q, const void* k_cache, const void* v_cache
   hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
                                     out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, max_kv_len, 0,
                                     kvl, qpos, from_pos, q_rotated, bt, ps_log2, max_pages,
-                                    num_pages, std::log2(theta), scale,
+                                    num_pages, rope_params(theta, d), scale,
                                     (float*)(wsb + ws.m_off), (float*)(wsb + ws.l_off),
                                     (float*)(wsb + ws.o_off), st, ev.first, ev.second);
   if (ev.first) g_timing.rec[1].push_back(ev);
@@ -452,7 +479,7 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
   // 1) the new token's rotated K and its V into cache row pos[b]
   hipError_t e = gqa::launch_cache_append(k_new, v_new, k_cache, v_cache, in_dtype == GQA_BF16,
                                           pos, nullptr, B, 1, h_kv, d, cap, max_pos + 1,
-                                          std::log2(theta), st);
+                                          rope_params(theta, d), st);
   if (e != hipSuccess) return hip_fail(e, "cache append launch");
   // 2) attend to rows 0 .. pos[b]
   return decode_ragged_launch(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap,
@@ -502,7 +529,7 @@ int gqa_decode_paged(const void* q, const void* k_new, const void* v_new, void* 
   if (append) {   // the new token's rotated K and its V at position q_pos[b]
     hipError_t e = gqa::launch_cache_append(k_new, v_new, k_pool, v_pool, in_dtype == GQA_BF16,
                                             q_pos, nullptr, B, 1, h_kv, d, reach, max_kv_len,
-                                            std::log2(theta), st, block_table, ps_log2,
+                                            rope_params(theta, d), st, block_table, ps_log2,
                                             max_pages, num_pages);
     if (e != hipSuccess) return hip_fail(e, "paged append launch");
   }
@@ -534,8 +561,23 @@ int gqa_qkv_epilogue(const void* qkv, const void* bias, void* q_out, void* k_cac
     return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   hipError_t e = gqa::launch_qkv_epilogue(qkv, bias, q_out, k_cache, v_cache, dtype == GQA_BF16,
                                           start, len, B, C, h_q, h_kv, d, cap, kend,
-                                          std::log2(theta), (hipStream_t)stream);
+                                          rope_params(theta, d), (hipStream_t)stream);
   return e == hipSuccess ? GQA_OK : hip_fail(e, "QKV epilogue launch");
+}
+
+int gqa_set_rope_yarn(double factor, double original_max_position, double beta_fast,
+                      double beta_slow) {
+  g_err.clear();
+  if (!std::isfinite(factor) || factor < 1.0)
+    return fail(GQA_ERR_INVALID_ARG, "factor=%g must be finite and >= 1", factor);
+  if (factor > 1.0) {
+    if (!(original_max_position >= 1.0) || !std::isfinite(original_max_position))
+      return fail(GQA_ERR_INVALID_ARG, "original_max_position must be >= 1");
+    if (!(beta_fast > beta_slow) || !(beta_slow > 0.0) || !std::isfinite(beta_fast))
+      return fail(GQA_ERR_INVALID_ARG, "need beta_fast > beta_slow > 0");
+  }
+  g_yarn = YarnConfig{factor, original_max_position, beta_fast, beta_slow};
+  return GQA_OK;
 }
 
 int gqa_timing_enable(int on) {

@@ -28,9 +28,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// RoPE inverse frequency of pair j: theta^(-2j/d), in fp64.
-__device__ __forceinline__ double rope_omega(int j, int d, double log2_theta) {
-  return exp2(-(2.0 * (double)j / (double)d) * log2_theta);
+// RoPE parameters of a call.  Pair j turns by pos * omega_j with
+// omega_j = theta^(-2j/d); with YaRN scaling by a factor s, omega_j is blended
+// towards omega_j / s by a ramp over the pair index (0 at or below ramp_lo:
+// kept; 1 at or above ramp_hi: divided by s), and cos and sin are multiplied
+// by mscale.  inv_factor = 1 and mscale = 1 give plain RoPE.
+struct RopeParams {
+  double log2_theta;
+  double inv_factor;
+  double ramp_lo, ramp_hi;
+  float mscale;
+};
+
+// RoPE inverse frequency of pair j, in fp64.
+__device__ __forceinline__ double rope_omega(int j, int d, const RopeParams& rp) {
+  const double w = exp2(-(2.0 * (double)j / (double)d) * rp.log2_theta);
+  if (rp.inv_factor == 1.0) return w;
+  const double r = fmin(fmax(((double)j - rp.ramp_lo) / (rp.ramp_hi - rp.ramp_lo), 0.0), 1.0);
+  return w * (1.0 - r) + w * rp.inv_factor * r;
 }
 
 // cos and sin of pos * omega.  The angle is formed and reduced to
@@ -43,6 +58,14 @@ __device__ __forceinline__ void rope_cos_sin(double pos, double omega, float& c,
   double r = fma(-n, kTwoPiHi, a);
   r = fma(-n, kTwoPiLo, r);
   sincosf((float)r, &s, &c);
+}
+
+// cos and sin of pair j at position pos under rp (YaRN's mscale included).
+__device__ __forceinline__ void rope_cs(double pos, int j, int d, const RopeParams& rp, float& c,
+                                        float& s) {
+  rope_cos_sin(pos, rope_omega(j, d, rp), c, s);
+  c *= rp.mscale;
+  s *= rp.mscale;
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

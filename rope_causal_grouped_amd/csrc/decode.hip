@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
     float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int64_t cap, int kv_len_max,
-    double q_pos_s, double log2_theta, float sl2, int n_split, const int64_t* __restrict__ kvl_arr,
+    double q_pos_s, RopeParams rp, float sl2, int n_split, const int64_t* __restrict__ kvl_arr,
     const int64_t* __restrict__ qpos_arr, int kvl_from_pos, int q_rotated, KvRows kr) {
   constexpr int CH = kDecodeChunk;
   constexpr int WK = CH / 4;            // keys per wave
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
       for (int e = 0; e < 8; ++e) {
         const int j = s * 32 + h4 * 8 + e;
         float cs_c = 1.f, cs_s = 0.f;   // q_rotated: the query is used as given
-        if (!q_rotated) rope_cos_sin(q_pos, rope_omega(j, D, log2_theta), cs_c, cs_s);
+        if (!q_rotated) rope_cs(q_pos, j, D, rp, cs_c, cs_s);
         const float x1 = (e & 1) ? __uint_as_float(r1[e >> 1] & 0xffff0000u)
                                  : __uint_as_float(r1[e >> 1] << 16);
         const float x2 = (e & 1) ? __uint_as_float(r2[e >> 1] & 0xffff0000u)
@@ -319,7 +319,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po, int h_q, int h_kv,
-    int g, int n_hb, int64_t cap, int kv_len_max, double q_pos_s, double log2_theta, float scale,
+    int g, int n_hb, int64_t cap, int kv_len_max, double q_pos_s, RopeParams rp, float scale,
     int n_split, const int64_t* __restrict__ kvl_arr, const int64_t* __restrict__ qpos_arr,
     int kvl_from_pos, int q_rotated, KvRows kr) {
   constexpr int CH = kDecodeChunk;
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     if (cc < nh) {
       const float* qrow = q + ((int64_t)b * h_q + (int64_t)u * g + hb * 16 + cc) * D;
       float c = 1.f, s = 0.f;   // q_rotated: the query is used as given
-      if (!q_rotated) rope_cos_sin(q_pos, rope_omega(j, D, log2_theta), c, s);
+      if (!q_rotated) rope_cs(q_pos, j, D, rp, c, s);
       y1 = fmaf(qrow[j], c, -qrow[j + D / 2] * s);
       y2 = fmaf(qrow[j + D / 2], c, qrow[j] * s);
     }
@@ -468,7 +468,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
                          int64_t kv_len, int64_t q_pos, const int64_t* kvl_arr,
                          const int64_t* qpos_arr, int kvl_from_pos, int q_rotated,
                          const int32_t* bt, int ps_log2, int64_t max_pages, int64_t num_pages,
-                         double log2_theta,
+                         RopeParams rp,
                          float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end) {
   const int g = h_q / h_kv;
@@ -482,23 +482,23 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
     if (d == 128)
       decode_split_bf16_kernel<128><<<grid, 256, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
-          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split, kvl_arr,
+          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, rp, sl2, n_split, kvl_arr,
           qpos_arr, kvl_from_pos, q_rotated, kr);
     else
       decode_split_bf16_kernel<64><<<grid, 256, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
-          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, sl2, n_split, kvl_arr,
+          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, rp, sl2, n_split, kvl_arr,
           qpos_arr, kvl_from_pos, q_rotated, kr);
   } else {
     if (d == 128)
       decode_split_f32_kernel<128><<<grid, 256, 0, st>>>(
           (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
-          n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split, kvl_arr, qpos_arr,
+          n_hb, cap, (int)kv_len, (double)q_pos, rp, scale, n_split, kvl_arr, qpos_arr,
           kvl_from_pos, q_rotated, kr);
     else
       decode_split_f32_kernel<64><<<grid, 256, 0, st>>>(
           (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
-          n_hb, cap, (int)kv_len, (double)q_pos, log2_theta, scale, n_split, kvl_arr, qpos_arr,
+          n_hb, cap, (int)kv_len, (double)q_pos, rp, scale, n_split, kvl_arr, qpos_arr,
           kvl_from_pos, q_rotated, kr);
   }
   hipError_t err = hipGetLastError();

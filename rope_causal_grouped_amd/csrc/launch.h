@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace gqa {
 
 constexpr int kPrefillTileK = 64;      // key padding granule of the prepared K/V
@@ -14,9 +16,9 @@ constexpr int kDecodeChunk = 1024;     // keys per decode split
 constexpr int kDecodeMaxSplitsLds = 8192;  // chunk weights staged by the merge kernel
 
 hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,
-                             double log2_theta, hipStream_t st);
+                             RopeParams rp, hipStream_t st);
 
-hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double log2_theta,
+hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, RopeParams rp,
                              hipStream_t st);
 
 hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
@@ -33,14 +35,14 @@ hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* c
 // through the block table bt [B][max_pages]
 hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc, int bf16,
                                const int64_t* start, const int64_t* len, int64_t B, int64_t C,
-                               int h_kv, int d, int64_t cap, int64_t end, double log2_theta,
+                               int h_kv, int d, int64_t cap, int64_t end, RopeParams rp,
                                hipStream_t st, const int32_t* bt = nullptr, int ps_log2 = 0,
                                int64_t max_pages = 0, int64_t num_pages = 0);
 
 hipError_t launch_qkv_epilogue(const void* x, const void* bias, void* q_out, void* kc, void* vc,
                                int bf16, const int64_t* start, const int64_t* len, int64_t B,
                                int64_t C, int h_q, int h_kv, int d, int64_t cap, int64_t end,
-                               double log2_theta, hipStream_t st);
+                               RopeParams rp, hipStream_t st);
 
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
                                const float* kmax, const float2* cs, void* o, int out_bf16,
@@ -67,7 +69,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
                          int64_t kv_len, int64_t q_pos, const int64_t* kvl_arr,
                          const int64_t* qpos_arr, int kvl_from_pos, int q_rotated,
                          const int32_t* bt, int ps_log2, int64_t max_pages, int64_t num_pages,
-                         double log2_theta,
+                         RopeParams rp,
                          float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end);
 

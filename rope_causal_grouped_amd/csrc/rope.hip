@@ -16,7 +16,7 @@ namespace gqa {
 template <typename T>
 __global__ __launch_bounds__(256) void rope_apply_kernel(T* __restrict__ x, int64_t n_pairs, int64_t L,
                                                          int h, int d, int64_t pos0,
-                                                         double log2_theta) {
+                                                         RopeParams rp) {
   const int half = d >> 1;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_pairs;
        idx += (int64_t)gridDim.x * blockDim.x) {
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(T* __restrict__ x, int6
     const int j = (int)(idx - row * half);
     const int64_t l = (row / h) % L;
     float c, s;
-    rope_cos_sin((double)(pos0 + l), rope_omega(j, d, log2_theta), c, s);
+    rope_cs((double)(pos0 + l), j, d, rp, c, s);
     T* p = x + row * d;
     float x1, x2;
     if constexpr (sizeof(T) == 2) {
@@ -47,39 +47,39 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(T* __restrict__ x, int6
 }
 
 hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,
-                             double log2_theta, hipStream_t st) {
+                             RopeParams rp, hipStream_t st) {
   const int64_t n_pairs = B * L * h * (d / 2);
   const int64_t want = (n_pairs + 255) / 256;
   const int grid = (int)(want < 65536 ? want : 65536);
   if (dtype == 1)
     rope_apply_kernel<uint16_t><<<grid, 256, 0, st>>>((uint16_t*)x, n_pairs, L, h, d, pos0,
-                                                      log2_theta);
+                                                      rp);
   else
-    rope_apply_kernel<float><<<grid, 256, 0, st>>>((float*)x, n_pairs, L, h, d, pos0, log2_theta);
+    rope_apply_kernel<float><<<grid, 256, 0, st>>>((float*)x, n_pairs, L, h, d, pos0, rp);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // cs[l][j] = (cos, sin)(pos(l) * omega_j) for l < L, j < d/2, pos(l) = pos0 + l.
 __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ cs, int64_t n, int d,
-                                                         int64_t pos0, double log2_theta) {
+                                                         int64_t pos0, RopeParams rp) {
   const int half = d >> 1;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t l = idx / half;
     const int j = (int)(idx - l * half);
     float c, s;
-    rope_cos_sin((double)(pos0 + l), rope_omega(j, d, log2_theta), c, s);
+    rope_cs((double)(pos0 + l), j, d, rp, c, s);
     cs[idx] = make_float2(c, s);
   }
 }
 
-hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, double log2_theta,
+hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, RopeParams rp,
                              hipStream_t st) {
   const int64_t n = L * (d / 2);
   const int64_t want = (n + 255) / 256;
   const int grid = (int)(want < 65536 ? want : 65536);
-  rope_table_kernel<<<grid, 256, 0, st>>>(cs, n, d, pos0, log2_theta);
+  rope_table_kernel<<<grid, 256, 0, st>>>(cs, n, d, pos0, rp);
   return hipGetLastError();
 }
 
@@ -286,7 +286,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ kc, T* __restrict__ vc,
     const int64_t* __restrict__ start, const int64_t* __restrict__ len, int64_t n_pairs,
-    int64_t C, int h_kv, int d, int64_t cap, int64_t end, double log2_theta,
+    int64_t C, int h_kv, int d, int64_t cap, int64_t end, RopeParams rp,
     const int32_t* __restrict__ bt, int ps_log2, int64_t max_pages, int64_t num_pages) {
   const int half = d >> 1;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n_pairs;
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
       dst = (((int64_t)pid * h_kv + u) * ((int64_t)1 << ps_log2) + (p & ((1 << ps_log2) - 1))) * d;
     }
     float c, s;
-    rope_cos_sin((double)p, rope_omega(j, d, log2_theta), c, s);
+    rope_cs((double)p, j, d, rp, c, s);
     const T* kr = k + row * d;
     const T* vr = v + row * d;
     T* kd = kc + dst;
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 
 hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc, int bf16,
                                const int64_t* start, const int64_t* len, int64_t B, int64_t C,
-                               int h_kv, int d, int64_t cap, int64_t end, double log2_theta,
+                               int h_kv, int d, int64_t cap, int64_t end, RopeParams rp,
                                hipStream_t st, const int32_t* bt, int ps_log2, int64_t max_pages,
                                int64_t num_pages) {
   const int64_t n_pairs = B * C * h_kv * (d / 2);
@@ -337,11 +337,11 @@ hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc,
   if (bf16)
     cache_append_kernel<uint16_t><<<grid, 256, 0, st>>>(
         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kc, (uint16_t*)vc, start, len, n_pairs,
-        C, h_kv, d, cap, end, log2_theta, bt, ps_log2, max_pages, num_pages);
+        C, h_kv, d, cap, end, rp, bt, ps_log2, max_pages, num_pages);
   else
     cache_append_kernel<float><<<grid, 256, 0, st>>>((const float*)k, (const float*)v, (float*)kc,
                                                      (float*)vc, start, len, n_pairs, C, h_kv, d,
-                                                     cap, end, log2_theta, bt, ps_log2, max_pages,
+                                                     cap, end, rp, bt, ps_log2, max_pages,
                                                      num_pages);
   return hipGetLastError();
 }
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(
     const T* __restrict__ x, const T* __restrict__ bias, T* __restrict__ q_out,
     T* __restrict__ kc, T* __restrict__ vc, const int64_t* __restrict__ start,
     const int64_t* __restrict__ len, int64_t n_rows, int64_t C, int h_q, int h_kv, int d,
-    int64_t cap, int64_t end, double log2_theta) {
+    int64_t cap, int64_t end, RopeParams rp) {
   constexpr int E = 16 / sizeof(T);             // elements per 16-byte chunk
   __shared__ float2 csl[kEpiTokens][64];        // (cos, sin) per token and pair (d <= 128)
   const int cpr = d / E;                        // chunks per head row
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(
     const int tok = idx / half, j = idx % half;
     const int64_t p = token_pos(tok);
     float c = 1.f, sn = 0.f;
-    if (p >= 0) rope_cos_sin((double)p, rope_omega(j, d, log2_theta), c, sn);
+    if (p >= 0) rope_cs((double)p, j, d, rp, c, sn);
     csl[tok][j] = make_float2(c, sn);
   }
   __syncthreads();
@@ -475,18 +475,18 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(
 hipError_t launch_qkv_epilogue(const void* x, const void* bias, void* q_out, void* kc, void* vc,
                                int bf16, const int64_t* start, const int64_t* len, int64_t B,
                                int64_t C, int h_q, int h_kv, int d, int64_t cap, int64_t end,
-                               double log2_theta, hipStream_t st) {
+                               RopeParams rp, hipStream_t st) {
   const int64_t n_rows = B * C;
   const unsigned grid = (unsigned)((n_rows + kEpiTokens - 1) / kEpiTokens);
   if (bf16)
     qkv_epilogue_kernel<uint16_t><<<grid, 256, 0, st>>>(
         (const uint16_t*)x, (const uint16_t*)bias, (uint16_t*)q_out, (uint16_t*)kc, (uint16_t*)vc,
-        start, len, n_rows, C, h_q, h_kv, d, cap, end, log2_theta);
+        start, len, n_rows, C, h_q, h_kv, d, cap, end, rp);
   else
     qkv_epilogue_kernel<float><<<grid, 256, 0, st>>>((const float*)x, (const float*)bias,
                                                      (float*)q_out, (float*)kc, (float*)vc, start,
                                                      len, n_rows, C, h_q, h_kv, d, cap, end,
-                                                     log2_theta);
+                                                     rp);
   return hipGetLastError();
 }
 

@@ -488,6 +488,55 @@ def pin_paged_append_is_contiguous(orc):
         close(orc.paged_rows(kp2, bt, b, cap, ps), kc2[b], 1e-12, "pool after append")
 
 
+# --------------------------------------------------------------- YaRN ----
+
+def pin_yarn_factor_one_is_plain(orc):
+    """A YaRN factor of 1 leaves RoPE unchanged."""
+    rng = _rng(21)
+    x = _rand(rng, 2, 5, 3, 64)
+    y = orc.YaRN(factor=1.0)
+    close(orc.inv_freq(64, y), orc.inv_freq(64), 0.0, "frequencies")
+    close(orc.rope(x, np.arange(100, 105), y), orc.rope(x, np.arange(100, 105)), 0.0, "rotation")
+
+
+def pin_yarn_regions(orc):
+    """Per pair, count the turns n = L_orig * omega / (2 pi) over the original
+    context (Qwen2: 32768 positions, base 1e6, extension 4x to 128K).  Pairs
+    turning at least twice beta_fast = 32 times keep their frequency; pairs
+    turning at most half of beta_slow = 1 times are slowed by the factor
+    exactly; every pair lies between, and the slow-down never decreases
+    towards low frequencies."""
+    d, s = 128, 4.0
+    y = orc.YaRN(theta=1.0e6, factor=s, original_max_position=32768.0)
+    w = np.array([1.0e6 ** (-2.0 * j / d) for j in range(d // 2)])
+    w2 = orc.inv_freq(d, y)
+    turns = 32768.0 * w / (2.0 * math.pi)
+    keep, slow = turns >= 64.0, turns <= 0.5
+    assert keep.sum() >= 8 and slow.sum() >= 8
+    assert np.allclose(w2[keep], w[keep], rtol=1e-13, atol=0.0), "kept pairs"
+    assert np.allclose(w2[slow], w[slow] / s, rtol=1e-13, atol=0.0), "slowed pairs"
+    assert np.all(w2 <= w * (1 + 1e-15)) and np.all(w2 >= w / s * (1 - 1e-15))
+    ratio = w / w2
+    assert np.all(np.diff(ratio) >= -1e-12)
+
+
+def pin_yarn_attention_factor(orc):
+    """Under YaRN with factor s every rotated row is longer by 0.1 ln s + 1
+    (the rotation keeps norms; the factor rescales the attention logits by
+    its square), and q'.k' still depends on m - n only."""
+    rng = _rng(22)
+    y = orc.YaRN(factor=8.0, original_max_position=4096.0)
+    x = _rand(rng, 1, 7, 2, 32)
+    xr = orc.rope(x, np.arange(500, 507), y)
+    close(np.linalg.norm(xr, axis=-1), np.linalg.norm(x, axis=-1) * (0.1 * math.log(8.0) + 1.0),
+          1e-12, "norm")
+    q = _rand(rng, 1, 1, 1, 32)
+    k = _rand(rng, 1, 1, 1, 32)
+    a = np.sum(orc.rope(q, [40000], y) * orc.rope(k, [39990], y))
+    b = np.sum(orc.rope(q, [10], y) * orc.rope(k, [0], y))
+    assert abs(a - b) < 1e-9, (a, b)
+
+
 ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_rope_half_split_pairing, pin_rope_norm, pin_rope_relative,
             pin_rope_group_law, pin_group_example, pin_repeat_interleave,
@@ -496,4 +545,5 @@ ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_chunked_prefill_is_prefill, pin_decode_append_is_prefill_row,
             pin_cache_append_pair0, pin_ragged_decode_is_single, pin_qkv_layout,
             pin_qkv_epilogue_then_attention, pin_paged_decode_is_contiguous,
-            pin_paged_append_is_contiguous]
+            pin_paged_append_is_contiguous, pin_yarn_factor_one_is_plain, pin_yarn_regions,
+            pin_yarn_attention_factor]

@@ -250,3 +250,12 @@ def paged_call(lib, **kw):
 def test_decode_paged_rejects(lib, kw, code):
     assert paged_call(lib, **kw) == code
     assert lib.gqa_last_error()
+
+
+def test_set_rope_yarn_rejects(lib):
+    assert lib.gqa_set_rope_yarn(0.5, 32768.0, 32.0, 1.0) == _lib.GQA_ERR_INVALID_ARG
+    assert lib.gqa_set_rope_yarn(4.0, 0.0, 32.0, 1.0) == _lib.GQA_ERR_INVALID_ARG
+    assert lib.gqa_set_rope_yarn(4.0, 32768.0, 1.0, 32.0) == _lib.GQA_ERR_INVALID_ARG
+    assert lib.gqa_set_rope_yarn(float("nan"), 32768.0, 32.0, 1.0) == _lib.GQA_ERR_INVALID_ARG
+    assert lib.gqa_set_rope_yarn(4.0, 32768.0, 32.0, 1.0) == _lib.GQA_OK
+    assert lib.gqa_set_rope_yarn(1.0, 0.0, 0.0, 0.0) == _lib.GQA_OK   # back to plain RoPE

@@ -368,3 +368,44 @@ def test_decode_paged_bad_page_is_nan():
     torch.cuda.synchronize()
     o = host(o)
     assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1]))
+
+
+# --------------------------------------------------------------- YaRN ----
+
+@pytest.fixture
+def yarn_4x():
+    """Qwen2's long-context setting for the test's calls, reset afterwards."""
+    gqa.set_rope_yarn(4.0, 32768.0, 32.0, 1.0)
+    try:
+        yield oracle.YaRN(theta=1.0e6, factor=4.0, original_max_position=32768.0)
+    finally:
+        gqa.set_rope_yarn(1.0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_yarn_rope_apply(yarn_4x, dtype):
+    q, _, _ = inputs(2, 37, 3, 3, 128, dtype, 45)
+    x = dev(q, dtype)
+    gqa.rope_apply(x, pos0=100000)
+    torch.cuda.synchronize()
+    assert_rotated_rows(host(x), oracle.rope(q, np.arange(100000, 100037), yarn_4x), dtype,
+                        "YaRN rope")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_yarn_prefill_and_decode(yarn_4x, dtype):
+    h_q, h_kv, d = (28, 4, 128) if dtype == torch.bfloat16 else (14, 2, 64)
+    B, L = 2, 700
+    note(f"YaRN prefill + decode {dtype}")
+    q, k, v = inputs(B, L, h_q, h_kv, d, dtype, 46)
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    kc = torch.zeros((B, L + 40000, h_kv, d), dtype=dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    o = gqa.prefill(qd, kd, vd, k_cache=kc, v_cache=vc)
+    od = gqa.decode(qd[:, -1].contiguous(), kc, vc, kv_len=L, q_pos=L + 39000)
+    torch.cuda.synchronize()
+    assert_parity(host(o), oracle.prefill(q, k, v, theta=yarn_4x), dtype, "YaRN prefill")
+    kc_h, vc_h = host(kc), host(vc)
+    assert_rotated_rows(kc_h[:, :L], oracle.rope(k, np.arange(L), yarn_4x), dtype, "YaRN cache")
+    assert_parity(host(od), oracle.decode(q[:, -1], kc_h, vc_h, L, L + 39000, theta=yarn_4x),
+                  dtype, "YaRN decode far past the cache")

@@ -3,6 +3,7 @@ check that at least one pin catches each of them."""
 
 import importlib.util
 import os
+import sys
 
 import numpy as np
 import pytest
@@ -16,6 +17,7 @@ ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file
 def fresh_oracle():
     spec = importlib.util.spec_from_file_location("oracle_mutant", ORACLE_SRC)
     mod = importlib.util.module_from_spec(spec)
+    sys.modules["oracle_mutant"] = mod    # dataclasses look the module up by name
     spec.loader.exec_module(mod)
     return mod
 
@@ -189,13 +191,34 @@ def m_paged_page_of_next_block(mod):
     mod.paged_rows = paged_rows
 
 
+def m_yarn_ramp_reversed(mod):
+    orig = mod.yarn_ramp
+    mod.yarn_ramp = lambda spec, d: 1.0 - orig(spec, d)
+
+
+def m_yarn_no_attention_factor(mod):
+    mod.rope_mscale = lambda theta: 1.0
+
+
+def m_yarn_factor_squared(mod):
+    orig = mod.inv_freq
+
+    def inv_freq(d, theta=mod.ROPE_THETA):
+        if isinstance(theta, mod.YaRN) and theta.factor != 1.0:
+            import dataclasses
+            theta = dataclasses.replace(theta, factor=theta.factor ** 2)
+        return orig(d, theta)
+    mod.inv_freq = inv_freq
+
+
 MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
            m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
            m_transposed_weights, m_softmax_no_norm, m_decode_unrotated_query,
            m_chunk_position_shift, m_ragged_first_value, m_cached_key_unrotated,
            m_qkv_k_v_swapped, m_qkv_bias_dropped, m_qkv_heads_transposed,
-           m_paged_row_major_page, m_paged_page_of_next_block]
+           m_paged_row_major_page, m_paged_page_of_next_block, m_yarn_ramp_reversed,
+           m_yarn_no_attention_factor, m_yarn_factor_squared]
 
 
 def failing_pins(mod):
