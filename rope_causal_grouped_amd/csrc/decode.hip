@@ -82,13 +82,18 @@ __device__ bool stage_pages(const KvRows& kr, int b, int k0, int k1, int* pg) {
   return bad == 0;
 }
 
-// element offset of (sequence b, position key, group u) in the K or V store
+// element offset of (sequence b, position key, group u) in the K or V store:
+// contiguous cache, or row key & (page_size - 1) of the key's page
+template <bool PAGED>
 __device__ __forceinline__ int64_t kv_row(const KvRows& kr, const int* pg, int k0, int b, int key,
                                           int u, int h_kv, int D) {
-  if (!kr.bt) return (((int64_t)b * kr.cap + key) * h_kv + u) * D;
-  const int page = pg[(key >> kr.ps_log2) - (k0 >> kr.ps_log2)];
-  const int row = key & ((1 << kr.ps_log2) - 1);
-  return (((int64_t)page * h_kv + u) * ((int64_t)1 << kr.ps_log2) + row) * D;
+  if constexpr (!PAGED) {
+    return ((int64_t)b * kr.cap * h_kv + u) * D + (int64_t)key * (h_kv * D);
+  } else {
+    const int page = pg[(key >> kr.ps_log2) - (k0 >> kr.ps_log2)];
+    const int row = key & ((1 << kr.ps_log2) - 1);
+    return (((int64_t)page * h_kv + u) * ((int64_t)1 << kr.ps_log2) + row) * D;
+  }
 }
 
 // partial state of an invalid chunk: the merge turns it into NaN output
@@ -118,7 +123,7 @@ int decode_num_splits(int64_t kv_len) {
 // key-contiguous operand.  Heads beyond 16 per group run as extra head
 // blocks (another pass over the chunk).  The cache is read once, so its
 // loads are non-temporal (they do not displace reused lines in the caches).
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     return;
   }
   const int chunk0 = split * CH;
-  if (kr.bt && !stage_pages(kr, b, chunk0, min(chunk0 + CH, kv_len), pg)) {
+  if (PAGED && !stage_pages(kr, b, chunk0, min(chunk0 + CH, kv_len), pg)) {
     write_nan_state(pm, pl, po, (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16,
                     min(16, g - hb * 16), D);
     return;
@@ -210,14 +215,14 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
 #pragma unroll
       for (int s = 0; s < NS; ++s)
         ka[blk][s] = __builtin_nontemporal_load(
-            (const u32x4*)(kc + kv_row(kr, pg, chunk0, b, key, u, h_kv, D) + s * 32 + h4 * 8));
+            (const u32x4*)(kc + kv_row<PAGED>(kr, pg, chunk0, b, key, u, h_kv, D) + s * 32 + h4 * 8));
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int ch = lane + 64 * i;
       const int key = min(k0 + ch / (D / 8), kv_len - 1);
       va[i] = __builtin_nontemporal_load(
-          (const u32x4*)(vc + kv_row(kr, pg, chunk0, b, key, u, h_kv, D) + (ch % (D / 8)) * 8));
+          (const u32x4*)(vc + kv_row<PAGED>(kr, pg, chunk0, b, key, u, h_kv, D) + (ch % (D / 8)) * 8));
     }
     // S^T for 2 x 16 keys
     f32x4 sacc[2];
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
 // head block, b); 16 threads per head.  Scores of the chunk go to LDS, then
 // each thread reduces one head's max and sum and accumulates 1/16 of its
 // output dims.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
     float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po, int h_q, int h_kv,
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     }
     return;
   }
-  if (kr.bt && !stage_pages(kr, b, split * CH, min(split * CH + CH, kv_len), pg)) {
+  if (PAGED && !stage_pages(kr, b, split * CH, min(split * CH + CH, kv_len), pg)) {
     write_nan_state(pm, pl, po, (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16, nh, D);
     return;
   }
@@ -371,7 +376,7 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
   const int k0 = split * CH;
   const int nk = min(CH, kv_len - k0);
   for (int kk = tid; kk < nk; kk += 256) {
-    const float* krow = kc + kv_row(kr, pg, k0, b, k0 + kk, u, h_kv, D);
+    const float* krow = kc + kv_row<PAGED>(kr, pg, k0, b, k0 + kk, u, h_kv, D);
     for (int cc = 0; cc < nh; ++cc) {
       float dot = 0.f;
       for (int dd = 0; dd < D; ++dd) dot = fmaf(qs[cc][dd], krow[dd], dot);
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
     for (int kk = 0; kk < nk; ++kk) {
       const float p = sc[cc][kk];
-      const float* vrow = vc + kv_row(kr, pg, k0, b, k0 + kk, u, h_kv, D) + sub * DPT;
+      const float* vrow = vc + kv_row<PAGED>(kr, pg, k0, b, k0 + kk, u, h_kv, D) + sub * DPT;
 #pragma unroll
       for (int e = 0; e < DPT; ++e) acc[e] = fmaf(p, vrow[e], acc[e]);
     }
@@ -478,29 +483,29 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
   const float sl2 = scale * 1.4426950408889634f;
   const KvRows kr{bt, ps_log2, max_pages, num_pages, cap};
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
+  const bool paged = bt != nullptr;
+#define GQA_SPLIT(KERNEL, T, DD, PG, SC)                                                         \
+  KERNEL<DD, PG><<<grid, 256, 0, st>>>((const T*)q, (const T*)kc, (const T*)vc, ws_m, ws_l, ws_o, \
+                                       h_q, h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, rp,  \
+                                       SC, n_split, kvl_arr, qpos_arr, kvl_from_pos, q_rotated, kr)
   if (in_bf16) {
-    if (d == 128)
-      decode_split_bf16_kernel<128><<<grid, 256, 0, st>>>(
-          (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
-          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, rp, sl2, n_split, kvl_arr,
-          qpos_arr, kvl_from_pos, q_rotated, kr);
-    else
-      decode_split_bf16_kernel<64><<<grid, 256, 0, st>>>(
-          (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, ws_m, ws_l, ws_o, h_q,
-          h_kv, g, n_hb, cap, (int)kv_len, (double)q_pos, rp, sl2, n_split, kvl_arr,
-          qpos_arr, kvl_from_pos, q_rotated, kr);
+    if (d == 128) {
+      if (paged) GQA_SPLIT(decode_split_bf16_kernel, uint16_t, 128, true, sl2);
+      else GQA_SPLIT(decode_split_bf16_kernel, uint16_t, 128, false, sl2);
+    } else {
+      if (paged) GQA_SPLIT(decode_split_bf16_kernel, uint16_t, 64, true, sl2);
+      else GQA_SPLIT(decode_split_bf16_kernel, uint16_t, 64, false, sl2);
+    }
   } else {
-    if (d == 128)
-      decode_split_f32_kernel<128><<<grid, 256, 0, st>>>(
-          (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
-          n_hb, cap, (int)kv_len, (double)q_pos, rp, scale, n_split, kvl_arr, qpos_arr,
-          kvl_from_pos, q_rotated, kr);
-    else
-      decode_split_f32_kernel<64><<<grid, 256, 0, st>>>(
-          (const float*)q, (const float*)kc, (const float*)vc, ws_m, ws_l, ws_o, h_q, h_kv, g,
-          n_hb, cap, (int)kv_len, (double)q_pos, rp, scale, n_split, kvl_arr, qpos_arr,
-          kvl_from_pos, q_rotated, kr);
+    if (d == 128) {
+      if (paged) GQA_SPLIT(decode_split_f32_kernel, float, 128, true, scale);
+      else GQA_SPLIT(decode_split_f32_kernel, float, 128, false, scale);
+    } else {
+      if (paged) GQA_SPLIT(decode_split_f32_kernel, float, 64, true, scale);
+      else GQA_SPLIT(decode_split_f32_kernel, float, 64, false, scale);
+    }
   }
+#undef GQA_SPLIT
   hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, st);
   if (err != hipSuccess) return err;
