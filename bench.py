@@ -48,8 +48,12 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
 # device copy: FETCH x 2.00, WRITE x 1.00).  Each figure is valid only for the
 # kernel source it was measured on (sha256 prefix); otherwise it reports null.
 TRAFFIC = {
-    "prefill": ("prefill_bf16.hip", "d8185fd8814ab33a", (137380.4 * 2.0 + 238261.5) * 1024),
-    "decode": ("decode.hip", "453db71308e11c0a", (1058210.9 * 2.0 + 14784.1) * 1024),
+    "prefill": ("prefill_bf16.hip", "df83c3ed623fdc47", (110757.5 * 2.0 + 233049.4) * 1024),
+    "decode": ("decode.hip", "55c3dd751eae0bac", (1058368.0 * 2.0 + 14784.1) * 1024),
+    "prefill_chunk": ("prefill_bf16.hip", "df83c3ed623fdc47", (42658.2 * 2.0 + 57732.9) * 1024),
+    "decode_append": ("decode.hip", "55c3dd751eae0bac", (928761.8 * 2.0 + 14784.1) * 1024),
+    "decode_paged": ("decode.hip", "55c3dd751eae0bac", (1054822.1 * 2.0 + 14784.1) * 1024),
+    "qkv_epilogue": ("rope.hip", "9a72d19c79f91c45", (73823.8 * 2.0 + 147456.0) * 1024),
 }
 
 
@@ -152,7 +156,7 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
         "value": flops / (call_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "call_ms": call_ms,
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": ach,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                     "kernel_ms": attn_avg, "traffic": None}}
+                     "kernel_ms": attn_avg, "traffic": traffic_bytes("prefill_chunk")}}
     del pre, qd, kd, vd, qc, kn, vn, kc, vc, ws, oc
     log(f"[bench] chunked prefill: {call_ms:.3f} ms per call")
 
@@ -203,7 +207,7 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
         "value": kvb / (call_ms * 1e-3) / 1e9, "unit": "GB/s", "call_ms": call_ms,
         "roofline": {"bound": "hbm", "kernel": "decode_split_bf16_kernel", "achieved": dach,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
-                     "kernel_ms": split_avg, "traffic": None}}
+                     "kernel_ms": split_avg, "traffic": traffic_bytes("decode_append")}}
     log(f"[bench] appending decode: {call_ms:.3f} ms per call")
     del kn, vn
 
@@ -251,7 +255,7 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
         "value": kvb / (call_ms * 1e-3) / 1e9, "unit": "GB/s", "call_ms": call_ms,
         "roofline": {"bound": "hbm", "kernel": "decode_split_bf16_kernel", "achieved": dach,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
-                     "kernel_ms": split_avg, "traffic": None}}
+                     "kernel_ms": split_avg, "traffic": traffic_bytes("decode_paged")}}
     log(f"[bench] paged decode: {call_ms:.3f} ms per call")
     del pools, bt, od, wsd
 
@@ -286,7 +290,7 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
         "value": rate, "unit": "GB/s", "call_ms": call_ms,
         "roofline": {"bound": "hbm", "kernel": "qkv_epilogue_kernel", "achieved": rate,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": rate / PEAK_HBM_GBS,
-                     "kernel_ms": call_ms, "traffic": None}}
+                     "kernel_ms": call_ms, "traffic": traffic_bytes("qkv_epilogue")}}
     log(f"[bench] QKV epilogue: {call_ms:.3f} ms per call")
     return res
 
