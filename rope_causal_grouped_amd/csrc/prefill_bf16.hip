@@ -77,7 +77,12 @@ __device__ __forceinline__ float bf16x8_sum(const bf16x8 v, float acc) {
 
 }  // namespace
 
-template <int D, bool OUT_BF16>
+// PRE: the kernel rotates Q itself (cs set) and folds scale * log2(e) into
+// it before the one bf16 rounding; the score products then start from -z
+// (z: the row's reference once known, 0 before) and a probability is a bare
+// exp2 of the shifted score.  Without PRE (Q arrives rotated and rounded)
+// the scale is applied to each score instead, so Q is rounded only once.
+template <int D, bool OUT_BF16, bool PRE>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
@@ -224,18 +229,32 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     u32x4 raw[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) raw[s] = *(const u32x4*)(qrow + s * 16 + hl * 8);
-    const float2* csr = cs + (int64_t)pos * (D / 2) + hl * 8;   // (cs NULL: q is rotated)
+    if constexpr (PRE) {
+      // cos/sin of the row's position, 16 bytes (two pairs) per load
+      const float4* csr = (const float4*)(cs + (int64_t)pos * (D / 2) + hl * 8);
+      f32x4 c4[NS / 2][4];
 #pragma unroll
-    for (int s = 0; s < NS / 2; ++s) {
+      for (int s = 0; s < NS / 2; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 r2 = cs ? csr[s * 16 + e] : make_float2(1.f, 0.f);   // NULL: rotated
-        const uint32_t w1 = raw[s][e >> 1], w2 = raw[s + NS / 2][e >> 1];
-        const float x1 = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
-        const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);
-        qb[s][e] = (__bf16)fmaf(x1, r2.x, -x2 * r2.y);
-        qb[s + NS / 2][e] = (__bf16)fmaf(x2, r2.x, x1 * r2.y);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float4 t = csr[s * 8 + e2];
+          c4[s][e2] = f32x4{t.x, t.y, t.z, t.w};
+        }
+#pragma unroll
+      for (int s = 0; s < NS / 2; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float cr = c4[s][e >> 1][(e & 1) * 2], sr = c4[s][e >> 1][(e & 1) * 2 + 1];
+          const uint32_t w1 = raw[s][e >> 1], w2 = raw[s + NS / 2][e >> 1];
+          const float x1 = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
+          const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);
+          qb[s][e] = (__bf16)(fmaf(x1, cr, -x2 * sr) * sl2);
+          qb[s + NS / 2][e] = (__bf16)(fmaf(x2, cr, x1 * sr) * sl2);
+        }
       }
+    } else {   // rotated already
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qb[s] = __builtin_bit_cast(bf16x8, raw[s]);
     }
   }
   // |q'| of the row from the bf16 values the matrix cores see, in score
@@ -250,7 +269,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         const float x = (float)qb[s][e];
         ss = fmaf(x, x, ss);
       }
-    qcap = sqrtf(sum_xor32(ss)) * sl2 * 1.01f;
+    qcap = sqrtf(sum_xor32(ss)) * (PRE ? 1.f : sl2) * 1.01f;
   }
 
   // ---- operand read offsets (elements), swizzled like the stores
@@ -270,6 +289,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const f32x16 zero16 = {};
+  float zsh = 0.f;     // PRE: shift already subtracted from the scores
+  f32x16 negz = {};    // PRE: -zsh, the initial accumulator of S^T
   f32x16 sacc[2];     // scores of the tile between its matrix and vector phases
   bf16x8 pb[2][2];    // probabilities between the vector and the next matrix phase
 #pragma unroll
@@ -299,8 +320,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   };
   auto mma_qk = [&](const bf16x8 a, int j) {
     const int s = j / 2, c = j % 2;
-    sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[s], s == 0 ? zero16 : sacc[c], 0, 0,
-                                                      0);
+    sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        a, qb[s], s == 0 ? (PRE ? negz : zero16) : sacc[c], 0, 0, 0);
   };
   // P.V of tile i-1 and S^T of tile i
   auto matrix_full = [&](int i) {
@@ -361,8 +382,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[e], sl2, -m_run));
-      pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[e], sl2, -m_run));
+      if constexpr (PRE) {
+        pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[e]);
+        pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[e]);
+      } else {
+        pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[e], sl2, -m_run));
+        pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[e], sl2, -m_run));
+      }
     }
     acc0 = bf16x8_sum(pb[0][0], acc0);
     acc1 = bf16x8_sum(pb[0][1], acc1);
@@ -399,10 +425,24 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-      mx = max_xor32(mx) * sl2;
+      mx = PRE ? max_xor32(mx) + zsh : max_xor32(mx) * sl2;
       if (mx > m_new + kRescaleThreshold) m_new = mx;
     }
     if (__builtin_amdgcn_ballot_w64(m_new != m_run)) rescale(m_new);
+    if constexpr (PRE) {
+      if (__builtin_amdgcn_ballot_w64(m_new != zsh)) {   // new shift: this tile's
+        const float d = zsh - m_new;                      // scores, and the next
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s0[e] += d;
+          s1[e] += d;
+        }
+        zsh = m_new;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) negz[e] = -m_new;
+        asm volatile("" : "+a"(negz));
+      }
+    }
     const float psum = probs(s0, s1);
     l_run += psum;
     // probabilities here are <= 2^64; a sum past 2^32 owes a raise of m by
@@ -500,15 +540,18 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   const int n_bu = (int)(B * h_kv);
   const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e): exp(x) = exp2(x log2 e)
   const unsigned grid = (unsigned)((int64_t)n_rb * n_bu);
-#define GQA_LAUNCH(DD, OB)                                                                    \
-  prefill_bf16_kernel<DD, OB><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, cs, o, (int)L,      \
-                                                        (int)Lpad, h_q, h_kv, g, n_rb, sl2,  \
-                                                        causal, qstart, qlen, (int)kend)
+#define GQA_LAUNCH(DD, OB, PR)                                                               \
+  prefill_bf16_kernel<DD, OB, PR><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, cs, o, (int)L,  \
+                                                            (int)Lpad, h_q, h_kv, g, n_rb,   \
+                                                            sl2, causal, qstart, qlen, (int)kend)
+#define GQA_LAUNCH_D(DD, OB) \
+  do { if (cs) GQA_LAUNCH(DD, OB, true); else GQA_LAUNCH(DD, OB, false); } while (0)
   if (d == 128) {
-    if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);
+    if (out_bf16) GQA_LAUNCH_D(128, true); else GQA_LAUNCH_D(128, false);
   } else {
-    if (out_bf16) GQA_LAUNCH(64, true); else GQA_LAUNCH(64, false);
+    if (out_bf16) GQA_LAUNCH_D(64, true); else GQA_LAUNCH_D(64, false);
   }
+#undef GQA_LAUNCH_D
 #undef GQA_LAUNCH
   return hipGetLastError();
 }
