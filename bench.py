@@ -73,8 +73,10 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # the shader clock ramps up over the first few tens of milliseconds of
+    # load; 100 untimed steps put the timed ones at the sustained clock
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--only", choices=["prefill", "decode", "next"], default=None,
                    help="run one part only (for profiling)")
     p.add_argument("--no-cpu-baseline", action="store_true")
