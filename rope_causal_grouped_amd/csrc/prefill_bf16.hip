@@ -203,63 +203,58 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
-  // ---- prologue part 1: K(0) on its way; largest K norm this workgroup
-  // will see (per-tile norms from the preparation pass)
+  // ---- prologue part 1.  Global reads in the order they are needed (the
+  // vector-memory counter retires them in order): per-tile K norms, the Q
+  // row and its cos/sin, then the first tiles straight into LDS.
   const int n = n_tiles;
-  if (grp) {
-    load_tile(ks[0], 0);
-    if (n > 1) load_tile(ks[1], 1);
-  } else {
-    load_tile(vs[0], 0);
-  }
-  {
-    const float* kmax_bu = kmax + (int64_t)bu * (Lpad / TK);
-    float km = 0.f;
-    for (int t = tid; t < n_tiles; t += NW * 64) km = fmaxf(km, kmax_bu[t]);
+  const float* kmax_bu = kmax + (int64_t)bu * (Lpad / TK);
+  float km = tid < n_tiles ? kmax_bu[tid] : 0.f;
+  const uint16_t* qrow = q + ((int64_t)((int64_t)b * L + pl) * h_q + head) * D;
+  u32x4 raw[NS];
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) km = wave_max_xor(km, m);
-    if (lane == 0) wred[wave] = km;
-  }
-
-  // ---- Q row: load, rotate at pos, round to bf16 (B operand layout: lane
-  // holds dims s*16 + hl*8 + e of its row; RoPE pairs are (s, s + NS/2)).
-  bf16x8 qb[NS];
-  {
-    const uint16_t* qrow = q + ((int64_t)((int64_t)b * L + pl) * h_q + head) * D;
-    u32x4 raw[NS];
+  for (int s = 0; s < NS; ++s) raw[s] = *(const u32x4*)(qrow + s * 16 + hl * 8);
+  f32x4 c4[NS / 2][4];   // PRE: cos/sin of the row's position, two pairs per load
+  if constexpr (PRE) {
+    const float4* csr = (const float4*)(cs + (int64_t)pos * (D / 2) + hl * 8);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) raw[s] = *(const u32x4*)(qrow + s * 16 + hl * 8);
-    if constexpr (PRE) {
-      // cos/sin of the row's position, 16 bytes (two pairs) per load
-      const float4* csr = (const float4*)(cs + (int64_t)pos * (D / 2) + hl * 8);
-      f32x4 c4[NS / 2][4];
+    for (int s = 0; s < NS / 2; ++s)
 #pragma unroll
-      for (int s = 0; s < NS / 2; ++s)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float4 t = csr[s * 8 + e2];
-          c4[s][e2] = f32x4{t.x, t.y, t.z, t.w};
-        }
-#pragma unroll
-      for (int s = 0; s < NS / 2; ++s) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float cr = c4[s][e >> 1][(e & 1) * 2], sr = c4[s][e >> 1][(e & 1) * 2 + 1];
-          const uint32_t w1 = raw[s][e >> 1], w2 = raw[s + NS / 2][e >> 1];
-          const float x1 = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
-          const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);
-          qb[s][e] = (__bf16)(fmaf(x1, cr, -x2 * sr) * sl2);
-          qb[s + NS / 2][e] = (__bf16)(fmaf(x2, cr, x1 * sr) * sl2);
-        }
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float4 t = csr[s * 8 + e2];
+        c4[s][e2] = f32x4{t.x, t.y, t.z, t.w};
       }
-    } else {   // rotated already
+  }
+  // K(0), K(1) by waves 4-7, V(0) (twice) by waves 0-3: the same count on
+  // every path keeps the compiler's own waits for Q exact (past the last
+  // tile a harmless repeat of tile 0)
+  load_tile(grp ? ks[0] : vs[0], 0);
+  load_tile(grp ? ks[1] : vs[0], grp && n > 1 ? 1 : 0);
+
+  // ---- Q row: rotate at pos, round to bf16 (B operand layout: lane holds
+  // dims s*16 + hl*8 + e of its row; RoPE pairs are (s, s + NS/2)); done
+  // after the first barrier, when its reads have long arrived.
+  bf16x8 qb[NS];
+  float qcap;
+  auto rotate_q = [&] {
+  if constexpr (PRE) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) qb[s] = __builtin_bit_cast(bf16x8, raw[s]);
+    for (int s = 0; s < NS / 2; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float cr = c4[s][e >> 1][(e & 1) * 2], sr = c4[s][e >> 1][(e & 1) * 2 + 1];
+        const uint32_t w1 = raw[s][e >> 1], w2 = raw[s + NS / 2][e >> 1];
+        const float x1 = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
+        const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);
+        qb[s][e] = (__bf16)(fmaf(x1, cr, -x2 * sr) * sl2);
+        qb[s + NS / 2][e] = (__bf16)(fmaf(x2, cr, x1 * sr) * sl2);
+      }
     }
+  } else {   // rotated already
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qb[s] = __builtin_bit_cast(bf16x8, raw[s]);
   }
   // |q'| of the row from the bf16 values the matrix cores see, in score
   // units (scale * log2 e), with a margin for fp32 rounding
-  float qcap;
   {
     float ss = 0.f;
 #pragma unroll
@@ -271,6 +266,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       }
     qcap = sqrtf(sum_xor32(ss)) * (PRE ? 1.f : sl2) * 1.01f;
   }
+  };
 
   // ---- operand read offsets (elements), swizzled like the stores
   const int kswz = (c32 / KRPB) % KCPR;       // same for key rows c32 and 32 + c32
@@ -452,9 +448,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       m_raise = ceilf(__builtin_amdgcn_logf(fmaxf(max_xor32(psum), 1.0f)));
   };
 
-  // ---- prologue part 2: K(0) resident, bound known
-  if (grp) landed(n > 1);
+  // ---- prologue part 2: largest K norm this workgroup will see (per-tile
+  // norms from the preparation pass; more than one per thread only past
+  // 32768 keys); K(0) resident, bound known
+  for (int t = tid + NW * 64; t < n_tiles; t += NW * 64) km = fmaxf(km, kmax_bu[t]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) km = wave_max_xor(km, m);
+  if (lane == 0) wred[wave] = km;
+  if (grp) landed(true);   // K(0); K(1) may stay in flight
   __syncthreads();
+  rotate_q();
   {
     float km = wred[0];
 #pragma unroll
