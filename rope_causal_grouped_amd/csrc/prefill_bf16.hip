@@ -366,13 +366,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      // keep the accumulators in AGPRs outside this rare branch
-      asm volatile("" : "+a"(oacc[db]));
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      asm volatile("" : "+a"(oacc[db]));
-    }
   };
   auto probs = [&](const f32x16& s0, const f32x16& s1) {
     float acc0 = 0.f, acc1 = 0.f;
@@ -404,8 +400,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
           for (int e = 0; e < 8; ++e) pb[kb][hs][e] = (__bf16)0.0f;
       return;
     }
+    // (no AGPR constraint anywhere in this kernel: at two waves per SIMD the
+    // compiler then keeps every MFMA accumulator in VGPRs, and the vector
+    // ALU reads the scores without copies)
     f32x16 s0 = sacc[0], s1 = sacc[1];
-    asm volatile("" : "+v"(s0), "+v"(s1));   // scores to VGPRs once
     if (masked(i)) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -436,7 +434,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         zsh = m_new;
 #pragma unroll
         for (int e = 0; e < 16; ++e) negz[e] = -m_new;
-        asm volatile("" : "+a"(negz));
       }
     }
     const float psum = probs(s0, s1);
