@@ -371,7 +371,7 @@ hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* c
 // chunks (dims c.. and d/2 + c..) that one rotation couples, or per 16-byte
 // chunk of a V head.  Sums and rotations in fp32, one rounding to the
 // storage type.  Sequences outside [0, end) are skipped.
-constexpr int kEpiTokens = 4;
+constexpr int kEpiTokens = 2;
 
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_epilogue_kernel(
@@ -381,6 +381,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(
     int64_t cap, int64_t end, RopeParams rp) {
   constexpr int E = 16 / sizeof(T);             // elements per 16-byte chunk
   __shared__ float2 csl[kEpiTokens][64];        // (cos, sin) per token and pair (d <= 128)
+  __shared__ double oml[64];                    // inverse frequency per pair
   const int cpr = d / E;                        // chunks per head row
   const int half = d / 2;
   const int nq = h_q * (cpr / 2), nk = h_kv * (cpr / 2), nv = h_kv * cpr;
@@ -396,16 +397,23 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(
     if (!(s0 >= 0 && n >= 0 && n <= C && s0 + n <= end) || i >= n) return -1;
     return s0 + i;
   };
+  for (int j = threadIdx.x; j < half; j += blockDim.x) oml[j] = rope_omega(j, d, rp);
+  __syncthreads();
   for (int idx = threadIdx.x; idx < kEpiTokens * half; idx += blockDim.x) {
     const int tok = idx / half, j = idx % half;
     const int64_t p = token_pos(tok);
     float c = 1.f, sn = 0.f;
-    if (p >= 0) rope_cs((double)p, j, d, rp, c, sn);
+    if (p >= 0) {
+      rope_cos_sin((double)p, oml[j], c, sn);
+      c *= rp.mscale;
+      sn *= rp.mscale;
+    }
     csl[tok][j] = make_float2(c, sn);
   }
   __syncthreads();
-  auto load = [&](const T* p, float* f) {
-    const u32x4 w = *(const u32x4*)p;
+  // the projection output is read once (non-temporal); the bias by every token
+  auto load = [&](const T* p, float* f, bool once = true) {
+    const u32x4 w = once ? __builtin_nontemporal_load((const u32x4*)p) : *(const u32x4*)p;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = bf16_bits_to_f32((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
@@ -424,12 +432,12 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(f[e]);
     }
-    *(u32x4*)p = w;
+    __builtin_nontemporal_store(w, (u32x4*)p);   // written once
   };
   auto add_bias = [&](float* f, int col) {
     if (!bias) return;
     float bf[E];
-    load(bias + col, bf);
+    load(bias + col, bf, false);
 #pragma unroll
     for (int e = 0; e < E; ++e) f[e] += bf[e];
   };
