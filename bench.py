@@ -53,7 +53,7 @@ TRAFFIC = {
     "prefill_chunk": ("prefill_bf16.hip", "30a3dff53fb99a95", (42616.7 * 2.0 + 58121.9) * 1024),
     "decode_append": ("decode.hip", "55c3dd751eae0bac", (928761.8 * 2.0 + 14784.1) * 1024),
     "decode_paged": ("decode.hip", "55c3dd751eae0bac", (1054822.1 * 2.0 + 14784.1) * 1024),
-    "qkv_epilogue": ("rope.hip", "9a72d19c79f91c45", (73823.8 * 2.0 + 147456.0) * 1024),
+    "qkv_epilogue": ("rope.hip", "72eefc0ef755f754", (73831.7 * 2.0 + 147459.8) * 1024),
 }
 
 
