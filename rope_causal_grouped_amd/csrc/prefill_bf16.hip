@@ -30,11 +30,11 @@
 // SIMD one wave's matrix-core work always runs against the other wave's
 // softmax.  A matrix phase reads 32 operand fragments from LDS; they are
 // issued a few MFMAs ahead of their use so that LDS latency stays hidden.
-// The wave group in its vector phase also streams tiles from HBM straight
-// into LDS (global_load_lds_dwordx4, no staging registers), two phases ahead
-// of their use: K by waves 4-7, V by waves 0-3, each in a three-slot ring.  LDS rows are unpadded; the 16-byte
-// chunk index is XOR-swizzled with the row index, which keeps the operand
-// reads free of bank conflicts.
+// The wave group in its vector phase also streams the next tile from HBM
+// straight into LDS (global_load_lds_dwordx4, no staging registers): K by
+// waves 4-7, V by waves 0-3, each into a two-slot ring.
+// LDS rows are unpadded; the 16-byte chunk index is XOR-swizzled with the
+// row index, which keeps the operand reads free of bank conflicts.
 //
 // Softmax without a per-tile max.  |q'| * max|k'| (Cauchy-Schwarz; max over
 // the keys this workgroup visits, from the per-tile norms of the preparation
@@ -42,10 +42,14 @@
 // 64 (exp2 units) of that bound, probabilities are formed against m directly
 // (<= 2^64, far inside fp32 and bf16 range) and the tile max is not needed;
 // m is raised only if a tile's probability sum passes 2^32, which keeps O
-// and l bounded.  Until then (the first tile at least) the tile max is taken
-// first and m follows it lazily (raised when the max grows by more than 8).
-// m never exceeds the true running max by more than log2(64), so the
-// largest probability cannot underflow.
+// and l bounded.  A bound of at most 64 makes m = 0 valid from the start
+// (scores lie in [-64, 64]: no probability overflows or underflows).
+// Otherwise the tile max is taken first, until m is within reach of the
+// bound, and m follows it lazily (raised when the max grows by more than
+// 8); m then never exceeds the true running max by more than log2(64), so
+// the largest probability cannot underflow.
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -66,6 +70,9 @@ constexpr float kSumCap = 4294967296.0f;    // 2^32
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+template <int P>
+using Slot = std::integral_constant<int, P % 2>;
+
 __device__ __forceinline__ float bf16x8_sum(const bf16x8 v, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
@@ -78,10 +85,10 @@ __device__ __forceinline__ float bf16x8_sum(const bf16x8 v, float acc) {
 }  // namespace
 
 // PRE: the kernel rotates Q itself (cs set) and folds scale * log2(e) into
-// it before the one bf16 rounding; the score products then start from -z
-// (z: the row's reference once known, 0 before) and a probability is a bare
-// exp2 of the shifted score.  Without PRE (Q arrives rotated and rounded)
-// the scale is applied to each score instead, so Q is rounded only once.
+// it before the one bf16 rounding; a probability is then a bare exp2 of the
+// score while every row of the wave has m = 0, and exp2(s - m) otherwise.
+// Without PRE (Q arrives rotated and rounded) the scale is applied to each
+// score instead, so Q is rounded only once.
 template <int D, bool OUT_BF16, bool PRE>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
@@ -103,8 +110,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   constexpr int TILE_CH = TK * D / 8;         // chunks per K (or V^T) tile
   constexpr int LPG = TILE_CH / 64 / 4;       // direct loads per wave when 4 waves load a tile
   static_assert(LPG >= 1, "tile too small for the wave count");
-  __shared__ __attribute__((aligned(16))) uint16_t ks[3][TK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[3][TK * D];
+  // two-slot rings for K and V^T tiles, one array per slot; the loop below
+  // is unrolled by two, so every slot address is a compile-time constant
+  // folded into the read instructions' offset fields
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[TK * D], ks1[TK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[TK * D], vs1[TK * D];
   __shared__ float wred[NW];
 
   const int tid = threadIdx.x;
@@ -197,11 +207,20 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
           (const void __attribute__((address_space(1)))*)(src + (int64_t)tile * TK * D + loff[n]),
           (void __attribute__((address_space(3)))*)&ring[(wg4 * LPG + n) * 64 * 8], 16, 0, 0);
   };
-  // wait for this wave's older tile; `newer`: one more tile was issued since
-  auto landed = [&](bool newer) {
-    if (newer) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPG) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  auto kslot = [&](auto P) -> uint16_t* {
+    if constexpr (decltype(P)::value == 0) return ks0;
+    else return ks1;
   };
+  auto vslot = [&](auto P) -> uint16_t* {
+    if constexpr (decltype(P)::value == 0) return vs0;
+    else return vs1;
+  };
+  // Workgroup barrier.  Its release fence makes every LDS write of the
+  // wave visible first, the direct tile loads included (the compiler waits
+  // for all loads in flight), so a tile issued in a period has landed when
+  // that period ends.  Letting the loads stay in flight across the barrier
+  // (a bare s_barrier with explicit waits for older tiles) measured slower.
+  auto bar = [] { __syncthreads(); };
 
   // ---- prologue part 1.  Global reads in the order they are needed (the
   // vector-memory counter retires them in order): per-tile K norms, the Q
@@ -224,11 +243,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         c4[s][e2] = f32x4{t.x, t.y, t.z, t.w};
       }
   }
-  // K(0), K(1) by waves 4-7, V(0) (twice) by waves 0-3: the same count on
-  // every path keeps the compiler's own waits for Q exact (past the last
-  // tile a harmless repeat of tile 0)
-  load_tile(grp ? ks[0] : vs[0], 0);
-  load_tile(grp ? ks[1] : vs[0], grp && n > 1 ? 1 : 0);
+  // K(0) by waves 4-7 (the first barrier publishes it)
+  if (grp) load_tile(ks0, 0);
 
   // ---- Q row: rotate at pos, round to bf16 (B operand layout: lane holds
   // dims s*16 + hl*8 + e of its row; RoPE pairs are (s, s + NS/2)); done
@@ -272,11 +288,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int kswz = (c32 / KRPB) % KCPR;       // same for key rows c32 and 32 + c32
   int kread[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) kread[s] = c32 * D + (((2 * s + hl) ^ kswz) * 8);
+  for (int s = 0; s < NS; ++s) kread[s] = (c32 * D + (((2 * s + hl) ^ kswz) * 8)) * 2;   // bytes
   const int vswz = (c32 / VRPB) % VCPR;       // same for dim rows db*32 + c32
   int vread[2];
 #pragma unroll
-  for (int hs = 0; hs < 2; ++hs) vread[hs] = c32 * TV + (((2 * hs + hl) ^ vswz) * 8);
+  for (int hs = 0; hs < 2; ++hs) vread[hs] = (c32 * TV + (((2 * hs + hl) ^ vswz) * 8)) * 2;
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -285,8 +301,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const f32x16 zero16 = {};
-  float zsh = 0.f;     // PRE: shift already subtracted from the scores
-  f32x16 negz = {};    // PRE: -zsh, the initial accumulator of S^T
   f32x16 sacc[2];     // scores of the tile between its matrix and vector phases
   bf16x8 pb[2][2];    // probabilities between the vector and the next matrix phase
 #pragma unroll
@@ -302,13 +316,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // j = (kb*2 + hs)*NDB + db; fragment NPV + 2s + c is K rows c*32.. at
   // k-step s.  All reads and MFMAs sit in one basic block; the scheduling
   // barriers issue the reads PF fragments ahead of their MFMAs.
-  auto read_v = [&](const uint16_t* vt0, int j) {
+  // Lane offsets are in bytes, so that slot base and fragment offset fold
+  // into the instruction's offset field.
+  auto read_v = [&](const uint16_t* vt0, const int (&vr)[2], int j) {
     const int kb = j / (2 * NDB), hs = (j / NDB) % 2, db = j % NDB;
-    return *(const bf16x8*)(vt0 + kb * D * TV + db * 32 * TV + vread[hs]);
+    return *(const bf16x8*)((const char*)vt0 + (kb * D * TV + db * 32 * TV) * 2 + vr[hs]);
   };
-  auto read_k = [&](const uint16_t* kt0, int j) {
+  auto read_k = [&](const uint16_t* kt0, const int (&kr)[NS], int j) {
     const int s = j / 2, c = j % 2;
-    return *(const bf16x8*)(kt0 + c * 32 * D + kread[s]);
+    return *(const bf16x8*)((const char*)kt0 + c * 32 * D * 2 + kr[s]);
   };
   auto mma_pv = [&](const bf16x8 a, int j) {
     const int kb = j / (2 * NDB), hs = (j / NDB) % 2, db = j % NDB;
@@ -317,17 +333,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   auto mma_qk = [&](const bf16x8 a, int j) {
     const int s = j / 2, c = j % 2;
     sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        a, qb[s], s == 0 ? (PRE ? negz : zero16) : sacc[c], 0, 0, 0);
+        a, qb[s], s == 0 ? zero16 : sacc[c], 0, 0, 0);
   };
-  // P.V of tile i-1 and S^T of tile i
-  auto matrix_full = [&](int i) {
-    const uint16_t* vt0 = vs[(i - 1) % 3];
-    const uint16_t* kt0 = ks[i % 3];
+  // P.V of tile i-1 and S^T of tile i (P = i mod 2)
+  auto matrix_full = [&](auto P) {
+    const uint16_t* vt0 = vslot(Slot<decltype(P)::value + 1>{});
+    const uint16_t* kt0 = kslot(P);
     bf16x8 fr[NR];
 #pragma unroll
-    for (int j = 0; j < NPV; ++j) fr[j] = read_v(vt0, j);
+    for (int j = 0; j < NPV; ++j) fr[j] = read_v(vt0, vread, j);
 #pragma unroll
-    for (int j = 0; j < NQK; ++j) fr[NPV + j] = read_k(kt0, j);
+    for (int j = 0; j < NQK; ++j) fr[NPV + j] = read_k(kt0, kread, j);
 #pragma unroll
     for (int j = 0; j < NPV; ++j) mma_pv(fr[j], j);
 #pragma unroll
@@ -342,20 +358,20 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);   // the MFMAs stay in this phase
   };
   // S^T of tile 0 only
-  auto matrix_qk = [&](int i) {
-    const uint16_t* kt0 = ks[i % 3];
+  auto matrix_qk = [&] {
+    const uint16_t* kt0 = ks0;
     bf16x8 fr[NQK];
 #pragma unroll
-    for (int j = 0; j < NQK; ++j) fr[j] = read_k(kt0, j);
+    for (int j = 0; j < NQK; ++j) fr[j] = read_k(kt0, kread, j);
 #pragma unroll
     for (int j = 0; j < NQK; ++j) mma_qk(fr[j], j);
   };
-  // P.V of the last tile only
+  // P.V of the last tile only (tile i - 1, slot (i - 1) mod 2)
   auto matrix_pv = [&](int i) {
-    const uint16_t* vt0 = vs[(i - 1) % 3];
+    const uint16_t* vt0 = (i - 1) % 2 == 0 ? vs0 : vs1;
     bf16x8 fr[NPV];
 #pragma unroll
-    for (int j = 0; j < NPV; ++j) fr[j] = read_v(vt0, j);
+    for (int j = 0; j < NPV; ++j) fr[j] = read_v(vt0, vread, j);
 #pragma unroll
     for (int j = 0; j < NPV; ++j) mma_pv(fr[j], j);
   };
@@ -370,13 +386,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
   };
-  auto probs = [&](const f32x16& s0, const f32x16& s1) {
+  // SH: the reference m of some row in the wave is not 0 (PRE only)
+  auto probs = [&](const f32x16& s0, const f32x16& s1, auto SH) {
     float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if constexpr (PRE) {
+      if constexpr (PRE && !decltype(SH)::value) {
         pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[e]);
         pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[e]);
+      } else if constexpr (PRE) {
+        pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[e] - m_run);
+        pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[e] - m_run);
       } else {
         pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[e], sl2, -m_run));
         pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[e], sl2, -m_run));
@@ -405,11 +425,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     // ALU reads the scores without copies)
     f32x16 s0 = sacc[0], s1 = sacc[1];
     if (masked(i)) {
+      // key of score e: i*TK + (e>>2)*8 + hl*4 + (e&3) (+32 for s1); compared
+      // as a constant offset against the row's limit within the tile
+      const int t = lim - i * TK - hl * 4;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = i * TK + (e >> 2) * 8 + hl * 4 + (e & 3);
-        if (key > lim) s0[e] = -INFINITY;
-        if (key + 32 > lim) s1[e] = -INFINITY;
+        const int c = (e >> 2) * 8 + (e & 3);
+        if (c > t) s0[e] = -INFINITY;
+        if (c + 32 > t) s1[e] = -INFINITY;
       }
     }
     // new reference: the owed raise (O and l already hold the tile that
@@ -419,24 +442,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-      mx = PRE ? max_xor32(mx) + zsh : max_xor32(mx) * sl2;
+      mx = PRE ? max_xor32(mx) : max_xor32(mx) * sl2;
       if (mx > m_new + kRescaleThreshold) m_new = mx;
     }
     if (__builtin_amdgcn_ballot_w64(m_new != m_run)) rescale(m_new);
-    if constexpr (PRE) {
-      if (__builtin_amdgcn_ballot_w64(m_new != zsh)) {   // new shift: this tile's
-        const float d = zsh - m_new;                      // scores, and the next
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s0[e] += d;
-          s1[e] += d;
-        }
-        zsh = m_new;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) negz[e] = -m_new;
-      }
-    }
-    const float psum = probs(s0, s1);
+    float psum;
+    if (PRE && __builtin_amdgcn_ballot_w64(m_run != 0.f))
+      psum = probs(s0, s1, std::true_type{});
+    else
+      psum = probs(s0, s1, std::false_type{});
     l_run += psum;
     // probabilities here are <= 2^64; a sum past 2^32 owes a raise of m by
     // its (integral) log2, taken at the next tile once P.V has added it
@@ -452,8 +466,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) km = wave_max_xor(km, m);
   if (lane == 0) wred[wave] = km;
-  if (grp) landed(true);   // K(0); K(1) may stay in flight
-  __syncthreads();
+  bar();
   rotate_q();
   {
     float km = wred[0];
@@ -461,49 +474,60 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     for (int w = 1; w < NW; ++w) km = fmaxf(km, wred[w]);
     crow = qcap * km;
   }
+  // a bound within the headroom makes 0 a valid reference from the start
+  // (every score lies in [-crow, crow]), which the scores need no shift for
+  if (crow <= kBoundHeadroom) m_run = 0.f;
 
   // ---- periods t = 0 .. 2 n_tiles + 1, each ending at a barrier.  Even
-  // period 2i: waves 0-3 run matrix phase i, waves 4-7 vector phase i-1 and
-  // issue K(i+2).  Odd period 2i+1: waves 0-3 run vector phase i and issue
-  // V(i+1), waves 4-7 matrix phase i.  Tiles live in three-slot rings
-  // (tile t in slot t % 3) and get two periods to land: the loading waves
-  // wait for K(i+1) and V(i) before the barrier that ends period 2i+1.
+  // period 2i: waves 0-3 run matrix phase i (V(i-1), K(i)), waves 4-7 vector
+  // phase i-1 and load K(i+1).  Odd period 2i+1: waves 0-3 run vector phase
+  // i and load V(i), waves 4-7 matrix phase i.  Tile t sits in slot t % 2; a
+  // load overwrites the tile read two periods before and has landed at the
+  // barrier that ends its period (past the last tile, waves 4-7 load the
+  // last K again, into the slot nobody reads any more).  The loop runs
+  // i = 1 .. n-1 unrolled by two, so every slot is static.
+  auto step0 = [&](auto P, int i) {        // waves 0-3, P = i mod 2
+    matrix_full(P);                        // period 2i
+    bar();
+    load_tile(vslot(P), i);                // period 2i+1
+    vector_phase(i);
+    bar();
+  };
+  auto step1 = [&](auto P, int i) {        // waves 4-7
+    load_tile(kslot(Slot<decltype(P)::value + 1>{}), min(i + 1, n - 1));   // period 2i
+    vector_phase(i - 1);
+    bar();
+    matrix_full(P);                        // period 2i+1
+    bar();
+  };
+  auto run = [&](auto step) {
+    int i = 1;
+    for (; i + 1 < n; i += 2) {
+      step(Slot<1>{}, i);
+      step(Slot<0>{}, i + 1);
+    }
+    if (i < n) step(Slot<1>{}, i);
+  };
   if (grp == 0) {
-    matrix_qk(0);                           // period 0
-    __syncthreads();
-    if (n > 1) load_tile(vs[1], 1);         // period 1
+    matrix_qk();                            // period 0
+    bar();
+    load_tile(vs0, 0);                      // period 1
     vector_phase(0);
-    landed(n > 1);
-    __syncthreads();
-    for (int i = 1; i < n; ++i) {
-      matrix_full(i);                       // period 2i
-      __syncthreads();
-      if (i + 1 < n) load_tile(vs[(i + 1) % 3], i + 1);   // period 2i+1
-      vector_phase(i);
-      landed(i + 1 < n);
-      __syncthreads();
-    }
+    bar();
+    run(step0);
     matrix_pv(n);                           // period 2n
-    __syncthreads();
-    __syncthreads();                        // period 2n+1
+    bar();
+    bar();                                  // period 2n+1
   } else {
-    if (n > 2) load_tile(ks[2], 2);         // period 0
-    __syncthreads();
-    matrix_qk(0);                           // period 1
-    landed(n > 2);
-    __syncthreads();
-    for (int i = 1; i < n; ++i) {
-      if (i + 2 < n) load_tile(ks[(i + 2) % 3], i + 2);   // period 2i
-      vector_phase(i - 1);
-      __syncthreads();
-      matrix_full(i);                       // period 2i+1
-      landed(i + 2 < n);
-      __syncthreads();
-    }
+    load_tile(ks1, min(1, n - 1));          // period 0
+    bar();
+    matrix_qk();                            // period 1
+    bar();
+    run(step1);
     vector_phase(n - 1);                    // period 2n
-    __syncthreads();
+    bar();
     matrix_pv(n);                           // period 2n+1
-    __syncthreads();
+    bar();
   }
 
   // ---- epilogue: O = O / l; lane holds dims db*32 + gq*8 + hl*4 + (0..3)

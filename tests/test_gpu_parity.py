@@ -18,8 +18,8 @@ import torch
 
 import oracle
 import rope_causal_grouped_amd as gqa
-from synthetic import (WORKLOADS, Workload, gen_decode_cache_b, gen_decode_query,
-                       gen_prefill, scaled_rows)
+from synthetic import (WORKLOADS, Workload, bf16_round, gen_decode_cache_b,
+                       gen_decode_query, gen_prefill, scaled_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -107,6 +107,58 @@ def test_prefill_bf16_small(shape):
     o = gqa.prefill(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16))
     torch.cuda.synchronize()
     assert_parity(host(o), oracle.prefill(q, k, v), torch.bfloat16, f"prefill bf16 {shape}")
+
+
+def attend_rounded_operands(q, k, v):
+    """The oracle's attention on the operands the bf16 matrix cores see: the
+    rotated Q times scale*log2(e) and the rotated K, each rounded to bf16
+    (scores then in log2 units, hence softmax scale ln 2)."""
+    B, L, h_q, d = q.shape
+    h_kv = k.shape[2]
+    pos = np.arange(L)
+    sl2 = math.log2(math.e) / math.sqrt(d)
+    qb = bf16_round((oracle.rope(q, pos) * sl2).astype(np.float32)).astype(np.float64)
+    kb = bf16_round(oracle.rope(k, pos).astype(np.float32)).astype(np.float64)
+    vis = oracle.visible(pos, pos)
+    out = np.empty((B, L, h_q, d))
+    for b in range(B):
+        for t in range(h_q):
+            u = oracle.kv_group(t, h_q, h_kv)
+            out[b, :, t] = oracle.attend(qb[b, :, t], kb[b, :, u], v[b, :, u], math.log(2), vis)
+    return out
+
+
+@pytest.mark.parametrize("sigma,boosted", [(3.0, 0), (0.5, 24)], ids=["sigma3", "boosted"])
+@pytest.mark.parametrize("shape", [(1, 333, 28, 4, 128), (2, 300, 14, 2, 64)],
+                         ids=lambda s: "B%d_L%d_%d/%d_d%d" % s)
+def test_prefill_bf16_large_scores(shape, sigma, boosted):
+    """Score bounds past the 64 (log2) headroom: the kernel takes tile maxima
+    first and shifts the scores by a nonzero reference.  With boosted rows
+    (x8) only some rows of a wave need the shift, the rest keep m = 0.
+
+    Rounding the rotated Q and K to bf16 perturbs a score by about 2^-9 of
+    its size, so at logits of 70 (sigma 3) the output moves by up to ~0.1
+    from the exact result whatever the softmax does: the relative-L2 bar is
+    checked against the oracle, the max-abs bar against the oracle's
+    attention on those rounded operands (where a one-ulp difference in an
+    operand still moves a weight by a few percent; V is kept at unit scale
+    so that this stays inside the bar)."""
+    B, L, h_q, h_kv, d = shape
+    note(f"prefill bf16 large scores {shape} sigma={sigma} boosted={boosted}")
+    w = Workload("t", "test", "prefill", B, L, h_q, h_kv, d, "bf16", 300 + L, sigma,
+                 boosted_rows=boosted)
+    q, k, v = gen_prefill(w)
+    v = bf16_round(v / np.float32(sigma))   # large scores, unit-scale values
+    o = gqa.prefill(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16))
+    torch.cuda.synchronize()
+    got = host(o)
+    want = oracle.prefill(q, k, v)
+    assert np.all(np.isfinite(got))
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    note(f"  vs oracle: max-abs {np.abs(got - want).max():.3e} rel-L2 {rel:.3e}")
+    assert rel <= TOL_BF16_REL
+    assert_parity(got, attend_rounded_operands(q, k, v), torch.bfloat16,
+                  f"prefill bf16 {shape} sigma={sigma} boosted={boosted} (rounded operands)")
 
 
 def test_prefill_bf16_noncausal_and_bf16_out():
