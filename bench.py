@@ -106,6 +106,32 @@ def cpu_baseline(w):
                       f"{w.name}; {flops / 1e9:.1f} causal GFLOP in {dt:.2f} s (fp64 NumPy)"}
 
 
+def measure_context(torch, gqa, dev):
+    """HBM context figures for the HBM-bound rooflines: the library's plain
+    streaming-read kernel over 2 GiB, and a 1 GiB framework device copy."""
+    res = {}
+    x = torch.ones(2**30, dtype=torch.bfloat16, device=dev)           # 2 GiB
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    a = torch.ones(2**28, dtype=torch.float32, device=dev)            # 1 GiB
+    b = torch.empty_like(a)
+    for name, fn, nbytes in (("read", lambda: gqa.stream_read(x, sink), 2**31),
+                             ("copy", lambda: b.copy_(a), 2 * 2**30)):
+        for _ in range(10):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_GBps"] = nbytes / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e9
+    res["kernels"] = ("read: gqa_stream_read over 2 GiB, 16-byte non-temporal loads (bytes "
+                      "read); copy: torch copy_ of 1 GiB fp32 (bytes read + written)")
+    del x, sink, a, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
     """Chunked prefill and appending decode on the prefill / decode shapes
     (``pre``/``dec``: the step's resident inputs, reused when present)."""
@@ -431,6 +457,10 @@ def main():
             out["config"] = {"workload": nx["workload"], "global_batch": wp.B,
                              "seq_len": wp.L, "parallelism": "single-gpu"}
             out["roofline"] = nx["roofline"]
+    if run_p and run_d:
+        out["context"] = measure_context(torch, gqa, dev)
+        log(f"[bench] context: read {out['context']['read_GBps']:.0f} GB/s, "
+            f"copy {out['context']['copy_GBps']:.0f} GB/s")
     if run_p and not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wp)

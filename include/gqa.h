@@ -273,6 +273,16 @@ const char* gqa_version(void);
 int gqa_timing_enable(int on);
 int gqa_timing_read(int which, double* total_ms, int64_t* count);
 
+/*
+ * Streaming-read helper for benchmarks (not part of the attention path): a
+ * plain kernel reads `bytes` at device pointer p once, 16 bytes per lane
+ * with non-temporal loads, on `stream`, and may write 4 bytes to the device
+ * pointer `sink`.  Its rate is the context for the HBM-bound kernels'
+ * roofline figures.  p must be 16-byte aligned and bytes a positive
+ * multiple of 16 (else GQA_ERR_INVALID_ARG).  Asynchronous.
+ */
+int gqa_stream_read(const void* p, size_t bytes, void* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

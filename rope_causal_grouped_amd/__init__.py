@@ -19,7 +19,7 @@ from ._lib import (GQA_BF16, GQA_F32, GQAError, check, lib)
 __all__ = ["rope_apply", "prefill", "decode", "prefill_chunk", "decode_ragged",
            "decode_append", "qkv_epilogue", "decode_paged", "decode_paged_workspace_size",
            "set_rope_yarn", "prefill_workspace_size", "prefill_chunk_workspace_size",
-           "decode_workspace_size", "timing_enable", "timing_read", "version",
+           "decode_workspace_size", "timing_enable", "timing_read", "stream_read", "version",
            "GQAError", "ROPE_THETA"]
 
 ROPE_THETA = 1.0e6
@@ -336,3 +336,13 @@ def timing_read(which: int):
     n = ctypes.c_int64()
     check(lib().gqa_timing_read(which, ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def stream_read(x: torch.Tensor, sink: torch.Tensor) -> None:
+    """Benchmark helper: read all of the contiguous device tensor x once
+    (16-byte non-temporal loads) on the current stream; sink is a device
+    tensor of at least 4 bytes."""
+    if not (x.is_cuda and sink.is_cuda and x.is_contiguous()) or sink.numel() * sink.element_size() < 4:
+        raise ValueError("stream_read: contiguous device tensor and a device sink of >= 4 bytes")
+    check(lib().gqa_stream_read(x.data_ptr(), x.numel() * x.element_size(), sink.data_ptr(),
+                                torch.cuda.current_stream(x.device).cuda_stream))

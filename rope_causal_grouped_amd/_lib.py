@@ -46,6 +46,7 @@ SIGNATURES = {
     "gqa_version": (ctypes.c_char_p, []),
     "gqa_timing_enable": (_I, [_I]),
     "gqa_timing_read": (_I, [_I, ctypes.POINTER(_D), ctypes.POINTER(_I64)]),
+    "gqa_stream_read": (_I, [_P, _SZ, _P, _P]),
 }
 
 _lib = None

@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
 
-SOURCES = ["api.cpp", "rope.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+SOURCES = ["api.cpp", "rope.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip",
+           "measure.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -607,4 +607,12 @@ int gqa_timing_read(int which, double* total_ms, int64_t* count) {
   return GQA_OK;
 }
 
+int gqa_stream_read(const void* p, size_t bytes, void* sink, hipStream_t stream) {
+  g_err.clear();
+  if (!p || !sink || bytes == 0 || bytes % 16 != 0 || (uintptr_t)p % 16 != 0)
+    return fail(GQA_ERR_INVALID_ARG, "stream_read: need a 16-byte aligned buffer and a size that is a positive multiple of 16");
+  const hipError_t e = gqa::launch_stream_read(p, bytes, (unsigned*)sink, stream);
+  return e == hipSuccess ? GQA_OK : hip_fail(e, "stream_read launch");
+}
+
 }  // extern "C"

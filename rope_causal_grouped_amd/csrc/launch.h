@@ -73,4 +73,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
                          float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end);
 
+// streaming read of `bytes` (a multiple of 16) at p, for benchmark context
+hipError_t launch_stream_read(const void* p, size_t bytes, unsigned* sink, hipStream_t st);
+
 }  // namespace gqa

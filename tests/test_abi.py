@@ -96,6 +96,16 @@ def test_decode_rejects(lib, kw, code):
     assert lib.gqa_last_error()
 
 
+def test_stream_read_rejects(lib):
+    bad = _lib.GQA_ERR_INVALID_ARG
+    assert lib.gqa_stream_read(None, 16, FAKE, None) == bad
+    assert lib.gqa_stream_read(FAKE, 16, None, None) == bad
+    assert lib.gqa_stream_read(FAKE, 0, FAKE, None) == bad
+    assert lib.gqa_stream_read(FAKE, 24, FAKE, None) == bad
+    assert lib.gqa_stream_read(FAKE + 8, 16, FAKE, None) == bad
+    assert lib.gqa_last_error()
+
+
 def test_rope_rejects(lib):
     assert lib.gqa_rope_apply(None, 1, 1, 4, 2, 64, 0, 1e6, None) == _lib.GQA_ERR_INVALID_ARG
     assert lib.gqa_rope_apply(FAKE, 1, 1, 4, 2, 63, 0, 1e6, None) == _lib.GQA_ERR_INVALID_ARG

@@ -292,3 +292,13 @@ def test_decode_workload():
         kb, vb = host_cache[b]
         want = oracle.decode(qh[b:b + 1], kb[None], vb[None], w.L, w.q_pos)[0]
         assert_parity(host(o[b]), want, torch.bfloat16, f"c3 batch {b}")
+
+
+def test_stream_read_runs():
+    """The benchmark's streaming-read helper reads a buffer and leaves the
+    sink alone for data whose XOR is not its marker value."""
+    x = torch.ones(1 << 20, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    gqa.stream_read(x, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
