@@ -14,7 +14,9 @@ holds the first 3072 rows, one gqa_decode_append step for 32 sequences at
 ragged positions 32767 - 256 b of a 32768-row cache, gqa_decode_paged on
 the decode workload's cache cut into 16-position pages under a shuffled
 block table, and gqa_qkv_epilogue over the packed projection output of the
-prefill workload's 4 x 4096 tokens.
+prefill workload's 4 x 4096 tokens.  The same gqa_prefill call is then timed
+on the two larger prefill workloads (72B heads at L 8192; 7B heads at
+L 32768) under "other_prefill", and the HBM context figures under "context".
 `value` is the prefill rate in TFLOP/s over the causal pairs only
 (4 * B * h_q * d * L(L+1)/2 flop per call) measured around the whole call;
 the decode rate (K/V cache bytes read once per KV group / call time) is
@@ -129,6 +131,50 @@ def measure_context(torch, gqa, dev):
                       "read); copy: torch copy_ of 1 GiB fp32 (bytes read + written)")
     del x, sink, a, b
     torch.cuda.empty_cache()
+    return res
+
+
+def measure_other_prefills(torch, gqa, dev, keys=("c4", "c5"), warmup=10, reps=20):
+    """The same gqa_prefill call on the larger prefill workloads (72B heads
+    at L 8192; 7B heads at L 32768 with boosted rows), for the scaling of
+    the attention kernel with L.  Outside the timed step."""
+    from synthetic import WORKLOADS, gen_prefill
+    res = {}
+    for key in keys:
+        w = WORKLOADS[key]
+        log(f"[bench] generating {w.name}")
+        q, k, v = gen_prefill(w)
+        qd, kd, vd = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in (q, k, v))
+        del q, k, v
+        od = torch.empty((w.B, w.L, w.h_q, w.d), dtype=torch.float32, device=dev)
+        ws = torch.empty(gqa.prefill_workspace_size(torch.bfloat16, w.B, w.L, w.h_kv, w.d),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(warmup):
+            gqa.prefill(qd, kd, vd, out=od, workspace=ws)
+        torch.cuda.synchronize()
+        gqa.timing_read(0)
+        gqa.timing_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gqa.prefill(qd, kd, vd, out=od, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        gqa.timing_enable(False)
+        call_ms = e0.elapsed_time(e1) / reps
+        attn_ms, attn_n = gqa.timing_read(0)
+        kern_ms = attn_ms / max(attn_n, 1)
+        flops = w.prefill_flops()
+        ach = flops / (kern_ms * 1e-3) / 1e12
+        res[key] = {"workload": f"{w.name}: B{w.B} L{w.L} h_q{w.h_q} h_kv{w.h_kv} d{w.d} bf16 in / fp32 out",
+                    "value": flops / (call_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "call_ms": call_ms,
+                    "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": ach,
+                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": ach / PEAK_BF16_TFLOPS, "kernel_ms": kern_ms,
+                                 "traffic": None}}
+        log(f"[bench] {key}: attention {kern_ms:.3f} ms -> {ach:.0f} TFLOP/s")
+        del qd, kd, vd, od, ws
+        torch.cuda.empty_cache()
     return res
 
 
@@ -458,6 +504,7 @@ def main():
                              "seq_len": wp.L, "parallelism": "single-gpu"}
             out["roofline"] = nx["roofline"]
     if run_p and run_d:
+        out["other_prefill"] = measure_other_prefills(torch, gqa, dev)
         out["context"] = measure_context(torch, gqa, dev)
         log(f"[bench] context: read {out['context']['read_GBps']:.0f} GB/s, "
             f"copy {out['context']['copy_GBps']:.0f} GB/s")

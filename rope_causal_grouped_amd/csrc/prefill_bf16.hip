@@ -94,7 +94,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
     const float2* __restrict__ cs, void* __restrict__ o, int L, int Lpad, int h_q, int h_kv,
-    int g, int n_rb, float sl2, int causal, const int64_t* __restrict__ qstart,
+    int g, int n_rb, int n_bu, float sl2, int causal, const int64_t* __restrict__ qstart,
     const int64_t* __restrict__ qlen, int kend) {
   constexpr int NS = D / 16;                  // 16-dim k-steps of S^T
   constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
@@ -123,18 +123,29 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int grp = wave >> 2;                  // 0: matrix phase first; 1: vector phase first
   const int hl = lane >> 5, c32 = lane & 31;
 
-  // Work item w = bu * n_rb + (n_rb - 1 - rb).  Workgroups are dispatched
-  // to the eight XCDs round-robin by id, and each XCD has its own L2, so the
-  // ids that land on one XCD get one contiguous range of work items: an XCD
-  // works through the row blocks of one (b, u) at a time and the K/V of
-  // that group stays in its L2.  Within a (b, u), the heaviest row blocks
-  // (latest positions, most keys) go first.
-  const int nwg = (int)gridDim.x;
+  // Work items: row block rb of group bu = (b, u).  Workgroups are
+  // dispatched to the eight XCDs round-robin by id, and each XCD has its own
+  // L2.  Each group is cut into s strided parts, s = 8 / gcd(groups, 8), so
+  // that the parts divide evenly among the XCDs: part r holds row blocks
+  // n_rb-1-r, n_rb-1-r-s, ...  XCD x works through parts x*ppx ..
+  // (x+1)*ppx-1 in turn: few groups at a time (their K/V stay in its L2),
+  // the same share of the work on every XCD (causal row blocks differ in
+  // cost), and within a part the heaviest row blocks (latest positions,
+  // most keys) first.  Ids past an XCD's items exit at once.
   const int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
-  const int per = nwg / kXcds, extra = nwg % kXcds;
-  const int w = xcd * per + min(xcd, extra) + j;
-  const int bu = w / n_rb;
-  const int rb = n_rb - 1 - (w - bu * n_rb);
+  const int low = n_bu & -n_bu;               // largest power of two dividing n_bu
+  const int s_parts = low >= kXcds ? 1 : kXcds / low;
+  const int ppx = n_bu * s_parts / kXcds;     // parts per XCD
+  int part = xcd * ppx, jj = j;
+  for (int t = 0; t < ppx; ++t) {
+    const int cnt = (n_rb - part % s_parts + s_parts - 1) / s_parts;
+    if (jj < cnt) break;
+    jj -= cnt;
+    ++part;
+  }
+  if (part >= (xcd + 1) * ppx) return;
+  const int bu = part / s_parts;
+  const int rb = n_rb - 1 - part % s_parts - s_parts * jj;
   const int b = bu / h_kv, u = bu % h_kv;
   const int R0 = rb * ROWS;
 
@@ -563,11 +574,16 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   const int n_rb = (int)((L * g + kPrefillRowsWG - 1) / kPrefillRowsWG);
   const int n_bu = (int)(B * h_kv);
   const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e): exp(x) = exp2(x log2 e)
-  const unsigned grid = (unsigned)((int64_t)n_rb * n_bu);
+  // XCD-balanced work order (see the kernel): s strided parts per group
+  const int low = n_bu & -n_bu;
+  const int s_parts = low >= kXcds ? 1 : kXcds / low;
+  const int ppx = n_bu * s_parts / kXcds;
+  const unsigned grid = (unsigned)((int64_t)kXcds * ppx * ((n_rb + s_parts - 1) / s_parts));
 #define GQA_LAUNCH(DD, OB, PR)                                                               \
   prefill_bf16_kernel<DD, OB, PR><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, cs, o, (int)L,  \
                                                             (int)Lpad, h_q, h_kv, g, n_rb,   \
-                                                            sl2, causal, qstart, qlen, (int)kend)
+                                                            n_bu, sl2, causal, qstart, qlen, \
+                                                            (int)kend)
 #define GQA_LAUNCH_D(DD, OB) \
   do { if (cs) GQA_LAUNCH(DD, OB, true); else GQA_LAUNCH(DD, OB, false); } while (0)
   if (d == 128) {
