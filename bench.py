@@ -50,9 +50,9 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
 # device copy: FETCH x 2.00, WRITE x 1.00).  Each figure is valid only for the
 # kernel source it was measured on (sha256 prefix); otherwise it reports null.
 TRAFFIC = {
-    "prefill": ("prefill_bf16.hip", "8951d03b3412e134", (117362.6 * 2.0 + 249418.7) * 1024),
+    "prefill": ("prefill_bf16.hip", "a39c81251f7e97a7", (117359.6 * 2.0 + 249996.4) * 1024),
     "decode": ("decode.hip", "55c3dd751eae0bac", (1058368.0 * 2.0 + 14784.1) * 1024),
-    "prefill_chunk": ("prefill_bf16.hip", "8951d03b3412e134", (44219.3 * 2.0 + 61472.8) * 1024),
+    "prefill_chunk": ("prefill_bf16.hip", "a39c81251f7e97a7", (44209.8 * 2.0 + 61692.1) * 1024),
     "decode_append": ("decode.hip", "55c3dd751eae0bac", (928761.8 * 2.0 + 14784.1) * 1024),
     "decode_paged": ("decode.hip", "55c3dd751eae0bac", (1054822.1 * 2.0 + 14784.1) * 1024),
     "qkv_epilogue": ("rope.hip", "72eefc0ef755f754", (73831.7 * 2.0 + 147459.8) * 1024),
