@@ -96,6 +96,9 @@ SMALL_BF16 = [
     (3, 64, 12, 2, 128),     # exactly one tile, g = 6 (1.5B ratio)
     (1, 65, 28, 4, 64),
     (1, 70, 40, 2, 128),     # g = 20 > 16
+    (3, 100, 4, 1, 128),     # 3 (batch, group) units: each cut into 8 strided parts
+    (5, 600, 12, 1, 64),     # 5 units, ragged part sizes across the XCDs
+    (3, 700, 16, 4, 128),    # 12 units: halves of groups per XCD
 ]
 
 
