@@ -15,8 +15,9 @@ ragged positions 32767 - 256 b of a 32768-row cache, gqa_decode_paged on
 the decode workload's cache cut into 16-position pages under a shuffled
 block table, and gqa_qkv_epilogue over the packed projection output of the
 prefill workload's 4 x 4096 tokens.  The same gqa_prefill call is then timed
-on the two larger prefill workloads (72B heads at L 8192; 7B heads at
-L 32768) under "other_prefill", and the HBM context figures under "context".
+on the other prefill workloads (72B heads at L 8192; 7B heads at L 32768;
+the small fp32 0.5B case as a latency) under "other_prefill", and the HBM
+context figures under "context".
 `value` is the prefill rate in TFLOP/s over the causal pairs only
 (4 * B * h_q * d * L(L+1)/2 flop per call) measured around the whole call;
 the decode rate (K/V cache bytes read once per KV group / call time) is
@@ -134,20 +135,23 @@ def measure_context(torch, gqa, dev):
     return res
 
 
-def measure_other_prefills(torch, gqa, dev, keys=("c4", "c5"), warmup=10, reps=20):
-    """The same gqa_prefill call on the larger prefill workloads (72B heads
-    at L 8192; 7B heads at L 32768 with boosted rows), for the scaling of
-    the attention kernel with L.  Outside the timed step."""
+def measure_other_prefills(torch, gqa, dev, keys=("c1", "c4", "c5"), warmup=10, reps=20):
+    """The same gqa_prefill call on the other prefill workloads, outside the
+    timed step: the larger ones (72B heads at L 8192; 7B heads at L 32768
+    with boosted rows), for the scaling of the attention kernel with L, and
+    the small fp32 one (0.5B heads, L 128), whose 29.6 MFLOP make it a
+    latency figure (no roofline)."""
     from synthetic import WORKLOADS, gen_prefill
     res = {}
     for key in keys:
         w = WORKLOADS[key]
         log(f"[bench] generating {w.name}")
         q, k, v = gen_prefill(w)
-        qd, kd, vd = (torch.from_numpy(x).to(dev, torch.bfloat16) for x in (q, k, v))
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        qd, kd, vd = (torch.from_numpy(x).to(dev, dt) for x in (q, k, v))
         del q, k, v
         od = torch.empty((w.B, w.L, w.h_q, w.d), dtype=torch.float32, device=dev)
-        ws = torch.empty(gqa.prefill_workspace_size(torch.bfloat16, w.B, w.L, w.h_kv, w.d),
+        ws = torch.empty(gqa.prefill_workspace_size(dt, w.B, w.L, w.h_kv, w.d),
                          dtype=torch.uint8, device=dev)
         for _ in range(warmup):
             gqa.prefill(qd, kd, vd, out=od, workspace=ws)
@@ -166,6 +170,13 @@ def measure_other_prefills(torch, gqa, dev, keys=("c4", "c5"), warmup=10, reps=2
         kern_ms = attn_ms / max(attn_n, 1)
         flops = w.prefill_flops()
         ach = flops / (kern_ms * 1e-3) / 1e12
+        if w.dtype != "bf16":
+            res[key] = {"workload": f"{w.name}: B{w.B} L{w.L} h_q{w.h_q} h_kv{w.h_kv} d{w.d} fp32",
+                        "call_us": call_ms * 1e3, "kernel_us": kern_ms * 1e3,
+                        "note": f"latency figure ({flops / 1e6:.1f} MFLOP); no roofline"}
+            log(f"[bench] {key}: call {call_ms * 1e3:.1f} us, attention {kern_ms * 1e3:.1f} us")
+            del qd, kd, vd, od, ws
+            continue
         res[key] = {"workload": f"{w.name}: B{w.B} L{w.L} h_q{w.h_q} h_kv{w.h_kv} d{w.d} bf16 in / fp32 out",
                     "value": flops / (call_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "call_ms": call_ms,
                     "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": ach,

@@ -19,6 +19,16 @@
 
 namespace gqa {
 
+namespace {
+
+// value of the lane CTRL names within the quad (DPP quad permute)
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+}  // namespace
+
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ v,
@@ -27,8 +37,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const int64_t* __restrict__ qlen, int kend) {
   constexpr int TK = 64;
   constexpr int E = D / 8;  // pair count per lane
-  __shared__ float ks[TK][D + 4];
-  __shared__ float vs[TK][D + 4];
+  __shared__ __attribute__((aligned(16))) float ks[TK][D + 4];
+  __shared__ __attribute__((aligned(16))) float vs[TK][D + 4];
 
   const int pbk = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int u = t / g;
@@ -77,7 +87,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   float acc[2 * E];
 #pragma unroll
   for (int e = 0; e < 2 * E; ++e) acc[e] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;   // running max in log2 units, sum
+  const float sl2 = scale * 1.4426950408889634f;   // scale * log2(e)
 
   const int last_row_pos = qs + min(nq - 1, pbk * TK + TK - 1);
   const int n_keys = causal ? last_row_pos + 1 : L;
@@ -85,43 +96,69 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   const float* vbase = v + (int64_t)b * vs_.batch + (int64_t)u * vs_.head;
 
   for (int k0 = 0; k0 < n_keys; k0 += TK) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < TK * D; idx += 256) {
-      const int kk = idx / D, dd = idx % D;
+    // stage the tile: every 16-byte load issued before the first store
+    constexpr int C4 = TK * D / 4 / 256;   // float4 loads per thread and array
+    float4 kv4[C4], vv4[C4];
+#pragma unroll
+    for (int r = 0; r < C4; ++r) {
+      const int idx = threadIdx.x + r * 256;
+      const int kk = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
       const int key = k0 + kk;
-      float kv = 0.f, vv = 0.f;
+      kv4[r] = vv4[r] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (key < nk) {
-        kv = kbase[(int64_t)key * ks_.row + dd];
-        vv = vbase[(int64_t)key * vs_.row + dd];
+        kv4[r] = *(const float4*)(kbase + (int64_t)key * ks_.row + d4);
+        vv4[r] = *(const float4*)(vbase + (int64_t)key * vs_.row + d4);
       }
-      ks[kk][dd] = kv;
-      vs[kk][dd] = vv;
     }
     __syncthreads();
-    const int ntile = min(TK, n_keys - k0);
-    for (int jj = 0; jj < ntile; ++jj) {
-      float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        dot = fmaf(qr[e], ks[jj][part * E + e], dot);
-        dot = fmaf(qr[E + e], ks[jj][D / 2 + part * E + e], dot);
-      }
-      dot += __shfl_xor(dot, 1, 64);
-      dot += __shfl_xor(dot, 2, 64);
-      const int key = k0 + jj;
-      if (!causal || key <= pos) {
-        const float s = dot * scale;
-        const float m_new = fmaxf(m, s);
-        const float alpha = expf(m - m_new);
-        const float p = expf(s - m_new);
-        l = fmaf(l, alpha, p);
+    for (int r = 0; r < C4; ++r) {
+      const int idx = threadIdx.x + r * 256;
+      const int kk = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+      *(float4*)&ks[kk][d4] = kv4[r];
+      *(float4*)&vs[kk][d4] = vv4[r];
+    }
+    __syncthreads();
+    // four keys per step: their dot products are independent, the quad
+    // sums use DPP lane swaps (no LDS round trip), scores are in log2 units
+    // with the hardware exp2 (~1 ulp), and O is rescaled once per step
+    const int ntile = min(TK, n_keys - k0);
+    for (int jj = 0; jj < ntile; jj += 4) {
+      float sv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float d0 = 0.f, d1 = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          acc[e] = fmaf(acc[e], alpha, p * vs[jj][part * E + e]);
-          acc[E + e] = fmaf(acc[E + e], alpha, p * vs[jj][D / 2 + part * E + e]);
+          d0 = fmaf(qr[e], ks[jj + k][part * E + e], d0);
+          d1 = fmaf(qr[E + e], ks[jj + k][D / 2 + part * E + e], d1);
         }
-        m = m_new;
+        float dot = d0 + d1;
+        dot += quad_swap<0xB1>(dot);   // lanes 0<->1, 2<->3
+        dot += quad_swap<0x4E>(dot);   // lanes 0<->2, 1<->3
+        const int key = k0 + jj + k;
+        sv[k] = (jj + k < ntile && (!causal || key <= pos)) ? dot * sl2 : -INFINITY;
       }
+      const float m_new = fmaxf(fmaxf(m, fmaxf(sv[0], sv[1])), fmaxf(sv[2], sv[3]));
+      const float mref = m_new == -INFINITY ? 0.f : m_new;   // no visible key yet
+      const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      float p[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p[k] = __builtin_amdgcn_exp2f(sv[k] - mref);
+      l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j1 = part * E + e, j2 = D / 2 + part * E + e;
+        float a1 = acc[e] * alpha, a2 = acc[E + e] * alpha;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a1 = fmaf(p[k], vs[jj + k][j1], a1);
+          a2 = fmaf(p[k], vs[jj + k][j2], a2);
+        }
+        acc[e] = a1;
+        acc[E + e] = a2;
+      }
+      m = m_new;
     }
   }
 
