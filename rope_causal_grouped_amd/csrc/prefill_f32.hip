@@ -8,8 +8,8 @@
 // one query head; four lanes share a row, each holding a quarter of its dims
 // (dims j and j + d/2 of a RoPE pair stay in one lane).  K' (rotated by the
 // preparation pass) and V tiles of 64 keys are staged in LDS and shared by
-// the 64 rows; the softmax is updated key by key.  Keys and values are read
-// through strides, so they may come from the preparation pass (rotated K,
+// the 64 rows; the softmax is updated four keys at a time.  Keys and values
+// are read through strides, so they may come from the preparation pass (rotated K,
 // [B][h_kv][L][d]) and the call's V, or straight from a per-layer cache
 // [B, cap, h_kv, d] when a chunk of queries at positions qstart[b] + i
 // attends to everything cached so far.
