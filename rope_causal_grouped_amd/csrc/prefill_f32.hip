@@ -4,11 +4,15 @@
 // head size 64).
 //
 // Same operation as the bf16 kernel (Qwen2 technical-report walkthrough,
-// aicoding.csdn.net, §4.1.3 steps 3-4).  A workgroup owns 64 positions of
+// aicoding.csdn.net, §4.1.3 steps 3-4).  A workgroup owns 16 positions of
 // one query head; four lanes share a row, each holding a quarter of its dims
 // (dims j and j + d/2 of a RoPE pair stay in one lane).  K' (rotated by the
-// preparation pass) and V tiles of 64 keys are staged in LDS and shared by
-// the 64 rows; the softmax is updated four keys at a time.  Keys and values
+// preparation pass) and V tiles of 64 keys are staged in LDS; each of the
+// four waves holds all 16 rows and takes a quarter of every tile's keys,
+// updating its own online softmax four keys at a time, and the quarters are
+// merged exactly at the end.  The small shapes this serves are latency-
+// bound, so the split buys parallelism: four times the workgroups of a
+// 64-row layout, and a quarter of the serial key chain per wave.  Keys and values
 // are read through strides, so they may come from the preparation pass (rotated K,
 // [B][h_kv][L][d]) and the call's V, or straight from a per-layer cache
 // [B, cap, h_kv, d] when a chunk of queries at positions qstart[b] + i
@@ -35,22 +39,26 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float2* __restrict__ cs, void* __restrict__ o, int L, int h_q, int h_kv, int g,
     float scale, int causal, KvStrides ks_, KvStrides vs_, const int64_t* __restrict__ qstart,
     const int64_t* __restrict__ qlen, int kend) {
-  constexpr int TK = 64;
-  constexpr int E = D / 8;  // pair count per lane
+  constexpr int TK = 64;                 // keys per staged tile
+  constexpr int RB = 16;                 // rows (positions) per workgroup
+  constexpr int KQ = TK / 4;             // keys of a tile per wave
+  constexpr int E = D / 8;               // pair count per lane
   __shared__ __attribute__((aligned(16))) float ks[TK][D + 4];
   __shared__ __attribute__((aligned(16))) float vs[TK][D + 4];
 
   const int pbk = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int u = t / g;
-  const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // key quarter
+  const int row = lane >> 2, part = lane & 3;
 
   // queries i < nq of sequence b at positions qs + i; keys 0 .. nk-1
   int qs = 0, nq = L;
   if (qstart) {
     const int64_t s0 = qstart[b], n = qlen ? qlen[b] : L;
     if (!(s0 >= 0 && n >= 0 && n <= L && s0 + n <= kend)) {   // out of range: NaN rows
-      const int pr = pbk * TK + row;
-      if (pr < L) {
+      const int pr = pbk * RB + row;
+      if (wave == 0 && pr < L) {
         const int64_t orow = ((int64_t)((int64_t)b * L + pr) * h_q + t) * D;
         for (int e = part; e < D; e += 4) {
           if constexpr (OUT_BF16) ((uint16_t*)o)[orow + e] = 0x7fc0u;
@@ -62,9 +70,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     qs = (int)s0;
     nq = (int)n;
   }
-  if (pbk * TK >= nq) return;
+  if (pbk * RB >= nq) return;
   const int nk = causal ? qs + nq : L;
-  const int pl_raw = pbk * TK + row;
+  const int pl_raw = pbk * RB + row;
   const bool valid = pl_raw < nq;
   const int pl = valid ? pl_raw : nq - 1;   // row of q / o
   const int pos = qs + pl;                  // its position
@@ -90,7 +98,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   float m = -INFINITY, l = 0.f;   // running max in log2 units, sum
   const float sl2 = scale * 1.4426950408889634f;   // scale * log2(e)
 
-  const int last_row_pos = qs + min(nq - 1, pbk * TK + TK - 1);
+  const int last_row_pos = qs + min(nq - 1, pbk * RB + RB - 1);
   const int n_keys = causal ? last_row_pos + 1 : L;
   const float* kbase = kp + (int64_t)b * ks_.batch + (int64_t)u * ks_.head;
   const float* vbase = v + (int64_t)b * vs_.batch + (int64_t)u * vs_.head;
@@ -119,11 +127,12 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
       *(float4*)&vs[kk][d4] = vv4[r];
     }
     __syncthreads();
-    // four keys per step: their dot products are independent, the quad
-    // sums use DPP lane swaps (no LDS round trip), scores are in log2 units
-    // with the hardware exp2 (~1 ulp), and O is rescaled once per step
+    // this wave's quarter of the tile, four keys per step: their dot
+    // products are independent, the quad sums use DPP lane swaps (no LDS
+    // round trip), scores are in log2 units with the hardware exp2 (~1
+    // ulp), and O is rescaled once per step
     const int ntile = min(TK, n_keys - k0);
-    for (int jj = 0; jj < ntile; jj += 4) {
+    for (int jj = wave * KQ; jj < min(wave * KQ + KQ, ntile); jj += 4) {
       float sv[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -162,20 +171,43 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
     }
   }
 
-  if (valid) {
-    const float inv = 1.0f / l;
-    const int64_t orow = ((int64_t)((int64_t)b * L + pl) * h_q + t) * D;
+  // merge the four key quarters (exact log-sum-exp combination): partial
+  // sums through LDS (the tile arrays, free once every wave is done), then
+  // wave 0 scales each quarter by 2^(m_w - M) and normalises
+  __syncthreads();
+  float* mb = &ks[0][0];   // [wave][element][lane]
+  float* ml = &vs[0][0];   // [wave][m | l][lane]
+  static_assert(4 * 2 * E * 64 <= TK * (D + 4), "merge buffer exceeds the tile array");
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = part * E + e;
-      if constexpr (OUT_BF16) {
-        ((uint16_t*)o)[orow + j] = f32_to_bf16_bits(acc[e] * inv);
-        ((uint16_t*)o)[orow + j + D / 2] = f32_to_bf16_bits(acc[E + e] * inv);
-      } else {
-        ((float*)o)[orow + j] = acc[e] * inv;
-        ((float*)o)[orow + j + D / 2] = acc[E + e] * inv;
-      }
-    }
+  for (int e = 0; e < 2 * E; ++e) mb[(wave * 2 * E + e) * 64 + lane] = acc[e];
+  ml[wave * 128 + lane] = m;
+  ml[wave * 128 + 64 + lane] = l;
+  __syncthreads();
+  if (wave != 0 || !valid) return;
+  float mw[4], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = ml[w * 128 + lane];
+    M = fmaxf(M, mw[w]);
+  }
+  // every row sees at least one key (its own position when causal), so M is finite
+  float sc[4], lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    sc[w] = __builtin_amdgcn_exp2f(mw[w] - M);   // 0 for a quarter that saw no key
+    lsum = fmaf(ml[w * 128 + 64 + lane], sc[w], lsum);
+  }
+  const float inv = 1.0f / lsum;
+  const int64_t orow = ((int64_t)((int64_t)b * L + pl) * h_q + t) * D;
+#pragma unroll
+  for (int e = 0; e < 2 * E; ++e) {
+    float y = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) y = fmaf(mb[(w * 2 * E + e) * 64 + lane], sc[w], y);
+    y *= inv;
+    const int j = e < E ? part * E + e : D / 2 + part * E + (e - E);
+    if constexpr (OUT_BF16) ((uint16_t*)o)[orow + j] = f32_to_bf16_bits(y);
+    else ((float*)o)[orow + j] = y;
   }
 }
 
@@ -185,7 +217,7 @@ hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, c
                               const int64_t* qstart, const int64_t* qlen, int64_t kend,
                               hipStream_t st) {
   const int g = h_q / h_kv;
-  dim3 grid((unsigned)((L + 63) / 64), (unsigned)h_q, (unsigned)B);
+  dim3 grid((unsigned)((L + 15) / 16), (unsigned)h_q, (unsigned)B);
 #define GQA_LAUNCH(DD, OB)                                                                   \
   prefill_f32_kernel<DD, OB><<<grid, 256, 0, st>>>(q, kp, v, cs, o, (int)L, h_q, h_kv, g, scale, \
                                                    causal, ks, vs, qstart, qlen, (int)kend)
