@@ -176,17 +176,25 @@ def test_prefill_bf16_noncausal_and_bf16_out():
     assert_parity(host(ob), oracle.prefill(q, k, v), torch.bfloat16, "bf16 output")
 
 
-@pytest.mark.parametrize("shape", [(2, 77, 6, 2, 128), (1, 200, 14, 2, 64), (1, 5, 4, 4, 64)])
+@pytest.mark.parametrize("shape", [(2, 77, 6, 2, 128), (1, 200, 14, 2, 64), (1, 5, 4, 4, 64),
+                                   (1, 290, 8, 1, 128), (3, 17, 4, 2, 64)])
 def test_prefill_f32_small(shape):
+    """Causal and full attention, fp32 and bf16 output; the shapes cover one
+    to five key tiles with ragged tails, partial 16-position row blocks, and
+    rows whose later key quarters see no key."""
     B, L, h_q, h_kv, d = shape
     note(f"prefill f32 {shape}")
     q, k, v = small_case(B, L, h_q, h_kv, d, torch.float32, 200 + L)
     qd, kd, vd = (dev(x, torch.float32) for x in (q, k, v))
     o = gqa.prefill(qd, kd, vd)
     on = gqa.prefill(qd, kd, vd, causal=False)
+    ob = gqa.prefill(qd, kd, vd, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    assert_parity(host(o), oracle.prefill(q, k, v), torch.float32, f"prefill f32 {shape}")
+    want = oracle.prefill(q, k, v)
+    assert_parity(host(o), want, torch.float32, f"prefill f32 {shape}")
     assert_parity(host(on), oracle.prefill(q, k, v, causal=False), torch.float32, "non-causal")
+    assert ob.dtype == torch.bfloat16
+    assert_parity(host(ob), want, torch.bfloat16, "bf16 output")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
