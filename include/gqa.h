@@ -49,7 +49,10 @@ extern "C" {
 /* status codes */
 #define GQA_OK               0
 #define GQA_ERR_INVALID_ARG (-1)  /* bad pointer, size, ratio or range      */
-#define GQA_ERR_UNSUPPORTED (-2)  /* valid but not built (d, dtype combo)   */
+#define GQA_ERR_UNSUPPORTED (-2)  /* valid but not built: d not 64 or 128,
+                                     or sizes past the kernels' index range
+                                     (prefill: L or kend > 2^24, h_q or
+                                     B*h_kv > 65535)                       */
 #define GQA_ERR_WORKSPACE   (-3)  /* workspace missing or too small         */
 #define GQA_ERR_HIP         (-4)  /* the HIP runtime refused a launch       */
 

@@ -200,7 +200,8 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     return fail(GQA_ERR_INVALID_ARG, "k_cache and v_cache must both be set or both be NULL");
   if (k_cache && cap < L) return fail(GQA_ERR_INVALID_ARG, "cap=%lld < L=%lld", (long long)cap, (long long)L);
   const int g = h_q / h_kv;
-  if (L * g + gqa::kPrefillRowsWG > INT_MAX || B * h_kv > 65535 || L > (INT64_C(1) << 24))
+  if (L * g + gqa::kPrefillRowsWG > INT_MAX || B * h_kv > 65535 || h_q > 65535 ||
+      L > (INT64_C(1) << 24))
     return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
   const int64_t n_rb = (L * g + gqa::kPrefillRowsWG - 1) / gqa::kPrefillRowsWG;
   if (n_rb * B * h_kv > INT_MAX) return fail(GQA_ERR_UNSUPPORTED, "grid too large");
@@ -329,7 +330,8 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
     return fail(GQA_ERR_INVALID_ARG, "kend=%lld outside [1, cap=%lld]", (long long)kend,
                 (long long)cap);
   const int g = h_q / h_kv;
-  if (C * g + gqa::kPrefillRowsWG > INT_MAX || B * h_kv > 65535 || kend > (INT64_C(1) << 24))
+  if (C * g + gqa::kPrefillRowsWG > INT_MAX || B * h_kv > 65535 || h_q > 65535 ||
+      kend > (INT64_C(1) << 24))
     return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
   const int64_t n_rb = (C * g + gqa::kPrefillRowsWG - 1) / gqa::kPrefillRowsWG;
   if (n_rb * B * h_kv > INT_MAX) return fail(GQA_ERR_UNSUPPORTED, "grid too large");

@@ -58,6 +58,8 @@ def prefill_call(lib, **kw):
     (dict(d=96), _lib.GQA_ERR_UNSUPPORTED),
     (dict(B=0), _lib.GQA_ERR_INVALID_ARG),
     (dict(L=0), _lib.GQA_ERR_INVALID_ARG),
+    (dict(L=(1 << 24) + 1), _lib.GQA_ERR_UNSUPPORTED),     # beyond the kernels' index range
+    (dict(h_q=65536, h_kv=1), _lib.GQA_ERR_UNSUPPORTED),   # a grid dimension
     (dict(in_dt=7), _lib.GQA_ERR_INVALID_ARG),
     (dict(theta=float("nan")), _lib.GQA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), _lib.GQA_ERR_INVALID_ARG),
@@ -143,6 +145,7 @@ def chunk_call(lib, **kw):
     (dict(kend=0), _lib.GQA_ERR_INVALID_ARG),
     (dict(h_q=4, h_kv=28), _lib.GQA_ERR_INVALID_ARG),
     (dict(d=96), _lib.GQA_ERR_UNSUPPORTED),
+    (dict(h_q=65536, h_kv=1), _lib.GQA_ERR_UNSUPPORTED),   # a grid dimension
     (dict(kc=FAKE + 8), _lib.GQA_ERR_INVALID_ARG),         # misaligned
     (dict(wsb=64), _lib.GQA_ERR_WORKSPACE),
     (dict(k=None), _lib.GQA_ERR_INVALID_ARG),              # k and v: both or neither
