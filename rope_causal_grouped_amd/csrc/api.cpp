@@ -236,16 +236,23 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, cs, o, out_dtype == GQA_BF16, B, L,
                                  Lpad, h_q, h_kv, d, scale, causal, nullptr, nullptr, L, st);
   } else {
-    float* kp = (float*)(wsb + ws.kp_off);
-    e = gqa::launch_kv_prepare_f32((const float*)k, (const float*)v, cs, kp, (float*)k_cache,
-                                   (float*)v_cache, B, L, h_kv, d, cap, st);
-    if (e != hipSuccess) return hip_fail(e, "K preparation launch");
-    if (ev.first) (void)hipEventRecord(ev.first, st);
-    const gqa::KvStrides ksd{(int64_t)h_kv * L * d, L * d, d};          // [B][h_kv][L][d]
     const gqa::KvStrides vsd{L * h_kv * d, d, (int64_t)h_kv * d};       // [B, L, h_kv, d]
-    e = gqa::launch_prefill_f32((const float*)q, kp, (const float*)v, cs, o,
-                                out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, ksd, vsd,
-                                nullptr, nullptr, L, st);
+    if (k_cache) {   // rotated K and V into the cache; attention reads the rotated copy
+      float* kp = (float*)(wsb + ws.kp_off);
+      e = gqa::launch_kv_prepare_f32((const float*)k, (const float*)v, cs, kp, (float*)k_cache,
+                                     (float*)v_cache, B, L, h_kv, d, cap, st);
+      if (e != hipSuccess) return hip_fail(e, "K preparation launch");
+      if (ev.first) (void)hipEventRecord(ev.first, st);
+      const gqa::KvStrides ksd{(int64_t)h_kv * L * d, L * d, d};        // [B][h_kv][L][d]
+      e = gqa::launch_prefill_f32((const float*)q, kp, (const float*)v, cs, nullptr, o,
+                                  out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, ksd,
+                                  vsd, nullptr, nullptr, L, st);
+    } else {         // no cache: the attention kernel rotates K as it stages each tile
+      if (ev.first) (void)hipEventRecord(ev.first, st);
+      e = gqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, cs, cs, o,
+                                  out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, vsd,
+                                  vsd, nullptr, nullptr, L, st);
+    }
   }
   if (ev.second) {
     (void)hipEventRecord(ev.second, st);
@@ -380,8 +387,8 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
     const gqa::KvStrides csd{cap * h_kv * d, d, (int64_t)h_kv * d};   // [B, cap, h_kv, d]
     if (ev.first) (void)hipEventRecord(ev.first, st);
     e = gqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache,
-                                q_rotated ? nullptr : cs, o, out_dtype == GQA_BF16, B, C, h_q,
-                                h_kv, d, scale, 1, csd, csd, start, len, kend, st);
+                                q_rotated ? nullptr : cs, nullptr, o, out_dtype == GQA_BF16, B, C,
+                                h_q, h_kv, d, scale, 1, csd, csd, start, len, kend, st);
   }
   if (ev.second) {
     (void)hipEventRecord(ev.second, st);

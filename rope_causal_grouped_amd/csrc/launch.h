@@ -56,9 +56,12 @@ struct KvStrides {
   int64_t batch, head, row;
 };
 
+// cs: the queries' cos/sin table (NULL: q is rotated already); kcs: the
+// keys' table, position = key index (NULL: kp holds rotated keys)
 hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, const float2* cs,
-                              void* o, int out_bf16, int64_t B, int64_t L, int h_q, int h_kv,
-                              int d, float scale, int causal, KvStrides ks, KvStrides vs,
+                              const float2* kcs, void* o, int out_bf16, int64_t B, int64_t L,
+                              int h_q, int h_kv, int d, float scale, int causal, KvStrides ks,
+                              KvStrides vs,
                               const int64_t* qstart, const int64_t* qlen, int64_t kend,
                               hipStream_t st);
 

@@ -6,17 +6,18 @@
 // Same operation as the bf16 kernel (Qwen2 technical-report walkthrough,
 // aicoding.csdn.net, §4.1.3 steps 3-4).  A workgroup owns 16 positions of
 // one query head; four lanes share a row, each holding a quarter of its dims
-// (dims j and j + d/2 of a RoPE pair stay in one lane).  K' (rotated by the
-// preparation pass) and V tiles of 64 keys are staged in LDS; each of the
+// (dims j and j + d/2 of a RoPE pair stay in one lane).  K' and V tiles of
+// 64 keys are staged in LDS (K rotated while staging, from the cos/sin
+// table, or rotated already by the pass that wrote the cache); each of the
 // four waves holds all 16 rows and takes a quarter of every tile's keys,
 // updating its own online softmax four keys at a time, and the quarters are
 // merged exactly at the end.  The small shapes this serves are latency-
 // bound, so the split buys parallelism: four times the workgroups of a
-// 64-row layout, and a quarter of the serial key chain per wave.  Keys and values
-// are read through strides, so they may come from the preparation pass (rotated K,
-// [B][h_kv][L][d]) and the call's V, or straight from a per-layer cache
-// [B, cap, h_kv, d] when a chunk of queries at positions qstart[b] + i
-// attends to everything cached so far.
+// 64-row layout, and a quarter of the serial key chain per wave.  Keys and
+// values are read through strides, so they may be the call's own K and V
+// [B, L, h_kv, d], the preparation pass's rotated K [B][h_kv][L][d], or a
+// per-layer cache [B, cap, h_kv, d] when a chunk of queries at positions
+// qstart[b] + i attends to everything cached so far.
 
 #include "common.h"
 #include "launch.h"
@@ -36,9 +37,9 @@ __device__ __forceinline__ float quad_swap(float x) {
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ v,
-    const float2* __restrict__ cs, void* __restrict__ o, int L, int h_q, int h_kv, int g,
-    float scale, int causal, KvStrides ks_, KvStrides vs_, const int64_t* __restrict__ qstart,
-    const int64_t* __restrict__ qlen, int kend) {
+    const float2* __restrict__ cs, const float2* __restrict__ kcs, void* __restrict__ o, int L,
+    int h_q, int h_kv, int g, float scale, int causal, KvStrides ks_, KvStrides vs_,
+    const int64_t* __restrict__ qstart, const int64_t* __restrict__ qlen, int kend) {
   constexpr int TK = 64;                 // keys per staged tile
   constexpr int RB = 16;                 // rows (positions) per workgroup
   constexpr int KQ = TK / 4;             // keys of a tile per wave
@@ -104,27 +105,50 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   const float* vbase = v + (int64_t)b * vs_.batch + (int64_t)u * vs_.head;
 
   for (int k0 = 0; k0 < n_keys; k0 += TK) {
-    // stage the tile: every 16-byte load issued before the first store
-    constexpr int C4 = TK * D / 4 / 256;   // float4 loads per thread and array
-    float4 kv4[C4], vv4[C4];
+    // stage the tile: every 16-byte load issued before the first store.  A
+    // thread takes four RoPE pairs (dims j4..j4+3 and j4+d/2..) of a key, so
+    // with kcs set it rotates K here, at the key's position (= its index)
+    constexpr int CP = TK * (D / 8) / 256;   // four-pair chunks per thread
+    float4 k1[CP], k2[CP], v1[CP], v2[CP];
 #pragma unroll
-    for (int r = 0; r < C4; ++r) {
+    for (int r = 0; r < CP; ++r) {
       const int idx = threadIdx.x + r * 256;
-      const int kk = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+      const int kk = idx / (D / 8), j4 = (idx % (D / 8)) * 4;
       const int key = k0 + kk;
-      kv4[r] = vv4[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      k1[r] = k2[r] = v1[r] = v2[r] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (key < nk) {
-        kv4[r] = *(const float4*)(kbase + (int64_t)key * ks_.row + d4);
-        vv4[r] = *(const float4*)(vbase + (int64_t)key * vs_.row + d4);
+        const float* kr = kbase + (int64_t)key * ks_.row + j4;
+        const float* vr = vbase + (int64_t)key * vs_.row + j4;
+        k1[r] = *(const float4*)kr;
+        k2[r] = *(const float4*)(kr + D / 2);
+        v1[r] = *(const float4*)vr;
+        v2[r] = *(const float4*)(vr + D / 2);
+        if (kcs) {
+          const float4* c4p = (const float4*)(kcs + (int64_t)key * (D / 2) + j4);
+          const float4 ca = c4p[0], cb = c4p[1];   // (cos, sin) of pairs j4 .. j4+3
+          const float c[4] = {ca.x, ca.z, cb.x, cb.z}, sn[4] = {ca.y, ca.w, cb.y, cb.w};
+          float x1[4] = {k1[r].x, k1[r].y, k1[r].z, k1[r].w};
+          float x2[4] = {k2[r].x, k2[r].y, k2[r].z, k2[r].w};
+          float y1[4], y2[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y1[e] = fmaf(x1[e], c[e], -x2[e] * sn[e]);
+            y2[e] = fmaf(x2[e], c[e], x1[e] * sn[e]);
+          }
+          k1[r] = make_float4(y1[0], y1[1], y1[2], y1[3]);
+          k2[r] = make_float4(y2[0], y2[1], y2[2], y2[3]);
+        }
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < C4; ++r) {
+    for (int r = 0; r < CP; ++r) {
       const int idx = threadIdx.x + r * 256;
-      const int kk = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-      *(float4*)&ks[kk][d4] = kv4[r];
-      *(float4*)&vs[kk][d4] = vv4[r];
+      const int kk = idx / (D / 8), j4 = (idx % (D / 8)) * 4;
+      *(float4*)&ks[kk][j4] = k1[r];
+      *(float4*)&ks[kk][j4 + D / 2] = k2[r];
+      *(float4*)&vs[kk][j4] = v1[r];
+      *(float4*)&vs[kk][j4 + D / 2] = v2[r];
     }
     __syncthreads();
     // this wave's quarter of the tile, four keys per step: their dot
@@ -212,15 +236,16 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
 }
 
 hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, const float2* cs,
-                              void* o, int out_bf16, int64_t B, int64_t L, int h_q, int h_kv,
-                              int d, float scale, int causal, KvStrides ks, KvStrides vs,
-                              const int64_t* qstart, const int64_t* qlen, int64_t kend,
-                              hipStream_t st) {
+                              const float2* kcs, void* o, int out_bf16, int64_t B, int64_t L,
+                              int h_q, int h_kv, int d, float scale, int causal, KvStrides ks,
+                              KvStrides vs, const int64_t* qstart, const int64_t* qlen,
+                              int64_t kend, hipStream_t st) {
   const int g = h_q / h_kv;
   dim3 grid((unsigned)((L + 15) / 16), (unsigned)h_q, (unsigned)B);
-#define GQA_LAUNCH(DD, OB)                                                                   \
-  prefill_f32_kernel<DD, OB><<<grid, 256, 0, st>>>(q, kp, v, cs, o, (int)L, h_q, h_kv, g, scale, \
-                                                   causal, ks, vs, qstart, qlen, (int)kend)
+#define GQA_LAUNCH(DD, OB)                                                               \
+  prefill_f32_kernel<DD, OB><<<grid, 256, 0, st>>>(q, kp, v, cs, kcs, o, (int)L, h_q, h_kv, g, \
+                                                   scale, causal, ks, vs, qstart, qlen,       \
+                                                   (int)kend)
   if (d == 128) {
     if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);
   } else {
