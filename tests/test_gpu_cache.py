@@ -402,9 +402,12 @@ def test_yarn_prefill_and_decode(yarn_4x, dtype):
     kc = torch.zeros((B, L + 40000, h_kv, d), dtype=dtype, device="cuda")
     vc = torch.zeros_like(kc)
     o = gqa.prefill(qd, kd, vd, k_cache=kc, v_cache=vc)
+    on = gqa.prefill(qd, kd, vd)   # no cache copy: another K path for fp32
     od = gqa.decode(qd[:, -1].contiguous(), kc, vc, kv_len=L, q_pos=L + 39000)
     torch.cuda.synchronize()
-    assert_parity(host(o), oracle.prefill(q, k, v, theta=yarn_4x), dtype, "YaRN prefill")
+    want = oracle.prefill(q, k, v, theta=yarn_4x)
+    assert_parity(host(o), want, dtype, "YaRN prefill")
+    assert_parity(host(on), want, dtype, "YaRN prefill without a cache")
     kc_h, vc_h = host(kc), host(vc)
     assert_rotated_rows(kc_h[:, :L], oracle.rope(k, np.arange(L), yarn_4x), dtype, "YaRN cache")
     assert_parity(host(od), oracle.decode(q[:, -1], kc_h, vc_h, L, L + 39000, theta=yarn_4x),
