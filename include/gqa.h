@@ -282,9 +282,10 @@ int gqa_timing_read(int which, double* total_ms, int64_t* count);
  * with non-temporal loads, on `stream`, and may write 4 bytes to the device
  * pointer `sink`.  Its rate is the context for the HBM-bound kernels'
  * roofline figures.  p must be 16-byte aligned and bytes a positive
- * multiple of 16 (else GQA_ERR_INVALID_ARG).  Asynchronous.
+ * multiple of 16 (else GQA_ERR_INVALID_ARG).  `stream` is a hipStream_t
+ * (NULL: the default stream), as for every other entry point.  Asynchronous.
  */
-int gqa_stream_read(const void* p, size_t bytes, void* sink, hipStream_t stream);
+int gqa_stream_read(const void* p, size_t bytes, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -272,3 +272,31 @@ def test_set_rope_yarn_rejects(lib):
     assert lib.gqa_set_rope_yarn(float("nan"), 32768.0, 32.0, 1.0) == _lib.GQA_ERR_INVALID_ARG
     assert lib.gqa_set_rope_yarn(4.0, 32768.0, 32.0, 1.0) == _lib.GQA_OK
     assert lib.gqa_set_rope_yarn(1.0, 0.0, 0.0, 0.0) == _lib.GQA_OK   # back to plain RoPE
+
+
+C_CONSUMER = os.path.join(ROOT, "tests", "c_abi", "consumer.c")
+
+
+def test_c99_consumer_compiles_links_and_runs(lib, tmp_path):
+    """A C99 translation unit that includes only gqa.h compiles warning-free
+    under -pedantic, links against libgqa.so by name, and its host-side calls
+    of every entry point behave as the header states."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = open(C_CONSUMER).read()
+    missing = [n for n in header_functions() if re.search(r"\b%s\s*\(" % n, src) is None]
+    assert not missing, f"consumer.c does not call {missing}"
+    obj = tmp_path / "consumer.o"
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), "-c", C_CONSUMER, "-o", str(obj)],
+                   check=True, capture_output=True, text=True)
+    subprocess.run([gcc, str(obj), "-o", str(exe), "-L", libdir, "-lgqa",
+                    "-Wl,-rpath," + libdir], check=True, capture_output=True, text=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "c99 consumer ok" in res.stdout
