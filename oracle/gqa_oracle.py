@@ -12,6 +12,7 @@ Sources (web pages on the Qwen2 decoder, cited by title/host and section):
   [evo]  "从 Qwen 1 到 Qwen 2 架构演进到底改了什么" (nxmr.cn)
   [ip]   "Qwen2架构解析：GQA与MoE技术在大模型中的创新应用" (intelliparadigm.com)
   [csdn] Qwen2 technical-report walkthrough (aicoding.csdn.net)
+  [yd]   "Qwen-2 详解" (yudonglee.me)
   [kn]   "Qwen2 / Qwen3 的实测配置差异与三个坑" (docs.keinmal.top)
 
 Readings taken where the pages are silent or disagree:

@@ -520,19 +520,60 @@ def pin_yarn_regions(orc):
     assert np.all(np.diff(ratio) >= -1e-12)
 
 
+def _yarn_golden():
+    """tests/golden/yarn_qwen2.txt: Qwen2's 4x YaRN setting, closed form in
+    decimal arithmetic (pairs 0, 20-43, 63; ramp bounds; attention factor)."""
+    meta, pairs = {}, []
+    for row in read_table("yarn_qwen2.txt"):
+        if row[0] in ("lo", "hi", "mscale"):
+            meta[row[0]] = float(row[1])
+        else:
+            num, _, den = row[1].partition("/")
+            pairs.append((int(row[0]), float(num) / float(den or 1), float(row[2]),
+                          float(row[3])))
+    return meta, pairs
+
+
+QWEN2_YARN = dict(theta=1.0e6, factor=4.0, original_max_position=32768.0, beta_fast=32.0,
+                  beta_slow=1.0)
+
+
+def pin_yarn_golden_frequencies(orc):
+    """Every pair of Qwen2's long-context setting (d 128, base 1e6, 32K window,
+    4x) against the closed-form values of tests/golden/yarn_qwen2.txt
+    ("Qwen-2 详解" (yudonglee.me) §6.2; walkthrough §5.3): the unscaled
+    frequencies, the ramp (0 up to pair 23, k/17 at pair 23 + k, 1 from pair
+    40) and the blended frequencies, including the whole ramp interior."""
+    meta, pairs = _yarn_golden()
+    assert (meta["lo"], meta["hi"]) == (23.0, 40.0)
+    y = orc.YaRN(**QWEN2_YARN)
+    ramp = orc.yarn_ramp(y, 128)
+    w0 = orc.inv_freq(128)
+    w = orc.inv_freq(128, y)
+    for j, r, om, om2 in pairs:
+        assert abs(ramp[j] - r) <= 1e-15, f"ramp of pair {j}: {ramp[j]!r} vs {r!r}"
+        assert abs(w0[j] - om) <= 1e-14 * om, f"omega of pair {j}: {w0[j]!r} vs {om!r}"
+        assert abs(w[j] - om2) <= 1e-14 * om2, f"scaled omega of pair {j}: {w[j]!r} vs {om2!r}"
+
+
 def pin_yarn_attention_factor(orc):
-    """Under YaRN with factor s every rotated row is longer by 0.1 ln s + 1
-    (the rotation keeps norms; the factor rescales the attention logits by
-    its square), and q'.k' still depends on m - n only."""
+    """Under Qwen2's 4x setting every rotated row is longer by the golden
+    factor 0.1 ln 4 + 1 = 1.1386... (tests/golden/yarn_qwen2.txt), so q'.k'
+    at equal positions is q.k times its square (the logit rescale of
+    walkthrough §5.3), and q'.k' still depends on m - n only."""
+    meta, _ = _yarn_golden()
+    ms = meta["mscale"]
+    assert abs(ms - 1.1386294361119891) < 1e-15
     rng = _rng(22)
-    y = orc.YaRN(factor=8.0, original_max_position=4096.0)
-    x = _rand(rng, 1, 7, 2, 32)
-    xr = orc.rope(x, np.arange(500, 507), y)
-    close(np.linalg.norm(xr, axis=-1), np.linalg.norm(x, axis=-1) * (0.1 * math.log(8.0) + 1.0),
-          1e-12, "norm")
-    q = _rand(rng, 1, 1, 1, 32)
-    k = _rand(rng, 1, 1, 1, 32)
-    a = np.sum(orc.rope(q, [40000], y) * orc.rope(k, [39990], y))
+    y = orc.YaRN(**QWEN2_YARN)
+    x = _rand(rng, 1, 7, 2, 128)
+    xr = orc.rope(x, np.arange(100000, 100007), y)
+    close(np.linalg.norm(xr, axis=-1), np.linalg.norm(x, axis=-1) * ms, 1e-12, "norm")
+    q = _rand(rng, 1, 1, 1, 128)
+    k = _rand(rng, 1, 1, 1, 128)
+    same = np.sum(orc.rope(q, [70000], y) * orc.rope(k, [70000], y))
+    assert abs(same - ms * ms * np.sum(q * k)) < 1e-11, (same, np.sum(q * k))
+    a = np.sum(orc.rope(q, [120000], y) * orc.rope(k, [119990], y))
     b = np.sum(orc.rope(q, [10], y) * orc.rope(k, [0], y))
     assert abs(a - b) < 1e-9, (a, b)
 
@@ -546,4 +587,4 @@ ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_cache_append_pair0, pin_ragged_decode_is_single, pin_qkv_layout,
             pin_qkv_epilogue_then_attention, pin_paged_decode_is_contiguous,
             pin_paged_append_is_contiguous, pin_yarn_factor_one_is_plain, pin_yarn_regions,
-            pin_yarn_attention_factor]
+            pin_yarn_golden_frequencies, pin_yarn_attention_factor]

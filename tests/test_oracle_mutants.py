@@ -2,6 +2,7 @@
 check that at least one pin catches each of them."""
 
 import importlib.util
+import math
 import os
 import sys
 
@@ -211,6 +212,28 @@ def m_yarn_factor_squared(mod):
     mod.inv_freq = inv_freq
 
 
+def m_yarn_round_bounds(mod):
+    """Ramp bounds rounded to the nearest pair instead of floor / ceil."""
+    def yarn_ramp(spec, d):
+        def corr_dim(n):
+            return d * math.log(spec.original_max_position / (n * 2.0 * math.pi)) / (
+                2.0 * math.log(spec.theta))
+        lo = max(round(corr_dim(spec.beta_fast)), 0)
+        hi = min(round(corr_dim(spec.beta_slow)), d - 1)
+        j = np.arange(d // 2, dtype=np.float64)
+        return np.clip((j - lo) / (hi - lo), 0.0, 1.0)
+    mod.yarn_ramp = yarn_ramp
+
+
+def m_yarn_blend_in_turns(mod):
+    """Ramp linear in the number of turns over the window, not in the pair index."""
+    def yarn_ramp(spec, d):
+        j = np.arange(d // 2, dtype=np.float64)
+        turns = spec.original_max_position * spec.theta ** (-2.0 * j / d) / (2.0 * math.pi)
+        return np.clip((spec.beta_fast - turns) / (spec.beta_fast - spec.beta_slow), 0.0, 1.0)
+    mod.yarn_ramp = yarn_ramp
+
+
 MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
            m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
@@ -218,7 +241,8 @@ MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_chunk_position_shift, m_ragged_first_value, m_cached_key_unrotated,
            m_qkv_k_v_swapped, m_qkv_bias_dropped, m_qkv_heads_transposed,
            m_paged_row_major_page, m_paged_page_of_next_block, m_yarn_ramp_reversed,
-           m_yarn_no_attention_factor, m_yarn_factor_squared]
+           m_yarn_no_attention_factor, m_yarn_factor_squared, m_yarn_round_bounds,
+           m_yarn_blend_in_turns]
 
 
 def failing_pins(mod):
