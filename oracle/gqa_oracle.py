@@ -219,6 +219,39 @@ def prefill_rows(q, k, v, rows, theta: float = ROPE_THETA,
     return out
 
 
+def prefill_group_rows(q_b, k_b, v_b, u: int, r0: int, r1: int,
+                       theta: float = ROPE_THETA, scale: float | None = None,
+                       causal: bool = True) -> np.ndarray:
+    """Rows r0 .. r1-1 of the prefill of one sequence for the g query heads
+    of KV group u: q_b [L, h_q, d], k_b/v_b [L, h_kv, d] (pre-RoPE, positions
+    0 .. L-1).  Returns [r1 - r0, g, d], equal to
+    prefill(q_b[None], k_b[None], v_b[None])[0, r0:r1, u*g:(u+1)*g].
+
+    The same steps as prefill ([csdn] §4.1.3 steps 3-4) restricted to those
+    query rows: a causal row i only sees keys 0..i, so keys past r1 - 1 are
+    not formed.  Cutting the output into such slices lets the full
+    workloads be evaluated piece by piece (and in parallel)."""
+    L, h_q, d = np.shape(q_b)
+    h_kv = np.shape(k_b)[1]
+    g = group_size(h_q, h_kv)
+    if not 0 <= r0 < r1 <= L:
+        raise ValueError("row range outside the sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    pos = np.arange(L)
+    nk = r1 if causal else L
+    qr = rope(np.asarray(q_b[r0:r1, u * g:(u + 1) * g], np.float64), pos[r0:r1], theta)
+    kr = rope(np.asarray(k_b[:nk, u:u + 1], np.float64), pos[:nk], theta)[:, 0]
+    vu = np.asarray(v_b[:nk, u], np.float64)
+    vis = visible(pos[r0:r1], pos[:nk]) if causal else np.ones((r1 - r0, nk), bool)
+    out = np.empty((r1 - r0, g, d), np.float64)
+    for c in range(g):
+        if kv_group(u * g + c, h_q, h_kv) != u:
+            raise AssertionError("head outside its group")
+        out[:, c, :] = attend(qr[:, c, :], kr, vu, scale, vis)
+    return out
+
+
 def decode(q, k_cache, v_cache, kv_len: int, q_pos: int,
            theta: float = ROPE_THETA, scale: float | None = None) -> np.ndarray:
     """One new query token per sequence.  q [B, h_q, d] (pre-RoPE, rotated

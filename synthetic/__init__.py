@@ -13,10 +13,10 @@ even) and kept in float32, so the host array holds exactly the values the
 GPU receives.
 """
 
-from .workloads import (WORKLOADS, Workload, bf16_round, gen_prefill,
+from .workloads import (WORKLOADS, Workload, bf16_round, gen_prefill, gen_prefill_b,
                         gen_decode_query, gen_decode_cache_b, gen_normal,
                         scaled_rows)
 
-__all__ = ["WORKLOADS", "Workload", "bf16_round", "gen_prefill",
+__all__ = ["WORKLOADS", "Workload", "bf16_round", "gen_prefill", "gen_prefill_b",
            "gen_decode_query", "gen_decode_cache_b", "gen_normal",
            "scaled_rows"]

@@ -130,6 +130,20 @@ def gen_prefill(w: Workload, B: int | None = None, L: int | None = None):
     return q, k, v
 
 
+def gen_prefill_b(w: Workload, b: int, L: int | None = None):
+    """(q, k, v) of batch slice b alone, each [L, h, d]: the same values as
+    gen_prefill(w)[i][b] (per-slice generators; boosted rows are the same in
+    every slice)."""
+    L = w.L if L is None else L
+    q = gen_normal(w.seed, TID_Q, b, (1, L, w.h_q, w.d), w.sigma, w.dtype)
+    k = gen_normal(w.seed, TID_K, b, (1, L, w.h_kv, w.d), w.sigma, w.dtype)
+    v = gen_normal(w.seed, TID_V, b, (1, L, w.h_kv, w.d), w.sigma, w.dtype)
+    if w.boosted_rows:
+        _boost(q, w.seed, 0, w.boosted_rows)
+        _boost(k, w.seed, 1, w.boosted_rows)
+    return q[0], k[0], v[0]
+
+
 def gen_decode_query(w: Workload, B: int | None = None) -> np.ndarray:
     """New query tokens [B, h_q, d] (pre-rotation) for a decode workload."""
     B = w.B if B is None else B

@@ -280,6 +280,26 @@ def pin_prefill_rows(orc):
     close(orc.prefill_rows(q, k, v, rows), want, 1e-12, "prefill_rows")
 
 
+def pin_prefill_group_rows(orc):
+    """Row slices of one sequence and one KV group, tiling every row with
+    ragged bounds, reassemble the full prefill (causal and not)."""
+    rng = _rng(23)
+    B, L, h_q, h_kv, d = 2, 23, 6, 2, 8
+    q = _rand(rng, B, L, h_q, d)
+    k = _rand(rng, B, L, h_kv, d)
+    v = _rand(rng, B, L, h_kv, d)
+    g = h_q // h_kv
+    for causal in (True, False):
+        want = orc.prefill(q, k, v, causal=causal)
+        got = np.full(want.shape, np.nan)
+        for b in range(B):
+            for u in range(h_kv):
+                for r0, r1 in ((0, 7), (7, 16), (16, 23)):
+                    got[b, r0:r1, u * g:(u + 1) * g] = orc.prefill_group_rows(
+                        q[b], k[b], v[b], u, r0, r1, causal=causal)
+        close(got, want, 1e-12, f"prefill_group_rows (causal={causal})")
+
+
 # ------------------------------------------------ cache, chunks, ragged --
 
 def pin_chunked_prefill_is_prefill(orc):
@@ -583,6 +603,7 @@ ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_rope_group_law, pin_group_example, pin_repeat_interleave,
             pin_sdpa, pin_brute, pin_softmax_causal, pin_future_invariance,
             pin_shift_invariance, pin_decode_is_prefill_row, pin_prefill_rows,
+            pin_prefill_group_rows,
             pin_chunked_prefill_is_prefill, pin_decode_append_is_prefill_row,
             pin_cache_append_pair0, pin_ragged_decode_is_single, pin_qkv_layout,
             pin_qkv_epilogue_then_attention, pin_paged_decode_is_contiguous,

@@ -412,3 +412,29 @@ def test_yarn_prefill_and_decode(yarn_4x, dtype):
     assert_rotated_rows(kc_h[:, :L], oracle.rope(k, np.arange(L), yarn_4x), dtype, "YaRN cache")
     assert_parity(host(od), oracle.decode(q[:, -1], kc_h, vc_h, L, L + 39000, theta=yarn_4x),
                   dtype, "YaRN decode far past the cache")
+
+
+def test_yarn_chunk_past_512_key_tiles(yarn_4x):
+    """A bf16 chunk at the end of a 40960-position sequence (YaRN 4x, past
+    the 32K window): the attention kernel walks 640 key tiles, more than one
+    per thread of its workgroup, including the per-tile norm scan over all
+    of them.  The whole chunk is compared."""
+    L, C, h_q, h_kv, d = 40960, 256, 28, 4, 128
+    s0 = L - C
+    dtype = torch.bfloat16
+    note(f"YaRN chunk at {s0}..{L - 1} over {L // 64} key tiles")
+    q, k, v = inputs(1, L, h_q, h_kv, d, dtype, 48)
+    kc = torch.zeros((1, L, h_kv, d), dtype=dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    kc[:, :s0].copy_(torch.from_numpy(k[:, :s0]))
+    vc[:, :s0].copy_(torch.from_numpy(v[:, :s0]))
+    gqa.rope_apply(kc[:, :s0])          # rows before the chunk: rotated K, as cached
+    o = gqa.prefill_chunk(dev(q[:, s0:], dtype), dev(k[:, s0:], dtype), dev(v[:, s0:], dtype),
+                          kc, vc, [s0], kend=L)
+    torch.cuda.synchronize()
+    g = h_q // h_kv
+    want = np.concatenate([oracle.prefill_group_rows(q[0], k[0], v[0], u, s0, L,
+                                                     theta=yarn_4x)
+                           for u in range(h_kv)], axis=1)
+    assert_parity(host(o)[0], want, dtype, f"YaRN chunk over {L // 64} key tiles")
+    assert want.shape == (C, h_q, d) and g == 7

@@ -234,6 +234,20 @@ def m_yarn_blend_in_turns(mod):
     mod.yarn_ramp = yarn_ramp
 
 
+def m_group_rows_short_keys(mod):
+    """Row slices that drop the diagonal key of their last row."""
+    orig = mod.prefill_group_rows
+
+    def prefill_group_rows(q_b, k_b, v_b, u, r0, r1, theta=mod.ROPE_THETA, scale=None,
+                           causal=True):
+        out = orig(q_b, k_b, v_b, u, r0, r1, theta, scale, causal)
+        if causal and r1 - r0 > 1:
+            out[-1] = orig(q_b[:r1 - 1], k_b[:r1 - 1], v_b[:r1 - 1], u, r1 - 2, r1 - 1, theta,
+                           scale, causal)[0]
+        return out
+    mod.prefill_group_rows = prefill_group_rows
+
+
 MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
            m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
@@ -242,7 +256,7 @@ MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_qkv_k_v_swapped, m_qkv_bias_dropped, m_qkv_heads_transposed,
            m_paged_row_major_page, m_paged_page_of_next_block, m_yarn_ramp_reversed,
            m_yarn_no_attention_factor, m_yarn_factor_squared, m_yarn_round_bounds,
-           m_yarn_blend_in_turns]
+           m_yarn_blend_in_turns, m_group_rows_short_keys]
 
 
 def failing_pins(mod):
