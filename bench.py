@@ -23,8 +23,13 @@ context figures under "context".
 the decode rate (K/V cache bytes read once per KV group / call time) is
 reported beside it.  Kernel durations for the roofline objects come from HIP
 events that the library records on the launch stream around its attention
-and split-K kernels.  The CPU baseline is the fp64 oracle timed on a bounded
-sample of the prefill workload.
+and split-K kernels.  Before the W warm-up steps the step runs for a fixed
+stretch of time (--clock-warmup-s), so that the timed steps see the
+sustained shader clock rather than the ramp from idle, whatever W is.
+After timing, the outputs of the timed calls are compared with the fp64
+oracle (the whole 7B prefill output and all 32 decode sequences); the
+oracle's prefill leg, run as a pool of single-threaded processes on the
+host cores, is also the CPU baseline.
 
 Prints one JSON line.  Only one GPU is supported.
 """
@@ -76,37 +81,101 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    # the shader clock ramps up over the first few tens of milliseconds of
-    # load; 100 untimed steps put the timed ones at the sustained clock
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    # the shader clock ramps up over the first tens of milliseconds of load;
+    # this much untimed work first puts the timed steps at the sustained clock
+    p.add_argument("--clock-warmup-s", type=float, default=0.5)
     p.add_argument("--only", choices=["prefill", "decode", "next"], default=None,
                    help="run one part only (for profiling)")
-    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle leg (CPU baseline and parity of the timed outputs)")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
 
 
-def cpu_baseline(w):
-    """Time the fp64 oracle (as it stands) on batch slice 0 of the prefill
-    workload (all heads, all positions)."""
-    import oracle
-    from synthetic import gen_prefill
+def oracle_leg(wp, wd, got_prefill, got_decode):
+    """The fp64 oracle over the whole output of the timed prefill call (the
+    CPU baseline: a pool of single-threaded processes, one per host core,
+    over (sequence, KV group, query rows) pieces) and over every sequence of
+    the decode call; both outputs are compared with it."""
+    from oracle import pool as opool
+    cores = opool.host_cores()
+    res = {}
+    with opool.oracle_pool(cores) as pool:
+        tasks = opool.prefill_tasks(wp.key)
+        cmp = opool.Comparison()
+        t0 = time.perf_counter()
+        for b, u, r0, r1, want in opool.prefill_pieces(pool, tasks):
+            if got_prefill is not None:
+                cmp.add(got_prefill[b, r0:r1, u * wp.g:(u + 1) * wp.g], want, (b, u, r0, r1))
+        dt = time.perf_counter() - t0
+        flops = wp.prefill_flops()
+        res["cpu_baseline"] = {
+            "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole {wp.name} output (B{wp.B}, {wp.h_q} query heads, all {wp.L} "
+                      f"positions): {flops / 1e9:.1f} causal GFLOP in {dt:.2f} s, fp64 NumPy "
+                      f"in {cores} single-threaded processes over {len(tasks)} "
+                      f"(sequence, KV group, rows) pieces"}
+        log(f"[bench] oracle: whole prefill output in {dt:.1f} s on {cores} cores")
+        parity = {}
+        if got_prefill is not None:
+            parity["prefill"] = {"workload": wp.name, "outputs": cmp.count,
+                                 "max_abs": cmp.max_abs, "rel_l2": cmp.rel_l2,
+                                 "nonfinite": cmp.nonfinite,
+                                 "ok": bool(cmp.nonfinite == 0 and cmp.max_abs <= 2e-2
+                                            and cmp.rel_l2 <= 1e-2)}
+        if got_decode is not None:
+            cmd = opool.Comparison()
+            for b, want in opool.decode_pieces(pool, wd.key):
+                cmd.add(got_decode[b], want, b)
+            parity["decode"] = {"workload": wd.name, "outputs": cmd.count,
+                                "max_abs": cmd.max_abs, "rel_l2": cmd.rel_l2,
+                                "nonfinite": cmd.nonfinite,
+                                "ok": bool(cmd.nonfinite == 0 and cmd.max_abs <= 2e-2
+                                           and cmd.rel_l2 <= 1e-2)}
+        for name, r in parity.items():
+            log(f"[bench] parity of the timed {name} call vs the fp64 oracle: "
+                f"max-abs {r['max_abs']:.3e}, rel-L2 {r['rel_l2']:.3e} over {r['outputs']} "
+                f"outputs ({'ok' if r['ok'] else 'FAILED'})")
+        res["parity"] = parity
+    return res
+
+
+def clock_warmup(torch, step, seconds):
+    """Run the step until `seconds` of GPU time have passed; returns the
+    number of steps run."""
+    if seconds <= 0:
+        return 0
+    n, busy = 0, 0.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while busy < seconds * 1e3:
+        e0.record()
+        for _ in range(5):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        busy += e0.elapsed_time(e1)
+        n += 5
+    return n
+
+
+def no_children_left():
+    """Wait for (or end) any child process this run started; returns what
+    was found, for the log."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
-    q, k, v = gen_prefill(w, B=1)
-    t0 = time.perf_counter()
-    oracle.prefill(q, k, v, theta=w.theta, scale=w.scale)
-    dt = time.perf_counter() - t0
-    flops = 4 * 1 * w.h_q * w.d * w.L * (w.L + 1) // 2
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"batch 0 of {w.B} ({w.h_q} query heads, all {w.L} positions) of "
-                      f"{w.name}; {flops / 1e9:.1f} causal GFLOP in {dt:.2f} s (fp64 NumPy)"}
+        import psutil
+    except ImportError:
+        return "psutil unavailable"
+    kids = psutil.Process().children(recursive=True)
+    for p in kids:
+        try:
+            p.wait(timeout=5)
+        except psutil.TimeoutExpired:
+            p.terminate()
+            p.wait(timeout=5)
+    return f"{len(kids)} child process(es) at exit" if kids else "no child processes at exit"
 
 
 def measure_context(torch, gqa, dev):
@@ -426,10 +495,12 @@ def main():
         if run_d:
             gqa.decode(qh, kc, vc, kv_len=wd.L, q_pos=wd.q_pos, out=odd, workspace=wsd)
 
+    n_clock = clock_warmup(torch, step, args.clock_warmup_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
+    log(f"[bench] clock warm-up {n_clock} steps ({args.clock_warmup_s:.2f} s), "
+        f"warmup done ({args.warmup} steps)")
 
     K = args.steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K)]
@@ -455,6 +526,9 @@ def main():
     attn_ms, attn_n = gqa.timing_read(0)
     split_ms, split_n = gqa.timing_read(1)
     log(f"[bench] timed {K} steps: {total_ms:.2f} ms total")
+    # outputs of the last timed calls, for the parity check after all timing
+    got_prefill = od.cpu().numpy() if run_p else None
+    got_decode = odd.cpu().numpy() if run_d else None
 
     if run_n:
         out_next = measure_next(args, torch, gqa, dev, wp, wd,
@@ -472,7 +546,8 @@ def main():
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": args.warmup,
            "ms_per_step": total_ms / K, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "clock_warmup": {"steps": n_clock, "seconds": args.clock_warmup_s}}
     if run_p:
         flops = wp.prefill_flops()
         attn_avg = attn_ms / max(attn_n, 1)
@@ -489,6 +564,10 @@ def main():
                            "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": ach / PEAK_BF16_TFLOPS, "kernel_ms": attn_avg,
                            "traffic": traffic_bytes("prefill")}
+        out["call_roofline"] = {"bound": "mfma", "achieved": out["value"],
+                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": out["value"] / PEAK_BF16_TFLOPS, "call_ms": pre_ms,
+                                "outside_attention_us": (pre_ms - attn_avg) * 1e3}
     if run_d:
         kvb = wd.decode_kv_bytes()
         split_avg = split_ms / max(split_n, 1)
@@ -520,8 +599,9 @@ def main():
         log(f"[bench] context: read {out['context']['read_GBps']:.0f} GB/s, "
             f"copy {out['context']['copy_GBps']:.0f} GB/s")
     if run_p and not args.no_cpu_baseline:
-        log("[bench] timing the fp64 oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(wp)
+        log("[bench] fp64 oracle on the host cores: CPU baseline and parity of the timed calls")
+        out.update(oracle_leg(wp, wd, got_prefill, got_decode))
+    log(f"[bench] {no_children_left()}")
     print(json.dumps(out), flush=True)
 
 
