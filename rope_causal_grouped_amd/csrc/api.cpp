@@ -119,7 +119,7 @@ int64_t prefill_lpad(int64_t L) { return (L + gqa::kPrefillTileK - 1) / gqa::kPr
 
 // workspace pieces of gqa_prefill
 struct PrefillWs {
-  size_t cs_off, kp_off, vt_off, kmax_off, total;
+  size_t cs_off, kp_off, vt_off, kmax_off, kexp_off, total;
 };
 
 PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
@@ -130,21 +130,27 @@ PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
   if (in_dtype == GQA_BF16) {
     const size_t kp = align256((size_t)B * h_kv * prefill_lpad(L) * d * 2);
     w.vt_off = cs + kp;
+    const size_t tiles = align256((size_t)B * h_kv * (prefill_lpad(L) / gqa::kPrefillTileK) * 4);
     w.kmax_off = cs + 2 * kp;
-    w.total = w.kmax_off + align256((size_t)B * h_kv * (prefill_lpad(L) / gqa::kPrefillTileK) * 4);
+    w.kexp_off = w.kmax_off + tiles;
+    w.total = w.kexp_off + tiles;
   } else {
     const size_t kp = align256((size_t)B * h_kv * L * d * 4);
     w.vt_off = cs + kp;
     w.kmax_off = cs + kp;
+    w.kexp_off = cs + kp;
     w.total = cs + kp;
   }
   return w;
 }
 
 struct DecodeWs {
-  size_t m_off, l_off, o_off, total;
+  size_t m_off, l_off, o_off, qr_off, tk_off, total;
 };
 
+// partial states per (b, u, chunk, head); rotated queries [B, h_q, d] (fp32
+// size, so one layout serves both input types); one ticket per (b, u, head
+// block of 16)
 DecodeWs decode_ws(int64_t B, int h_q, int h_kv, int d, int64_t cap) {
   const int g = h_q / h_kv;
   const size_t n = (size_t)B * h_kv * gqa::decode_num_splits(cap) * g;
@@ -152,8 +158,16 @@ DecodeWs decode_ws(int64_t B, int h_q, int h_kv, int d, int64_t cap) {
   w.m_off = 0;
   w.l_off = align256(n * 4);
   w.o_off = w.l_off + align256(n * 4);
-  w.total = w.o_off + align256(n * (size_t)d * 4);
+  w.qr_off = w.o_off + align256(n * (size_t)d * 4);
+  w.tk_off = w.qr_off + align256((size_t)B * h_q * d * 4);
+  w.total = w.tk_off + align256((size_t)B * h_kv * ((g + 15) / 16) * 4);
   return w;
+}
+
+gqa::DecodeWsPtrs decode_ws_ptrs(void* workspace, const DecodeWs& ws) {
+  char* b = (char*)workspace;
+  return {(float*)(b + ws.m_off), (float*)(b + ws.l_off), (float*)(b + ws.o_off),
+          (void*)(b + ws.qr_off), (int*)(b + ws.tk_off)};
 }
 
 }  // namespace
@@ -228,13 +242,15 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     uint16_t* kp = (uint16_t*)(wsb + ws.kp_off);
     uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
     float* kmax = (float*)(wsb + ws.kmax_off);
+    int* kexp = (int*)(wsb + ws.kexp_off);
     e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, cs, kp, vt, kmax,
-                                    (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad, h_kv, d,
-                                    cap, L, nullptr, nullptr, L, st);
+                                    kexp, (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad,
+                                    h_kv, d, cap, L, nullptr, nullptr, L, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     if (ev.first) (void)hipEventRecord(ev.first, st);
-    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, cs, o, out_dtype == GQA_BF16, B, L,
-                                 Lpad, h_q, h_kv, d, scale, causal, nullptr, nullptr, L, st);
+    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, kexp, cs, o,
+                                 out_dtype == GQA_BF16, B, L, Lpad, h_q, h_kv, d, scale, causal,
+                                 nullptr, nullptr, L, st);
   } else {
     const gqa::KvStrides vsd{L * h_kv * d, d, (int64_t)h_kv * d};       // [B, L, h_kv, d]
     if (k_cache) {   // rotated K and V into the cache; attention reads the rotated copy
@@ -288,7 +304,7 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                 "kv_len=%lld > q_pos+1=%lld: the query may only see keys at or before its position",
                 (long long)kv_len, (long long)(q_pos + 1));
   if (cap > (INT64_C(1) << 30) || q_pos > (INT64_C(1) << 40) || B > 65535 || h_q > 65535 ||
-      gqa::decode_num_splits(cap) > gqa::kDecodeMaxSplitsLds)
+      gqa::decode_num_splits(cap) > gqa::kDecodeMaxSplits)
     return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
       !aligned16(workspace))
@@ -297,16 +313,26 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   if (!workspace || workspace_bytes < ws.total)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
                 workspace ? workspace_bytes : (size_t)0);
-  char* wsb = (char*)workspace;
+  gqa::DecodeArgs a{};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.o = o;
+  a.in_bf16 = in_dtype == GQA_BF16;
+  a.out_bf16 = out_dtype == GQA_BF16;
+  a.B = B;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.d = d;
+  a.cap = cap;
+  a.kv_len = kv_len;
+  a.q_pos = q_pos;
+  a.rp = rope_params(theta, d);
+  a.scale = scale;
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   if (g_timing.on) ev = g_timing.take();
-  hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
-                                    out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, kv_len, q_pos,
-                                    nullptr, nullptr, 0, 0, nullptr, 0, 0, 0,
-                                    rope_params(theta, d), scale,
-                                    (float*)(wsb + ws.m_off),
-                                    (float*)(wsb + ws.l_off), (float*)(wsb + ws.o_off),
-                                    (hipStream_t)stream, ev.first, ev.second);
+  hipError_t e = gqa::launch_decode(a, decode_ws_ptrs(workspace, ws), (hipStream_t)stream,
+                                    ev.first, ev.second);
   if (ev.first) g_timing.rec[1].push_back(ev);
   return e == hipSuccess ? GQA_OK : hip_fail(e, "decode launch");
 }
@@ -373,13 +399,14 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
     uint16_t* kp = (uint16_t*)(wsb + ws.kp_off);
     uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
     float* kmax = (float*)(wsb + ws.kmax_off);
+    int* kexp = (int*)(wsb + ws.kexp_off);
     e = gqa::launch_kv_prepare_bf16((const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
-                                    kp, vt, kmax, nullptr, nullptr, B, C, Lpad, h_kv, d, cap, cap,
-                                    start, len, kend, st);
+                                    kp, vt, kmax, kexp, nullptr, nullptr, B, C, Lpad, h_kv, d, cap,
+                                    cap, start, len, kend, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     // 3) the chunk's queries against them
     if (ev.first) (void)hipEventRecord(ev.first, st);
-    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, q_rotated ? nullptr : cs, o,
+    e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, kexp, q_rotated ? nullptr : cs, o,
                                  out_dtype == GQA_BF16, B, C, Lpad, h_q, h_kv, d, scale, 1, start,
                                  len, kend, st);
   } else {
@@ -415,7 +442,7 @@ int decode_ragged_check(const void* q, const void* k_cache, const void* v_cache,
     return fail(GQA_ERR_INVALID_ARG, "longest sequence %lld outside [1, cap=%lld]",
                 (long long)max_kv_len, (long long)cap);
   if (cap > (INT64_C(1) << 30) || B > 65535 || h_q > 65535 ||
-      gqa::decode_num_splits(cap) > gqa::kDecodeMaxSplitsLds)
+      gqa::decode_num_splits(cap) > gqa::kDecodeMaxSplits)
     return fail(GQA_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
       !aligned16(workspace))
@@ -427,23 +454,46 @@ int decode_ragged_check(const void* q, const void* k_cache, const void* v_cache,
   return GQA_OK;
 }
 
-// dispatch of a checked ragged decode
+// dispatch of a checked ragged decode; k_new / v_new set: the new token is
+// appended at q_pos[b] first (if q_pos[b] < append_end)
 int decode_ragged_launch(const void* q, const void* k_cache, const void* v_cache, void* o,
                          int in_dtype, int out_dtype, int64_t B, int h_q, int h_kv, int d,
                          int64_t cap, const int64_t* kvl, const int64_t* qpos, int from_pos,
                          int q_rotated, int64_t max_kv_len, double theta, float scale,
                          void* workspace, hipStream_t st, const int32_t* bt = nullptr,
-                         int ps_log2 = 0, int64_t max_pages = 0, int64_t num_pages = 0) {
+                         int ps_log2 = 0, int64_t max_pages = 0, int64_t num_pages = 0,
+                         const void* k_new = nullptr, const void* v_new = nullptr,
+                         int64_t append_end = 0) {
   const DecodeWs ws = decode_ws(B, h_q, h_kv, d, cap);
-  char* wsb = (char*)workspace;
+  gqa::DecodeArgs a{};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.o = o;
+  a.in_bf16 = in_dtype == GQA_BF16;
+  a.out_bf16 = out_dtype == GQA_BF16;
+  a.B = B;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.d = d;
+  a.cap = cap;
+  a.kv_len = max_kv_len;
+  a.kvl_arr = kvl;
+  a.qpos_arr = qpos;
+  a.kvl_from_pos = from_pos;
+  a.q_rotated = q_rotated;
+  a.bt = bt;
+  a.ps_log2 = ps_log2;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.append_end = append_end;
+  a.rp = rope_params(theta, d);
+  a.scale = scale;
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   if (g_timing.on) ev = g_timing.take();
-  hipError_t e = gqa::launch_decode(q, k_cache, v_cache, o, in_dtype == GQA_BF16,
-                                    out_dtype == GQA_BF16, B, h_q, h_kv, d, cap, max_kv_len, 0,
-                                    kvl, qpos, from_pos, q_rotated, bt, ps_log2, max_pages,
-                                    num_pages, rope_params(theta, d), scale,
-                                    (float*)(wsb + ws.m_off), (float*)(wsb + ws.l_off),
-                                    (float*)(wsb + ws.o_off), st, ev.first, ev.second);
+  hipError_t e = gqa::launch_decode(a, decode_ws_ptrs(workspace, ws), st, ev.first, ev.second);
   if (ev.first) g_timing.rec[1].push_back(ev);
   return e == hipSuccess ? GQA_OK : hip_fail(e, "decode launch");
 }
@@ -484,15 +534,11 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
   if (int rc = decode_ragged_check(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d,
                                    cap, max_pos + 1, theta, scale, workspace, workspace_bytes))
     return rc;
-  hipStream_t st = (hipStream_t)stream;
-  // 1) the new token's rotated K and its V into cache row pos[b]
-  hipError_t e = gqa::launch_cache_append(k_new, v_new, k_cache, v_cache, in_dtype == GQA_BF16,
-                                          pos, nullptr, B, 1, h_kv, d, cap, max_pos + 1,
-                                          rope_params(theta, d), st);
-  if (e != hipSuccess) return hip_fail(e, "cache append launch");
-  // 2) attend to rows 0 .. pos[b]
+  // the new token's rotated K and its V go to cache row pos[b] (preparation
+  // kernel), then it attends to rows 0 .. pos[b]
   return decode_ragged_launch(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap,
-                              nullptr, pos, 1, 0, max_pos + 1, theta, scale, workspace, st);
+                              nullptr, pos, 1, 0, max_pos + 1, theta, scale, workspace,
+                              (hipStream_t)stream, nullptr, 0, 0, 0, k_new, v_new, max_pos + 1);
 }
 
 size_t gqa_decode_paged_workspace_size(int64_t B, int h_q, int h_kv, int d,
@@ -531,21 +577,15 @@ int gqa_decode_paged(const void* q, const void* k_new, const void* v_new, void* 
                                    max_kv_len, max_kv_len, theta, scale, workspace,
                                    workspace_bytes))
     return rc;
-  const int64_t reach = max_pages * page_size;
-  hipStream_t st = (hipStream_t)stream;
   int ps_log2 = 0;
   while ((1 << ps_log2) < page_size) ++ps_log2;
-  if (append) {   // the new token's rotated K and its V at position q_pos[b]
-    hipError_t e = gqa::launch_cache_append(k_new, v_new, k_pool, v_pool, in_dtype == GQA_BF16,
-                                            q_pos, nullptr, B, 1, h_kv, d, reach, max_kv_len,
-                                            rope_params(theta, d), st, block_table, ps_log2,
-                                            max_pages, num_pages);
-    if (e != hipSuccess) return hip_fail(e, "paged append launch");
-  }
+  // with append, the new token's rotated K and its V go to position q_pos[b]
+  // first (preparation kernel)
   return decode_ragged_launch(q, k_pool, v_pool, o, in_dtype, out_dtype, B, h_q, h_kv, d,
                               max_kv_len, kv_len, q_pos, append ? 1 : 0, q_rotated != 0,
-                              max_kv_len, theta, scale, workspace, st, block_table, ps_log2,
-                              max_pages, num_pages);
+                              max_kv_len, theta, scale, workspace, (hipStream_t)stream,
+                              block_table, ps_log2, max_pages, num_pages, k_new, v_new,
+                              max_kv_len);
 }
 
 int gqa_qkv_epilogue(const void* qkv, const void* bias, void* q_out, void* k_cache,

@@ -7,6 +7,7 @@
 namespace gqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -66,6 +67,16 @@ __device__ __forceinline__ void rope_cs(double pos, int j, int d, const RopePara
   rope_cos_sin(pos, rope_omega(j, d, rp), c, s);
   c *= rp.mscale;
   s *= rp.mscale;
+}
+
+// Power of two that score operands with largest magnitude amax are divided
+// by before rounding to fp16: 0 below 2^14, else the smallest e with
+// amax * 2^-e < 2^14, so the operands stay finite (fp16 ends at 65504).
+__device__ __forceinline__ int kexp_of(float amax) {
+  if (!(amax >= 16384.0f)) return 0;
+  int e;
+  (void)frexpf(amax, &e);   // amax < 2^e
+  return e - 14;
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

@@ -13,7 +13,7 @@ constexpr int kPrefillTileK = 64;      // key padding granule of the prepared K/
 constexpr int kPrefillTileV = 32;      // keys per attention tile; V^T is stored per such tile
 constexpr int kPrefillRowsWG = 256;    // stacked (position, head) rows per workgroup
 constexpr int kDecodeChunk = 1024;     // keys per decode split
-constexpr int kDecodeMaxSplitsLds = 8192;  // chunk weights staged by the merge kernel
+constexpr int kDecodeMaxSplits = 8192;  // bound on the chunks of one sequence (8M keys)
 
 hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,
                              RopeParams rp, hipStream_t st);
@@ -22,10 +22,11 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, RopePar
                              hipStream_t st);
 
 hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
-                                  uint16_t* kp, uint16_t* vt, float* kmax, uint16_t* kc,
-                                  uint16_t* vc, int64_t B, int64_t L, int64_t Lpad, int h_kv, int d,
-                                  int64_t cap, int64_t src_rows, const int64_t* kstart,
-                                  const int64_t* klen, int64_t kend, hipStream_t st);
+                                  uint16_t* kp, uint16_t* vt, float* kmax, int* kexp,
+                                  uint16_t* kc, uint16_t* vc, int64_t B, int64_t L, int64_t Lpad,
+                                  int h_kv, int d, int64_t cap, int64_t src_rows,
+                                  const int64_t* kstart, const int64_t* klen, int64_t kend,
+                                  hipStream_t st);
 
 hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* cs, float* kp,
                                  float* kc, float* vc, int64_t B, int64_t L, int h_kv, int d,
@@ -45,7 +46,8 @@ hipError_t launch_qkv_epilogue(const void* x, const void* bias, void* q_out, voi
                                RopeParams rp, hipStream_t st);
 
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
-                               const float* kmax, const float2* cs, void* o, int out_bf16,
+                               const float* kmax, const int* kexp, const float2* cs, void* o,
+                               int out_bf16,
                                int64_t B, int64_t L, int64_t Lpad, int h_q, int h_kv, int d,
                                float scale, int causal, const int64_t* qstart,
                                const int64_t* qlen, int64_t kend, hipStream_t st);
@@ -67,13 +69,46 @@ hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, c
 
 int decode_num_splits(int64_t kv_len);
 
-hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, int in_bf16,
-                         int out_bf16, int64_t B, int h_q, int h_kv, int d, int64_t cap,
-                         int64_t kv_len, int64_t q_pos, const int64_t* kvl_arr,
-                         const int64_t* qpos_arr, int kvl_from_pos, int q_rotated,
-                         const int32_t* bt, int ps_log2, int64_t max_pages, int64_t num_pages,
-                         RopeParams rp,
-                         float scale, float* ws_m, float* ws_l, float* ws_o, hipStream_t st,
+// One decode call.  Scalar kv_len / q_pos, or per-sequence arrays (then
+// kv_len bounds every length and sets the chunk count); k_new / v_new set:
+// the new token of sequence b is appended at qpos_arr[b] first (if it lies
+// in [0, append_end)), and kvl_from_pos makes its length qpos_arr[b] + 1.
+// bt set: kc / vc are page pools [num_pages, h_kv, 2^ps_log2, d] addressed
+// through the block table bt [B][max_pages].
+struct DecodeArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  void* o;
+  int in_bf16, out_bf16;
+  int64_t B;
+  int h_q, h_kv, d;
+  int64_t cap, kv_len, q_pos;
+  const int64_t* kvl_arr;
+  const int64_t* qpos_arr;
+  int kvl_from_pos, q_rotated;
+  const int32_t* bt;
+  int ps_log2;
+  int64_t max_pages, num_pages;
+  const void* k_new;
+  const void* v_new;
+  int64_t append_end;
+  RopeParams rp;
+  float scale;
+};
+
+// Workspace pieces of a decode call: partial states per (b, u, chunk, head)
+// (max m, sum l, unnormalised o[d]), the rotated queries [B, h_q, d] in the
+// input type, and one arrival ticket per (b, u, head block of 16).
+struct DecodeWsPtrs {
+  float* m;
+  float* l;
+  float* o;
+  void* qr;
+  int* tickets;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t st,
                          hipEvent_t ev_begin, hipEvent_t ev_end);
 
 // streaming read of `bytes` (a multiple of 16) at p, for benchmark context

@@ -1,5 +1,5 @@
-// Causal GQA prefill on bf16 matrix cores (gfx950), RoPE fused into the Q
-// load, fp32 accumulation, online softmax.
+// Causal GQA prefill on the matrix cores (gfx950) for bf16 inputs, RoPE
+// fused into the Q load, fp32 accumulation, online softmax.
 //
 // What it computes (Qwen2 technical-report walkthrough, aicoding.csdn.net,
 // §4.1.3 steps 3-4): for query head t and its KV group u = t / g,
@@ -16,12 +16,20 @@
 // them: the g-fold K/V reuse GQA offers (same page, closing note of §4.1.3).
 // Eight waves own 32 rows each, two waves per SIMD.
 //
-// Per 64-key tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// Per 64-key tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_f16
 // (K from LDS as the A operand, the wave's rotated Q rows resident in VGPRs
 // as the B operand), so each lane holds half of one query row's scores.  The
-// probabilities, rounded to bf16, are already in the B-operand layout of
-// O^T += V^T P^T; V arrives pre-transposed (keys contiguous, in the
-// accumulator's lane order) from the preparation pass, in 32-key sub-tiles.
+// rotated rows are rounded once to fp16 for this product: their 11-bit
+// significand keeps the logits of large rows (the 32K workload's rows scaled
+// by 8) within the bf16 tolerance, where bf16-rounded Q' and K' do not, at
+// the same matrix-core rate.  Q' carries scale * log2(e), so scores come out
+// in log2 units.  An operand row or tile whose largest element reaches 2^14
+// is stored divided by a power of two (fp16 ends at 65504) and its scores
+// are multiplied back before the softmax; ordinary inputs never take that
+// path.  The probabilities, rounded to bf16, are already in the B-operand
+// layout of O^T += V^T P^T on v_mfma_f32_32x32x16_bf16; V arrives
+// pre-transposed (keys contiguous, in the accumulator's lane order) from the
+// preparation pass, in 32-key sub-tiles.
 //
 // Ping-pong schedule.  Each wave alternates between a matrix phase (P.V of
 // tile i-1, then S^T of tile i) and a vector phase (softmax of tile i).
@@ -84,16 +92,16 @@ __device__ __forceinline__ float bf16x8_sum(const bf16x8 v, float acc) {
 
 }  // namespace
 
-// PRE: the kernel rotates Q itself (cs set) and folds scale * log2(e) into
-// it before the one bf16 rounding; a probability is then a bare exp2 of the
-// score while every row of the wave has m = 0, and exp2(s - m) otherwise.
-// Without PRE (Q arrives rotated and rounded) the scale is applied to each
-// score instead, so Q is rounded only once.
+// PRE: the kernel rotates Q itself (cs set); otherwise Q arrives rotated
+// (bf16).  Either way scale * log2(e) is folded into Q' before its one fp16
+// rounding; a probability is then a bare exp2 of the score while every row
+// of the wave has m = 0, and exp2(s - m) otherwise.
 template <int D, bool OUT_BF16, bool PRE>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vt, const float* __restrict__ kmax,
-    const float2* __restrict__ cs, void* __restrict__ o, int L, int Lpad, int h_q, int h_kv,
+    const int* __restrict__ kexp, const float2* __restrict__ cs, void* __restrict__ o, int L,
+    int Lpad, int h_q, int h_kv,
     int g, int n_rb, int n_bu, float sl2, int causal, const int64_t* __restrict__ qstart,
     const int64_t* __restrict__ qlen, int kend) {
   constexpr int NS = D / 16;                  // 16-dim k-steps of S^T
@@ -116,6 +124,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ks0[TK * D], ks1[TK * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs0[TK * D], vs1[TK * D];
   __shared__ float wred[NW];
+  __shared__ int wexp[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -238,7 +247,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // row and its cos/sin, then the first tiles straight into LDS.
   const int n = n_tiles;
   const float* kmax_bu = kmax + (int64_t)bu * (Lpad / TK);
+  const int* kexp_bu = kexp + (int64_t)bu * (Lpad / TK);
   float km = tid < n_tiles ? kmax_bu[tid] : 0.f;
+  int kx = tid < n_tiles ? kexp_bu[tid] : 0;
   const uint16_t* qrow = q + ((int64_t)((int64_t)b * L + pl) * h_q + head) * D;
   u32x4 raw[NS];
 #pragma unroll
@@ -257,42 +268,50 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // K(0) by waves 4-7 (the first barrier publishes it)
   if (grp) load_tile(ks0, 0);
 
-  // ---- Q row: rotate at pos, round to bf16 (B operand layout: lane holds
-  // dims s*16 + hl*8 + e of its row; RoPE pairs are (s, s + NS/2)); done
-  // after the first barrier, when its reads have long arrived.
-  bf16x8 qb[NS];
-  float qcap;
-  auto rotate_q = [&] {
-  if constexpr (PRE) {
-#pragma unroll
-    for (int s = 0; s < NS / 2; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float cr = c4[s][e >> 1][(e & 1) * 2], sr = c4[s][e >> 1][(e & 1) * 2 + 1];
-        const uint32_t w1 = raw[s][e >> 1], w2 = raw[s + NS / 2][e >> 1];
-        const float x1 = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
-        const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);
-        qb[s][e] = (__bf16)(fmaf(x1, cr, -x2 * sr) * sl2);
-        qb[s + NS / 2][e] = (__bf16)(fmaf(x2, cr, x1 * sr) * sl2);
-      }
+  // ---- Q row: rotate at pos, fold in scale * log2(e), divide by 2^eq when
+  // the row's largest element reaches 2^14, round to fp16 (B operand
+  // layout: lane holds dims s*16 + hl*8 + e of its row; RoPE pairs are
+  // (s, s + NS/2)); done after the first barrier, when its reads have long
+  // arrived.
+  f16x8 qb[NS];
+  float qcap;      // bound on |q'| in score units, with a margin for rounding
+  float qfac;      // 2^eq: multiplies this row's scores back (slow path only)
+  bool qslow;      // some row of the wave has eq != 0 (wave-uniform)
+  auto q_elem = [&](int s, int e) -> float {   // element (s, e) of Q' * scale * log2(e)
+    const uint32_t w1 = raw[s][e >> 1];
+    const float x = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
+    if constexpr (PRE) {
+      const int sp = s < NS / 2 ? s + NS / 2 : s - NS / 2;   // the pair's other half
+      const uint32_t w2 = raw[sp][e >> 1];
+      const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);
+      const int s4 = s < NS / 2 ? s : s - NS / 2;
+      const float cr = c4[s4][e >> 1][(e & 1) * 2], sr = c4[s4][e >> 1][(e & 1) * 2 + 1];
+      return (s < NS / 2 ? fmaf(x, cr, -x2 * sr) : fmaf(x, cr, x2 * sr)) * sl2;
+    } else {
+      return x * sl2;
     }
-  } else {   // rotated already
+  };
+  auto rotate_q = [&] {
+    float amax = 0.f;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qb[s] = __builtin_bit_cast(bf16x8, raw[s]);
-  }
-  // |q'| of the row from the bf16 values the matrix cores see, in score
-  // units (scale * log2 e), with a margin for fp32 rounding
-  {
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q_elem(s, e)));
+    const int eq = kexp_of(max_xor32(amax));
+    const float down = __builtin_ldexpf(1.0f, -eq);
     float ss = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (float)qb[s][e];
-        ss = fmaf(x, x, ss);
+        const _Float16 h = (_Float16)(q_elem(s, e) * down);
+        qb[s][e] = h;
+        ss = fmaf((float)h, (float)h, ss);
       }
-    qcap = sqrtf(sum_xor32(ss)) * (PRE ? 1.f : sl2) * 1.01f;
-  }
+    qfac = __builtin_ldexpf(1.0f, eq);
+    qslow = __builtin_amdgcn_ballot_w64(eq != 0) != 0;
+    // |q'| of the row from the fp16 values the matrix cores see
+    qcap = sqrtf(sum_xor32(ss)) * qfac * 1.01f;
   };
 
   // ---- operand read offsets (elements), swizzled like the stores
@@ -335,16 +354,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   };
   auto read_k = [&](const uint16_t* kt0, const int (&kr)[NS], int j) {
     const int s = j / 2, c = j % 2;
-    return *(const bf16x8*)((const char*)kt0 + c * 32 * D * 2 + kr[s]);
+    return __builtin_bit_cast(bf16x8,
+                              *(const f16x8*)((const char*)kt0 + c * 32 * D * 2 + kr[s]));
   };
   auto mma_pv = [&](const bf16x8 a, int j) {
     const int kb = j / (2 * NDB), hs = (j / NDB) % 2, db = j % NDB;
     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][hs], oacc[db], 0, 0, 0);
   };
-  auto mma_qk = [&](const bf16x8 a, int j) {
+  auto mma_qk = [&](const bf16x8 a, int j) {   // a: an fp16 K' fragment (16 bytes)
     const int s = j / 2, c = j % 2;
-    sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        a, qb[s], s == 0 ? zero16 : sacc[c], 0, 0, 0);
+    sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        __builtin_bit_cast(f16x8, a), qb[s], s == 0 ? zero16 : sacc[c], 0, 0, 0);
   };
   // P.V of tile i-1 and S^T of tile i (P = i mod 2)
   auto matrix_full = [&](auto P) {
@@ -397,20 +417,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
   };
-  // SH: the reference m of some row in the wave is not 0 (PRE only)
+  // SH: the reference m of some row in the wave is not 0
   auto probs = [&](const f32x16& s0, const f32x16& s1, auto SH) {
     float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if constexpr (PRE && !decltype(SH)::value) {
+      if constexpr (!decltype(SH)::value) {
         pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[e]);
         pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[e]);
-      } else if constexpr (PRE) {
+      } else {
         pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s0[e] - m_run);
         pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(s1[e] - m_run);
-      } else {
-        pb[0][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s0[e], sl2, -m_run));
-        pb[1][e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s1[e], sl2, -m_run));
       }
     }
     acc0 = bf16x8_sum(pb[0][0], acc0);
@@ -420,6 +437,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     return acc0 + acc1;
   };
   float crow = 0.f;   // bound on this row's scores, score units (set after the prologue)
+  bool kslow = false;   // some key tile of the workgroup has kexp != 0 (uniform)
   float m_raise = 0.f;  // raise of m owed by the previous tile's large sum (applied lazily)
   auto vector_phase = [&](int i) {
     if (!active(i)) {   // keys beyond this wave's rows: contribute nothing
@@ -435,6 +453,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     // compiler then keeps every MFMA accumulator in VGPRs, and the vector
     // ALU reads the scores without copies)
     f32x16 s0 = sacc[0], s1 = sacc[1];
+    if (qslow || kslow) {   // operands stored divided by powers of two: scores back to scale
+      float f = qfac;
+      if (kslow) f = __builtin_ldexpf(f, kexp_bu[i]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s0[e] *= f;
+        s1[e] *= f;
+      }
+    }
     if (masked(i)) {
       // key of score e: i*TK + (e>>2)*8 + hl*4 + (e&3) (+32 for s1); compared
       // as a constant offset against the row's limit within the tile
@@ -453,12 +480,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-      mx = PRE ? max_xor32(mx) : max_xor32(mx) * sl2;
+      mx = max_xor32(mx);
       if (mx > m_new + kRescaleThreshold) m_new = mx;
     }
     if (__builtin_amdgcn_ballot_w64(m_new != m_run)) rescale(m_new);
     float psum;
-    if (PRE && __builtin_amdgcn_ballot_w64(m_run != 0.f))
+    if (__builtin_amdgcn_ballot_w64(m_run != 0.f))
       psum = probs(s0, s1, std::true_type{});
     else
       psum = probs(s0, s1, std::false_type{});
@@ -473,17 +500,27 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // ---- prologue part 2: largest K norm this workgroup will see (per-tile
   // norms from the preparation pass; more than one per thread only past
   // 32768 keys); K(0) resident, bound known
-  for (int t = tid + NW * 64; t < n_tiles; t += NW * 64) km = fmaxf(km, kmax_bu[t]);
+  for (int t = tid + NW * 64; t < n_tiles; t += NW * 64) {
+    km = fmaxf(km, kmax_bu[t]);
+    kx = max(kx, kexp_bu[t]);
+  }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) km = wave_max_xor(km, m);
+  if (__builtin_amdgcn_ballot_w64(kx != 0) != 0 && lane == 0) wexp[wave] = 1;
+  else if (lane == 0) wexp[wave] = 0;
   if (lane == 0) wred[wave] = km;
   bar();
   rotate_q();
   {
     float km = wred[0];
+    int any = wexp[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) km = fmaxf(km, wred[w]);
+    for (int w = 1; w < NW; ++w) {
+      km = fmaxf(km, wred[w]);
+      any |= wexp[w];
+    }
     crow = qcap * km;
+    kslow = __builtin_amdgcn_readfirstlane(any) != 0;
   }
   // a bound within the headroom makes 0 a valid reference from the start
   // (every score lies in [-crow, crow]), which the scores need no shift for
@@ -566,7 +603,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 }
 
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
-                               const float* kmax, const float2* cs, void* o, int out_bf16,
+                               const float* kmax, const int* kexp, const float2* cs, void* o,
+                               int out_bf16,
                                int64_t B, int64_t L, int64_t Lpad, int h_q, int h_kv, int d,
                                float scale, int causal, const int64_t* qstart,
                                const int64_t* qlen, int64_t kend, hipStream_t st) {
@@ -580,7 +618,7 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   const int ppx = n_bu * s_parts / kXcds;
   const unsigned grid = (unsigned)((int64_t)kXcds * ppx * ((n_rb + s_parts - 1) / s_parts));
 #define GQA_LAUNCH(DD, OB, PR)                                                               \
-  prefill_bf16_kernel<DD, OB, PR><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, cs, o, (int)L,  \
+  prefill_bf16_kernel<DD, OB, PR><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, kexp, cs, o, (int)L, \
                                                             (int)Lpad, h_q, h_kv, g, n_rb,   \
                                                             n_bu, sl2, causal, qstart, qlen, \
                                                             (int)kend)

@@ -86,35 +86,42 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, RopePar
 // ---------------------------------------------------------------------------
 // K/V preparation for the bf16 prefill.  One workgroup per (64-key tile,
 // KV group u, batch b):
-//   kp[b][u][key][:]   rotated K, bf16, keys contiguous per group (a 64-key
-//                      tile is one contiguous 16 KB block for d = 128);
-//   kmax[b][u][tile]   the largest rotated-K row norm of the tile (an upper
-//                      bound on its scores for a given query norm);
+//   kp[b][u][key][:]   rotated K as fp16 (the score operand: its 11-bit
+//                      significand keeps the logits of large rows within
+//                      the bf16 tolerance, where bf16 K' would not), times
+//                      2^-kexp of the tile; keys contiguous per group (a
+//                      64-key tile is one contiguous 16 KB block, d = 128);
+//   kexp[b][u][tile]   0, or the power of two the tile was divided by when
+//                      its largest element reached 2^14 (fp16 stays finite);
+//   kmax[b][u][tile]   the largest row norm of the tile's stored K' (times
+//                      2^kexp): an upper bound on its scores for a given
+//                      query norm;
 //   vt[b][u][t32][dim][32] V transposed per 32-key attention tile, so the
 //                      attention kernel's P.V operand reads consecutive keys
 //                      of one dim; inside each 16-key group the keys are
 //                      stored in the order 0-3, 8-11, 4-7, 12-15, which is
 //                      the order in which one lane of the 32x32 score
 //                      accumulator holds them.
-// Rows past L are zero.  If kc/vc are set, the rotated K and the V rows are
-// also written to the per-layer cache [B, cap, h_kv, d].  The source rows of
-// sequence b start at k + b * src_rows * h_kv * d (src_rows = L for the
-// call's own K/V, cap for a cache).  With kstart set, sequence b has
-// kstart[b] + klen[b] rows (0 if that is not within [0, kend]); with cs NULL
-// the source K is taken as already rotated (a cache).
+// Rows past L are zero.  If kc/vc are set, the rotated K (bf16, rounded once
+// from the fp32 rotation) and the V rows are also written to the per-layer
+// cache [B, cap, h_kv, d].  The source rows of sequence b start at
+// k + b * src_rows * h_kv * d (src_rows = L for the call's own K/V, cap for a
+// cache).  With kstart set, sequence b has kstart[b] + klen[b] rows (0 if
+// that is not within [0, kend]); with cs NULL the source K is taken as
+// already rotated (a cache).
 template <int D>
 __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float2* __restrict__ cs,
     uint16_t* __restrict__ kp, uint16_t* __restrict__ vt, float* __restrict__ kmax,
-    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t L, int64_t Lpad, int h_kv,
-    int64_t cap, int64_t src_rows, const int64_t* __restrict__ kstart,
+    int* __restrict__ kexp, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t L,
+    int64_t Lpad, int h_kv, int64_t cap, int64_t src_rows, const int64_t* __restrict__ kstart,
     const int64_t* __restrict__ klen, int64_t kend) {
   constexpr int TK = 64;
   constexpr int HALF = D / 2;
   constexpr int PP = HALF / 4;        // RoPE pairs per thread: 4 threads per key row
   constexpr int TV = kPrefillTileV;
   __shared__ __attribute__((aligned(16))) uint16_t vs[TK][D + 8];
-  __shared__ float wmax[4];
+  __shared__ float wred[4];
   const int tile = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t key0 = (int64_t)tile * TK;
@@ -122,81 +129,97 @@ __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
     const int64_t s0 = kstart[b], n = klen ? klen[b] : L;
     L = (s0 >= 0 && n >= 0 && n <= L && s0 + n <= kend) ? s0 + n : 0;
   }
-  {
-    const int kk = tid >> 2, part = tid & 3;
-    const int64_t key = key0 + kk;
-    uint16_t o1[PP], o2[PP];
-    float ss = 0.f;
-    if (key < L) {
-      const uint16_t* src = k + (((int64_t)b * src_rows + key) * h_kv + u) * D + part * PP;
-      uint16_t x1[PP], x2[PP];
+  const int kk = tid >> 2, part = tid & 3;
+  const int64_t key = key0 + kk;
+  // ---- this thread's quarter of a K row, rotated (or as given), in fp32
+  float y1[PP], y2[PP];
+  float amax = 0.f;
+  if (key < L) {
+    const uint16_t* src = k + (((int64_t)b * src_rows + key) * h_kv + u) * D + part * PP;
+    uint16_t x1[PP], x2[PP];
 #pragma unroll
-      for (int c = 0; c < PP / 8; ++c) {
-        *(u32x4*)&x1[c * 8] = *(const u32x4*)(src + c * 8);
-        *(u32x4*)&x2[c * 8] = *(const u32x4*)(src + HALF + c * 8);
-      }
-      if (cs) {   // rotate here; otherwise the source rows are rotated already
-        const float2* csr = cs + key * HALF + part * PP;
-#pragma unroll
-        for (int e = 0; e < PP; ++e) {
-          const float2 r = csr[e];
-          const float a = bf16_bits_to_f32(x1[e]), bb = bf16_bits_to_f32(x2[e]);
-          o1[e] = f32_to_bf16_bits(fmaf(a, r.x, -bb * r.y));
-          o2[e] = f32_to_bf16_bits(fmaf(bb, r.x, a * r.y));
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < PP; ++e) {
-          o1[e] = x1[e];
-          o2[e] = x2[e];
-        }
-      }
+    for (int c = 0; c < PP / 8; ++c) {
+      *(u32x4*)&x1[c * 8] = *(const u32x4*)(src + c * 8);
+      *(u32x4*)&x2[c * 8] = *(const u32x4*)(src + HALF + c * 8);
+    }
+    if (cs) {   // rotate here; otherwise the source rows are rotated already
+      const float2* csr = cs + key * HALF + part * PP;
 #pragma unroll
       for (int e = 0; e < PP; ++e) {
-        const float y1 = bf16_bits_to_f32(o1[e]), y2 = bf16_bits_to_f32(o2[e]);
-        ss = fmaf(y1, y1, fmaf(y2, y2, ss));
-      }
-      if (kc) {
-        uint16_t* cdst = kc + (((int64_t)b * cap + key) * h_kv + u) * D + part * PP;
-#pragma unroll
-        for (int c = 0; c < PP / 8; ++c) {
-          *(u32x4*)(cdst + c * 8) = *(const u32x4*)&o1[c * 8];
-          *(u32x4*)(cdst + HALF + c * 8) = *(const u32x4*)&o2[c * 8];
-        }
+        const float2 r = csr[e];
+        const float a = bf16_bits_to_f32(x1[e]), bb = bf16_bits_to_f32(x2[e]);
+        y1[e] = fmaf(a, r.x, -bb * r.y);
+        y2[e] = fmaf(bb, r.x, a * r.y);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < PP; ++e) o1[e] = o2[e] = 0;
+      for (int e = 0; e < PP; ++e) {
+        y1[e] = bf16_bits_to_f32(x1[e]);
+        y2[e] = bf16_bits_to_f32(x2[e]);
+      }
     }
-    uint16_t* kdst = kp + (((int64_t)b * h_kv + u) * Lpad + key) * D + part * PP;
 #pragma unroll
-    for (int c = 0; c < PP / 8; ++c) {
-      *(u32x4*)(kdst + c * 8) = *(const u32x4*)&o1[c * 8];
-      *(u32x4*)(kdst + HALF + c * 8) = *(const u32x4*)&o2[c * 8];
+    for (int e = 0; e < PP; ++e) amax = fmaxf(amax, fmaxf(fabsf(y1[e]), fabsf(y2[e])));
+    if (kc) {   // the cache keeps bf16, rounded once from the fp32 rotation
+      uint16_t o1[PP], o2[PP];
+#pragma unroll
+      for (int e = 0; e < PP; ++e) {
+        o1[e] = f32_to_bf16_bits(y1[e]);
+        o2[e] = f32_to_bf16_bits(y2[e]);
+      }
+      uint16_t* cdst = kc + (((int64_t)b * cap + key) * h_kv + u) * D + part * PP;
+#pragma unroll
+      for (int c = 0; c < PP / 8; ++c) {
+        *(u32x4*)(cdst + c * 8) = *(const u32x4*)&o1[c * 8];
+        *(u32x4*)(cdst + HALF + c * 8) = *(const u32x4*)&o2[c * 8];
+      }
     }
-    // squared row norm (4 threads per row), then the max over the tile's rows
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
+  } else {
 #pragma unroll
-    for (int m = 4; m < 64; m <<= 1) ss = fmaxf(ss, __shfl_xor(ss, m, 64));
-    if ((tid & 63) == 0) wmax[tid >> 6] = ss;
+    for (int e = 0; e < PP; ++e) y1[e] = y2[e] = 0.f;
   }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if ((tid & 63) == 0) wred[tid >> 6] = amax;
 
   // ---- V rows into LDS (and the cache copy), 16 bytes per thread and step
   for (int c = tid; c < TK * D / 8; c += 256) {
-    const int kk = c / (D / 8), c8 = c % (D / 8);
-    const int64_t key = key0 + kk;
+    const int vk = c / (D / 8), c8 = c % (D / 8);
+    const int64_t vkey = key0 + vk;
     u32x4 val = {0u, 0u, 0u, 0u};
-    if (key < L) {
-      val = *(const u32x4*)(v + (((int64_t)b * src_rows + key) * h_kv + u) * D + c8 * 8);
-      if (vc) *(u32x4*)(vc + (((int64_t)b * cap + key) * h_kv + u) * D + c8 * 8) = val;
+    if (vkey < L) {
+      val = *(const u32x4*)(v + (((int64_t)b * src_rows + vkey) * h_kv + u) * D + c8 * 8);
+      if (vc) *(u32x4*)(vc + (((int64_t)b * cap + vkey) * h_kv + u) * D + c8 * 8) = val;
     }
-    *(u32x4*)&vs[kk][c8 * 8] = val;
+    *(u32x4*)&vs[vk][c8 * 8] = val;
   }
   __syncthreads();
-  if (tid == 0)
-    kmax[((int64_t)b * h_kv + u) * (Lpad / TK) + tile] =
-        sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+
+  // ---- the tile's exponent, K' as fp16, and the tile's largest row norm
+  const int ex = kexp_of(fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3])));
+  const float down = __builtin_ldexpf(1.0f, -ex);
+  uint16_t h1[PP], h2[PP];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < PP; ++e) {
+    const _Float16 a = (_Float16)(y1[e] * down), bb = (_Float16)(y2[e] * down);
+    h1[e] = __builtin_bit_cast(uint16_t, a);
+    h2[e] = __builtin_bit_cast(uint16_t, bb);
+    ss = fmaf((float)a, (float)a, fmaf((float)bb, (float)bb, ss));
+  }
+  uint16_t* kdst = kp + (((int64_t)b * h_kv + u) * Lpad + key) * D + part * PP;
+#pragma unroll
+  for (int c = 0; c < PP / 8; ++c) {
+    *(u32x4*)(kdst + c * 8) = *(const u32x4*)&h1[c * 8];
+    *(u32x4*)(kdst + HALF + c * 8) = *(const u32x4*)&h2[c * 8];
+  }
+  // squared row norm (4 threads per row), then the max over the tile's rows
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+#pragma unroll
+  for (int m = 4; m < 64; m <<= 1) ss = fmaxf(ss, __shfl_xor(ss, m, 64));
+  __syncthreads();   // every thread has read wred
+  if ((tid & 63) == 0) wred[tid >> 6] = ss;
 
   // ---- V^T in tiles of TV keys: vt[b][u][key / TV][dim][TV]; each thread
   // writes 8 consecutive (permuted) keys of one dim
@@ -208,10 +231,17 @@ __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int p = p0 + e, pp = p & 15;
-      const int kk = sub * TV + (p & ~15) + ((pp & 7) >> 2) * 8 + (pp >> 3) * 4 + (pp & 3);
-      w[e] = vs[kk][dd];
+      const int vk = sub * TV + (p & ~15) + ((pp & 7) >> 2) * 8 + (pp >> 3) * 4 + (pp & 3);
+      w[e] = vs[vk][dd];
     }
     *(u32x4*)(vdst + (int64_t)c * 8) = *(const u32x4*)w;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int64_t t = ((int64_t)b * h_kv + u) * (Lpad / TK) + tile;
+    kmax[t] = __builtin_ldexpf(sqrtf(fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]))),
+                               ex);
+    kexp[t] = ex;
   }
 }
 
@@ -256,17 +286,20 @@ __global__ __launch_bounds__(256) void kv_prepare_f32_kernel(
 }
 
 hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
-                                  uint16_t* kp, uint16_t* vt, float* kmax, uint16_t* kc,
-                                  uint16_t* vc, int64_t B, int64_t L, int64_t Lpad, int h_kv, int d,
-                                  int64_t cap, int64_t src_rows, const int64_t* kstart,
-                                  const int64_t* klen, int64_t kend, hipStream_t st) {
+                                  uint16_t* kp, uint16_t* vt, float* kmax, int* kexp,
+                                  uint16_t* kc, uint16_t* vc, int64_t B, int64_t L, int64_t Lpad,
+                                  int h_kv, int d, int64_t cap, int64_t src_rows,
+                                  const int64_t* kstart, const int64_t* klen, int64_t kend,
+                                  hipStream_t st) {
   dim3 grid((unsigned)(Lpad / 64), (unsigned)h_kv, (unsigned)B);
   if (d == 128)
-    kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kc, vc, L, Lpad,
-                                                      h_kv, cap, src_rows, kstart, klen, kend);
+    kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kexp, kc, vc, L,
+                                                      Lpad, h_kv, cap, src_rows, kstart, klen,
+                                                      kend);
   else
-    kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kc, vc, L, Lpad,
-                                                     h_kv, cap, src_rows, kstart, klen, kend);
+    kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kexp, kc, vc, L,
+                                                     Lpad, h_kv, cap, src_rows, kstart, klen,
+                                                     kend);
   return hipGetLastError();
 }
 
