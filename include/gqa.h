@@ -82,8 +82,12 @@ size_t gqa_prefill_workspace_size(int in_dtype, int64_t B, int64_t L,
  *   h_q must be a positive multiple of h_kv (a reversed ratio is rejected,
  *   "Qwen2 / Qwen3 的实测配置差异与三个坑" (docs.keinmal.top) pitfall 2).
  *   d must be 64 or 128 (the head sizes of the Qwen2 size table).
- * bf16 inputs run on bf16 matrix cores with fp32 accumulation; f32 inputs
- * run in fp32 throughout.
+ * bf16 inputs run on the matrix cores with fp32 accumulation: the rotated
+ * Q (times scale * log2 e) and K are rounded once to fp16 for Q'K'^T, the
+ * probabilities to bf16 for P.V.  fp16 bounds their range: an output row
+ * is NaN when its query has such an element of magnitude >= 2^14, or when
+ * any key its workgroup visits has a rotated K element >= 2^14 (a group's
+ * later rows all see that key).  f32 inputs run in fp32 throughout.
  */
 int gqa_prefill(const void* q, const void* k, const void* v, void* o,
                 int in_dtype, int out_dtype,
@@ -144,6 +148,7 @@ size_t gqa_prefill_chunk_workspace_size(int in_dtype, int64_t B, int64_t kend,
  * be NULL when the cache already holds the chunk's rows (as written by
  * gqa_qkv_epilogue); step 1 is then skipped.  q_rotated != 0: q holds
  * queries rotated already (gqa_qkv_epilogue's q_out), used as given.
+ * bf16 chunks have the operand range of gqa_prefill (NaN rows beyond it).
  */
 int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o,
                       int in_dtype, int out_dtype,

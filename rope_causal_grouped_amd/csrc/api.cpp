@@ -145,12 +145,11 @@ PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
 }
 
 struct DecodeWs {
-  size_t m_off, l_off, o_off, qr_off, tk_off, total;
+  size_t m_off, l_off, o_off, qr_off, total;
 };
 
-// partial states per (b, u, chunk, head); rotated queries [B, h_q, d] (fp32
-// size, so one layout serves both input types); one ticket per (b, u, head
-// block of 16)
+// partial states per (b, u, chunk, head); rotated queries [B, h_q, d] of an
+// appending step (fp32 size, so one layout serves both input types)
 DecodeWs decode_ws(int64_t B, int h_q, int h_kv, int d, int64_t cap) {
   const int g = h_q / h_kv;
   const size_t n = (size_t)B * h_kv * gqa::decode_num_splits(cap) * g;
@@ -159,15 +158,14 @@ DecodeWs decode_ws(int64_t B, int h_q, int h_kv, int d, int64_t cap) {
   w.l_off = align256(n * 4);
   w.o_off = w.l_off + align256(n * 4);
   w.qr_off = w.o_off + align256(n * (size_t)d * 4);
-  w.tk_off = w.qr_off + align256((size_t)B * h_q * d * 4);
-  w.total = w.tk_off + align256((size_t)B * h_kv * ((g + 15) / 16) * 4);
+  w.total = w.qr_off + align256((size_t)B * h_q * d * 4);
   return w;
 }
 
 gqa::DecodeWsPtrs decode_ws_ptrs(void* workspace, const DecodeWs& ws) {
   char* b = (char*)workspace;
   return {(float*)(b + ws.m_off), (float*)(b + ws.l_off), (float*)(b + ws.o_off),
-          (void*)(b + ws.qr_off), (int*)(b + ws.tk_off)};
+          (void*)(b + ws.qr_off)};
 }
 
 }  // namespace

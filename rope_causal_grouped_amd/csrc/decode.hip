@@ -5,19 +5,17 @@
 // aicoding.csdn.net, §4.1.3: the cache holds only the h_kv groups' K and V,
 // appended every step).  The query is rotated here at q_pos.
 //
-// Two launches per call.  A small preparation kernel rotates each query row
-// once (rounded once to the storage type), sets the per-group arrival
-// tickets of the call to zero and, for the appending variants, writes the
-// new token's rotated K and its V into the cache.  Then the cache of one
-// (batch, group) is cut into chunks of kDecodeChunk keys; a workgroup
-// streams one chunk exactly once for all g query heads of the group (that
-// single pass over the h_kv-group cache is what GQA saves in bandwidth, same
-// page §4.1.1) and leaves an unnormalised partial state (row max m, sum l,
-// weighted sum o).  The workgroup that finishes last among the chunks of a
-// group (an atomic ticket per group) merges them:
+// The cache of one (batch, group) is cut into chunks of kDecodeChunk keys;
+// a workgroup streams one chunk exactly once for all g query heads of the
+// group (that single pass over the h_kv-group cache is what GQA saves in
+// bandwidth, same page §4.1.1) and leaves an unnormalised partial state
+// (row max m, sum l, weighted sum o).  A second kernel merges the chunks:
 //   M = max_s m_s,  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
 // which equals the unsplit softmax exactly (up to rounding).  Maxima are
-// kept in the log2 domain (scores pre-multiplied by scale * log2 e).
+// kept in the log2 domain (scores pre-multiplied by scale * log2 e).  (A
+// merge by the last-arriving chunk of each group, through an atomic ticket,
+// needs a device-scope release in every workgroup; on gfx950 that writes
+// back the XCD's L2 each time and made the call four times slower.)
 //
 // Ragged batches: with qpos_arr set, sequence b has its own query position
 // qpos_arr[b] and length kvl_arr[b] (or qpos_arr[b] + 1 when the step has
@@ -27,9 +25,10 @@
 // sequence whose length or position is out of range has no keys at all and
 // its output becomes NaN.  With q_rotated set the query arrives rotated
 // already (gqa_qkv_epilogue writes it so) and is used as given.  With an
-// appended token (k_new set) sequence b's new row goes to position
-// qpos_arr[b] if that lies in [0, append_end); the sequence then attends
-// to rows 0 .. qpos_arr[b].
+// appended token (k_new set) a preparation kernel first writes sequence b's
+// new row to position qpos_arr[b], if that lies in [0, append_end), and
+// rotates the query once into the workspace; the sequence then attends to
+// rows 0 .. qpos_arr[b].
 //
 // Paged cache: with a block table, position j of sequence b lives in page
 // bt[b][j >> ps_log2], row j & (page_size - 1), of the pools
@@ -119,47 +118,6 @@ __device__ void write_flat_state(float* pm, float* pl, float* po, int64_t out0, 
   }
 }
 
-// True in every thread of the workgroup that is the last of the n workgroups
-// sharing `ticket` to get here.  Each thread's earlier writes are released
-// device-wide before the ticket is taken; the last workgroup acquires, so it
-// sees every other workgroup's partial state.  The ticket is an ordinary
-// (vector-memory) atomic add.
-__device__ bool last_arrival(int* ticket, int n) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(ticket, 1) == n - 1;
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-// Merge of the n_split partial states of nh heads (partial index of head c
-// of split s: base + s * g + c) into o rows orow0 + c: one thread per
-// (head, dim), every thread walking the chunks of its head.
-template <int D, bool OUT_BF16>
-__device__ void merge_heads(const float* __restrict__ pm, const float* __restrict__ pl,
-                            const float* __restrict__ po, void* __restrict__ o, int64_t base,
-                            int g, int n_split, int nh, int64_t orow0) {
-  for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
-    const int c = idx / D, dim = idx % D;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pm[base + (int64_t)s * g + c]);
-    float acc = 0.f, lsum = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const int64_t e = base + (int64_t)s * g + c;
-      const float w = __builtin_amdgcn_exp2f(pm[e] - M);
-      lsum = fmaf(w, pl[e], lsum);
-      acc = fmaf(w, po[e * D + dim], acc);
-    }
-    const float y = acc / lsum;
-    const int64_t oo = (orow0 + c) * D + dim;
-    if constexpr (OUT_BF16) ((uint16_t*)o)[oo] = f32_to_bf16_bits(y);
-    else ((float*)o)[oo] = y;
-  }
-}
-
 }  // namespace
 
 int decode_num_splits(int64_t kv_len) {
@@ -167,22 +125,21 @@ int decode_num_splits(int64_t kv_len) {
 }
 
 // ---------------------------------------------------------------------------
-// Preparation, one workgroup per sequence b: (1) the sequence's tickets set
-// to zero; (2) its query rows rotated at the query position (or used as
-// given when q_rotated) and rounded once to T, into qr [B, h_q, d]; (3) with
-// k_new set, the new token's K rotated at p = qpos_arr[b] and its V written
-// to cache position p (contiguous, or through the block table), if
-// 0 <= p < append_end and its page id is in range.
+// Preparation of an appending step, one workgroup per sequence b: (1) its
+// query rows rotated at p = qpos_arr[b] (or used as given when q_rotated)
+// and rounded once to T, into qr [B, h_q, d]; (2) the new token's K
+// rotated at p and its V written to cache position p (contiguous, or
+// through the block table), if 0 <= p < append_end and its page id is in
+// range.
 template <typename T>
 __global__ __launch_bounds__(256) void decode_prep_kernel(
-    const T* __restrict__ q, T* __restrict__ qr, int* __restrict__ tickets, int n_tk,
-    const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ kc,
-    T* __restrict__ vc, int h_q, int h_kv, int d, int64_t append_end, double q_pos_s,
-    const int64_t* __restrict__ qpos_arr, int q_rotated, RopeParams rp, KvRows kr) {
+    const T* __restrict__ q, T* __restrict__ qr, const T* __restrict__ k_new,
+    const T* __restrict__ v_new, T* __restrict__ kc, T* __restrict__ vc, int h_q, int h_kv,
+    int d, int64_t append_end, const int64_t* __restrict__ qpos_arr, int q_rotated,
+    RopeParams rp, KvRows kr) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const int half = d >> 1;
-  for (int i = tid; i < n_tk; i += blockDim.x) tickets[(int64_t)b * n_tk + i] = 0;
-  const int64_t qp = qpos_arr ? qpos_arr[b] : (int64_t)q_pos_s;
+  const int64_t qp = qpos_arr[b];
   auto ld = [](const T* p) -> float {
     if constexpr (sizeof(T) == 2) return bf16_bits_to_f32(*(const uint16_t*)p);
     else return *p;
@@ -197,11 +154,11 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(
     T* dst = qr + ((int64_t)b * h_q + t) * d;
     const float x1 = ld(src + j), x2 = ld(src + j + half);
     float c = 1.f, sn = 0.f;
-    if (!q_rotated) rope_cs(qpos_arr ? (double)qp : q_pos_s, j, d, rp, c, sn);
+    if (!q_rotated) rope_cs((double)qp, j, d, rp, c, sn);
     st(dst + j, fmaf(x1, c, -x2 * sn));
     st(dst + j + half, fmaf(x2, c, x1 * sn));
   }
-  if (!k_new || !(qp >= 0 && qp < append_end)) return;
+  if (!(qp >= 0 && qp < append_end)) return;
   int64_t row0 = ((int64_t)b * kr.cap + qp) * h_kv * d;   // contiguous: [B, cap, h_kv, d]
   int64_t head_stride = d;
   if (kr.bt) {
@@ -237,14 +194,13 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(
 // key-contiguous operand.  Heads beyond 16 per group run as extra head
 // blocks (another pass over the chunk).  The cache is read once, so its
 // loads are non-temporal (they do not displace reused lines in the caches).
-// The last workgroup of the group's chunks merges them into o.
-template <int D, bool PAGED, bool OUT_BF16>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
-    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ po, int* __restrict__ tickets, void* __restrict__ o, int h_q, int h_kv,
-    int g, int n_hb, int kv_len_max, float sl2, int n_split, const int64_t* __restrict__ kvl_arr,
-    const int64_t* __restrict__ qpos_arr, int kvl_from_pos, KvRows kr) {
+    float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int kv_len_max, double q_pos_s,
+    RopeParams rp, float sl2, int n_split, const int64_t* __restrict__ kvl_arr,
+    const int64_t* __restrict__ qpos_arr, int kvl_from_pos, int q_rotated, KvRows kr) {
   constexpr int CH = kDecodeChunk;
   constexpr int WK = CH / 4;            // keys per wave
   constexpr int NS = D / 32;            // 32-dim k-steps of S^T
@@ -263,7 +219,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
   const int col = lane & 15, h4 = lane >> 4;
   const int c = hb * 16 + col;
   const int nh = min(16, g - hb * 16);
-  const int kv_len = seq_len(b, kv_len_max, 0.0, kvl_arr, qpos_arr, kvl_from_pos).kv_len;
+  const SeqLen sq = seq_len(b, kv_len_max, q_pos_s, kvl_arr, qpos_arr, kvl_from_pos);
+  const int kv_len = sq.kv_len;
   const int chunk0 = split * CH;
   const int64_t out0 = (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16;
 
@@ -272,18 +229,32 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
   } else if (PAGED && !stage_pages(kr, b, chunk0, min(chunk0 + CH, kv_len), pg)) {
     write_flat_state(pm, pl, po, out0, nh, D, __builtin_nanf(""));
   } else {
-    // ---- rotated query (preparation kernel), B operand: lane holds head
-    // `col`, dims s*32 + h4*8 + e
+    // ---- rotated query, B operand: lane holds head `col`, dims
+    // s*32 + h4*8 + e (rotated here at the query position unless q_rotated)
     bf16x8 qb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[s][e] = (__bf16)0.f;
     if (c < g) {
-      const uint16_t* qrow = qr + ((int64_t)b * h_q + (int64_t)u * g + c) * D;
+      const uint16_t* qrow = q + ((int64_t)b * h_q + (int64_t)u * g + c) * D;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) qb[s] = *(const bf16x8*)(qrow + s * 32 + h4 * 8);
-    } else {
+      for (int s = 0; s < NS / 2; ++s) {
+        const u32x4 r1 = *(const u32x4*)(qrow + s * 32 + h4 * 8);
+        const u32x4 r2 = *(const u32x4*)(qrow + s * 32 + h4 * 8 + D / 2);
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qb[s][e] = (__bf16)0.f;
+        for (int e = 0; e < 8; ++e) {
+          const int j = s * 32 + h4 * 8 + e;
+          float cs_c = 1.f, cs_s = 0.f;   // q_rotated: the query is used as given
+          if (!q_rotated) rope_cs(sq.q_pos, j, D, rp, cs_c, cs_s);
+          const float x1 = (e & 1) ? __uint_as_float(r1[e >> 1] & 0xffff0000u)
+                                   : __uint_as_float(r1[e >> 1] << 16);
+          const float x2 = (e & 1) ? __uint_as_float(r2[e >> 1] & 0xffff0000u)
+                                   : __uint_as_float(r2[e >> 1] << 16);
+          qb[s][e] = (__bf16)fmaf(x1, cs_c, -x2 * cs_s);
+          qb[s + NS / 2][e] = (__bf16)fmaf(x2, cs_c, x1 * cs_s);
+        }
+      }
     }
 
     const int kw0 = chunk0 + wave * WK;
@@ -405,23 +376,19 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
     }
   }
 
-  // ---- the last chunk of (b, u, head block) to finish merges all of them
-  if (last_arrival(tickets + ((int64_t)b * h_kv + u) * n_hb + hb, n_split))
-    merge_heads<D, OUT_BF16>(pm, pl, po, o, out0 - (int64_t)split * g, g, n_split, nh,
-                             (int64_t)b * h_q + (int64_t)u * g + hb * 16);
 }
 
 // fp32 cache, vector ALU (the fp32 parity path).  Workgroup = (chunk, u x
 // head block, b); 16 threads per head.  Scores of the chunk go to LDS, then
 // each thread reduces one head's max and sum and accumulates 1/16 of its
-// output dims.  The last workgroup of the group's chunks merges them.
-template <int D, bool PAGED, bool OUT_BF16>
+// output dims.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_f32_kernel(
-    const float* __restrict__ qr, const float* __restrict__ kc, const float* __restrict__ vc,
-    float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po,
-    int* __restrict__ tickets, void* __restrict__ o, int h_q, int h_kv, int g, int n_hb,
-    int kv_len_max, float scale, int n_split, const int64_t* __restrict__ kvl_arr,
-    const int64_t* __restrict__ qpos_arr, int kvl_from_pos, KvRows kr) {
+    const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
+    float* __restrict__ pm, float* __restrict__ pl, float* __restrict__ po, int h_q, int h_kv,
+    int g, int n_hb, int kv_len_max, double q_pos_s, RopeParams rp, float scale, int n_split,
+    const int64_t* __restrict__ kvl_arr, const int64_t* __restrict__ qpos_arr, int kvl_from_pos,
+    int q_rotated, KvRows kr) {
   constexpr int CH = kDecodeChunk;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float qs[16][D];
@@ -432,7 +399,8 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int nh = min(16, g - hb * 16);
-  const int kv_len = seq_len(b, kv_len_max, 0.0, kvl_arr, qpos_arr, kvl_from_pos).kv_len;
+  const SeqLen sq = seq_len(b, kv_len_max, q_pos_s, kvl_arr, qpos_arr, kvl_from_pos);
+  const int kv_len = sq.kv_len;
   const int64_t out0 = (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16;
 
   if (split * CH >= kv_len) {   // chunk past this sequence's keys: empty state
@@ -440,10 +408,18 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
   } else if (PAGED && !stage_pages(kr, b, split * CH, min(split * CH + CH, kv_len), pg)) {
     write_flat_state(pm, pl, po, out0, nh, D, __builtin_nanf(""));
   } else {
-    for (int idx = tid; idx < 16 * D; idx += 256) {
-      const int cc = idx / D, dd = idx % D;
-      qs[cc][dd] = cc < nh ? qr[((int64_t)b * h_q + (int64_t)u * g + hb * 16 + cc) * D + dd]
-                           : 0.f;
+    for (int idx = tid; idx < 16 * (D / 2); idx += 256) {
+      const int cc = idx / (D / 2), j = idx % (D / 2);
+      float y1 = 0.f, y2 = 0.f;
+      if (cc < nh) {
+        const float* qrow = q + ((int64_t)b * h_q + (int64_t)u * g + hb * 16 + cc) * D;
+        float c = 1.f, s = 0.f;   // q_rotated: the query is used as given
+        if (!q_rotated) rope_cs(sq.q_pos, j, D, rp, c, s);
+        y1 = fmaf(qrow[j], c, -qrow[j + D / 2] * s);
+        y2 = fmaf(qrow[j + D / 2], c, qrow[j] * s);
+      }
+      qs[cc][j] = y1;
+      qs[cc][j + D / 2] = y2;
     }
     __syncthreads();
 
@@ -494,9 +470,52 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(
     }
   }
 
-  if (last_arrival(tickets + ((int64_t)b * h_kv + u) * n_hb + hb, n_split))
-    merge_heads<D, OUT_BF16>(pm, pl, po, o, out0 - (int64_t)split * g, g, n_split, nh,
-                             (int64_t)b * h_q + (int64_t)u * g + hb * 16);
+}
+
+// Merge of the chunk partials of one (b, query head), one thread per dim.
+// Chunk states are folded in batches of 32, every load of a batch issued
+// before any of them is used (one memory latency per batch), with an online
+// rescale between batches.  Empty chunks (m = -inf) weigh nothing; a NaN
+// state, or no non-empty chunk at all, gives NaN.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ pm,
+                                                         const float* __restrict__ pl,
+                                                         const float* __restrict__ po,
+                                                         void* __restrict__ o, int h_q, int h_kv,
+                                                         int g, int n_split) {
+  constexpr int NB = 32;
+  const int t = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
+  const int u = t / g, c = t % g;
+  const int64_t base = (((int64_t)b * h_kv + u) * n_split) * g + c;
+  float M = -INFINITY, lsum = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < n_split; s0 += NB) {
+    float mv[NB], lv[NB], ov[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const bool in = s0 + j < n_split;
+      const int64_t e = base + (int64_t)(in ? s0 + j : 0) * g;
+      mv[j] = in ? pm[e] : -INFINITY;
+      lv[j] = in ? pl[e] : 0.f;
+      ov[j] = in ? po[e * D + dim] : 0.f;
+    }
+    float mn = M;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) mn = fmaxf(mn, mv[j]);
+    const float a = mn == M ? 1.f : __builtin_amdgcn_exp2f(M - mn);
+    acc *= a;
+    lsum *= a;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float w = mv[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[j] - mn);
+      acc = fmaf(w, ov[j], acc);
+      lsum = fmaf(w, lv[j], lsum);
+    }
+    M = mn;
+  }
+  const float y = acc / lsum;
+  const int64_t oo = ((int64_t)b * h_q + t) * D + dim;
+  if constexpr (OUT_BF16) ((uint16_t*)o)[oo] = f32_to_bf16_bits(y);
+  else ((float*)o)[oo] = y;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t st,
@@ -505,38 +524,38 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t
   const int n_hb = (g + 15) / 16;
   const int n_split = decode_num_splits(a.kv_len);
   const KvRows kr{a.bt, a.ps_log2, a.max_pages, a.num_pages, a.cap};
-  const int n_tk = a.h_kv * n_hb;
-  // 1) tickets, rotated queries, appended token
-  if (a.in_bf16)
-    decode_prep_kernel<uint16_t><<<(unsigned)a.B, 256, 0, st>>>(
-        (const uint16_t*)a.q, (uint16_t*)w.qr, w.tickets, n_tk, (const uint16_t*)a.k_new,
-        (const uint16_t*)a.v_new, (uint16_t*)a.kc, (uint16_t*)a.vc, a.h_q, a.h_kv, a.d,
-        a.append_end, (double)a.q_pos, a.qpos_arr, a.q_rotated, a.rp, kr);
-  else
-    decode_prep_kernel<float><<<(unsigned)a.B, 256, 0, st>>>(
-        (const float*)a.q, (float*)w.qr, w.tickets, n_tk, (const float*)a.k_new,
-        (const float*)a.v_new, (float*)a.kc, (float*)a.vc, a.h_q, a.h_kv, a.d, a.append_end,
-        (double)a.q_pos, a.qpos_arr, a.q_rotated, a.rp, kr);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  // 2) split-K streaming with the merge folded in
+  const void* q = a.q;
+  int q_rotated = a.q_rotated;
+  hipError_t err;
+  if (a.k_new) {   // 0) append the new token; the query, rotated once, into the workspace
+    if (a.in_bf16)
+      decode_prep_kernel<uint16_t><<<(unsigned)a.B, 256, 0, st>>>(
+          (const uint16_t*)a.q, (uint16_t*)w.qr, (const uint16_t*)a.k_new,
+          (const uint16_t*)a.v_new, (uint16_t*)a.kc, (uint16_t*)a.vc, a.h_q, a.h_kv, a.d,
+          a.append_end, a.qpos_arr, a.q_rotated, a.rp, kr);
+    else
+      decode_prep_kernel<float><<<(unsigned)a.B, 256, 0, st>>>(
+          (const float*)a.q, (float*)w.qr, (const float*)a.k_new, (const float*)a.v_new,
+          (float*)a.kc, (float*)a.vc, a.h_q, a.h_kv, a.d, a.append_end, a.qpos_arr,
+          a.q_rotated, a.rp, kr);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    q = w.qr;
+    q_rotated = 1;
+  }
+  // 1) split-K streaming
   dim3 grid((unsigned)n_split, (unsigned)(a.h_kv * n_hb), (unsigned)a.B);
   const float sl2 = a.scale * 1.4426950408889634f;
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
-#define GQA_SPLIT(KERNEL, T, DD, PG, OB, SC)                                                   \
-  KERNEL<DD, PG, OB><<<grid, 256, 0, st>>>((const T*)w.qr, (const T*)a.kc, (const T*)a.vc,     \
-                                           w.m, w.l, w.o, w.tickets, a.o, a.h_q, a.h_kv, g,    \
-                                           n_hb, (int)a.kv_len, SC, n_split, a.kvl_arr,       \
-                                           a.qpos_arr, a.kvl_from_pos, kr)
-#define GQA_SPLIT_OB(KERNEL, T, DD, PG, SC)                   \
-  do {                                                        \
-    if (a.out_bf16) GQA_SPLIT(KERNEL, T, DD, PG, true, SC);   \
-    else GQA_SPLIT(KERNEL, T, DD, PG, false, SC);             \
-  } while (0)
-#define GQA_SPLIT_PG(KERNEL, T, DD, SC)                              \
-  do {                                                               \
-    if (a.bt) GQA_SPLIT_OB(KERNEL, T, DD, true, SC);                 \
-    else GQA_SPLIT_OB(KERNEL, T, DD, false, SC);                     \
+#define GQA_SPLIT(KERNEL, T, DD, PG, SC)                                                      \
+  KERNEL<DD, PG><<<grid, 256, 0, st>>>((const T*)q, (const T*)a.kc, (const T*)a.vc, w.m, w.l, \
+                                       w.o, a.h_q, a.h_kv, g, n_hb, (int)a.kv_len,           \
+                                       (double)a.q_pos, a.rp, SC, n_split, a.kvl_arr,         \
+                                       a.qpos_arr, a.kvl_from_pos, q_rotated, kr)
+#define GQA_SPLIT_PG(KERNEL, T, DD, SC)                   \
+  do {                                                    \
+    if (a.bt) GQA_SPLIT(KERNEL, T, DD, true, SC);         \
+    else GQA_SPLIT(KERNEL, T, DD, false, SC);             \
   } while (0)
   if (a.in_bf16) {
     if (a.d == 128) GQA_SPLIT_PG(decode_split_bf16_kernel, uint16_t, 128, sl2);
@@ -546,11 +565,21 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t
     else GQA_SPLIT_PG(decode_split_f32_kernel, float, 64, a.scale);
   }
 #undef GQA_SPLIT_PG
-#undef GQA_SPLIT_OB
 #undef GQA_SPLIT
   err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, st);
-  return err;
+  if (err != hipSuccess) return err;
+  // 2) merge of the chunks
+  dim3 mgrid((unsigned)a.h_q, (unsigned)a.B);
+#define GQA_MERGE(DD, OB) \
+  decode_merge_kernel<DD, OB><<<mgrid, DD, 0, st>>>(w.m, w.l, w.o, a.o, a.h_q, a.h_kv, g, n_split)
+  if (a.d == 128) {
+    if (a.out_bf16) GQA_MERGE(128, true); else GQA_MERGE(128, false);
+  } else {
+    if (a.out_bf16) GQA_MERGE(64, true); else GQA_MERGE(64, false);
+  }
+#undef GQA_MERGE
+  return hipGetLastError();
 }
 
 }  // namespace gqa

@@ -98,14 +98,13 @@ struct DecodeArgs {
 };
 
 // Workspace pieces of a decode call: partial states per (b, u, chunk, head)
-// (max m, sum l, unnormalised o[d]), the rotated queries [B, h_q, d] in the
-// input type, and one arrival ticket per (b, u, head block of 16).
+// (max m, sum l, unnormalised o[d]) and, for an appending step, the rotated
+// queries [B, h_q, d] in the input type.
 struct DecodeWsPtrs {
   float* m;
   float* l;
   float* o;
   void* qr;
-  int* tickets;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t st,

@@ -23,10 +23,11 @@
 // significand keeps the logits of large rows (the 32K workload's rows scaled
 // by 8) within the bf16 tolerance, where bf16-rounded Q' and K' do not, at
 // the same matrix-core rate.  Q' carries scale * log2(e), so scores come out
-// in log2 units.  An operand row or tile whose largest element reaches 2^14
-// is stored divided by a power of two (fp16 ends at 65504) and its scores
-// are multiplied back before the softmax; ordinary inputs never take that
-// path.  The probabilities, rounded to bf16, are already in the B-operand
+// in log2 units.  fp16 ends at 65504: a row whose Q' * scale * log2(e) has
+// an element of magnitude 2^14 or more, and every row of a workgroup whose
+// keys hold such a rotated K element (the preparation pass flags the tile),
+// gets NaN operands and so NaN output; nothing is checked inside the loop.  The
+// probabilities, rounded to bf16, are already in the B-operand
 // layout of O^T += V^T P^T on v_mfma_f32_32x32x16_bf16; V arrives
 // pre-transposed (keys contiguous, in the accumulator's lane order) from the
 // preparation pass, in 32-key sub-tiles.
@@ -275,43 +276,38 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // arrived.
   f16x8 qb[NS];
   float qcap;      // bound on |q'| in score units, with a margin for rounding
-  float qfac;      // 2^eq: multiplies this row's scores back (slow path only)
-  bool qslow;      // some row of the wave has eq != 0 (wave-uniform)
-  auto q_elem = [&](int s, int e) -> float {   // element (s, e) of Q' * scale * log2(e)
-    const uint32_t w1 = raw[s][e >> 1];
-    const float x = (e & 1) ? __uint_as_float(w1 & 0xffff0000u) : __uint_as_float(w1 << 16);
-    if constexpr (PRE) {
-      const int sp = s < NS / 2 ? s + NS / 2 : s - NS / 2;   // the pair's other half
-      const uint32_t w2 = raw[sp][e >> 1];
-      const float x2 = (e & 1) ? __uint_as_float(w2 & 0xffff0000u) : __uint_as_float(w2 << 16);
-      const int s4 = s < NS / 2 ? s : s - NS / 2;
-      const float cr = c4[s4][e >> 1][(e & 1) * 2], sr = c4[s4][e >> 1][(e & 1) * 2 + 1];
-      return (s < NS / 2 ? fmaf(x, cr, -x2 * sr) : fmaf(x, cr, x2 * sr)) * sl2;
-    } else {
-      return x * sl2;
-    }
-  };
+  bool qbad;       // this row's Q' is outside the fp16 operand range
   auto rotate_q = [&] {
-    float amax = 0.f;
+    float amax = 0.f, ss = 0.f;
+    auto put = [&](int s, int e, float y) {
+      const _Float16 h = (_Float16)y;
+      qb[s][e] = h;
+      amax = fmaxf(amax, fabsf(y));
+      ss = fmaf((float)h, (float)h, ss);
+    };
+    auto bf = [](uint32_t w, int e) {
+      return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    };
+    if constexpr (PRE) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS / 2; ++s) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q_elem(s, e)));
-    const int eq = kexp_of(max_xor32(amax));
-    const float down = __builtin_ldexpf(1.0f, -eq);
-    float ss = 0.f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const _Float16 h = (_Float16)(q_elem(s, e) * down);
-        qb[s][e] = h;
-        ss = fmaf((float)h, (float)h, ss);
+        for (int e = 0; e < 8; ++e) {
+          const float cr = c4[s][e >> 1][(e & 1) * 2], sr = c4[s][e >> 1][(e & 1) * 2 + 1];
+          const float x1 = bf(raw[s][e >> 1], e), x2 = bf(raw[s + NS / 2][e >> 1], e);
+          put(s, e, fmaf(x1, cr, -x2 * sr) * sl2);
+          put(s + NS / 2, e, fmaf(x2, cr, x1 * sr) * sl2);
+        }
       }
-    qfac = __builtin_ldexpf(1.0f, eq);
-    qslow = __builtin_amdgcn_ballot_w64(eq != 0) != 0;
+    } else {   // rotated already
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) put(s, e, bf(raw[s][e >> 1], e) * sl2);
+    }
+    qbad = kexp_of(max_xor32(amax)) != 0;
     // |q'| of the row from the fp16 values the matrix cores see
-    qcap = sqrtf(sum_xor32(ss)) * qfac * 1.01f;
+    qcap = sqrtf(sum_xor32(ss)) * 1.01f;
   };
 
   // ---- operand read offsets (elements), swizzled like the stores
@@ -437,7 +433,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     return acc0 + acc1;
   };
   float crow = 0.f;   // bound on this row's scores, score units (set after the prologue)
-  bool kslow = false;   // some key tile of the workgroup has kexp != 0 (uniform)
   float m_raise = 0.f;  // raise of m owed by the previous tile's large sum (applied lazily)
   auto vector_phase = [&](int i) {
     if (!active(i)) {   // keys beyond this wave's rows: contribute nothing
@@ -453,15 +448,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     // compiler then keeps every MFMA accumulator in VGPRs, and the vector
     // ALU reads the scores without copies)
     f32x16 s0 = sacc[0], s1 = sacc[1];
-    if (qslow || kslow) {   // operands stored divided by powers of two: scores back to scale
-      float f = qfac;
-      if (kslow) f = __builtin_ldexpf(f, kexp_bu[i]);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s0[e] *= f;
-        s1[e] *= f;
-      }
-    }
     if (masked(i)) {
       // key of score e: i*TK + (e>>2)*8 + hl*4 + (e&3) (+32 for s1); compared
       // as a constant offset against the row's limit within the tile
@@ -520,7 +506,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       any |= wexp[w];
     }
     crow = qcap * km;
-    kslow = __builtin_amdgcn_readfirstlane(any) != 0;
+    if (qbad || any != 0) {   // outside the fp16 operand range: NaN scores, NaN row
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[s][e] = (_Float16)__builtin_nanf("");
+    }
   }
   // a bound within the headroom makes 0 a valid reference from the start
   // (every score lies in [-crow, crow]), which the scores need no shift for

@@ -120,10 +120,10 @@ def test_workspace_sizes(lib):
     n = lib.gqa_prefill_workspace_size(1, 4, 4096, 4, 128)
     assert n == 4096 * 64 * 8 + 2 * 4 * 4 * 4096 * 128 * 2 + 2 * 4 * 4 * 64 * 4
     assert lib.gqa_prefill_workspace_size(1, 0, 10, 4, 128) == 0
-    # decode: (m, l, o[d]) per (b, group, 1024-key chunk, head), the rotated
-    # queries (fp32-sized) and one arrival ticket per (b, group, 16 heads)
+    # decode: (m, l, o[d]) per (b, group, 1024-key chunk, head) and the
+    # rotated queries of an appending step (fp32-sized)
     n = lib.gqa_decode_workspace_size(32, 28, 4, 128, 32768)
-    assert n == 32 * 4 * 32 * 7 * (2 + 128) * 4 + 32 * 28 * 128 * 4 + 32 * 4 * 4
+    assert n == 32 * 4 * 32 * 7 * (2 + 128) * 4 + 32 * 28 * 128 * 4
     assert lib.gqa_decode_workspace_size(1, 28, 3, 128, 10) == 0
 
 

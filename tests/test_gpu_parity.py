@@ -134,6 +134,30 @@ def test_prefill_bf16_large_scores(shape, sigma, boosted):
                   f"prefill bf16 {shape} sigma={sigma} boosted={boosted}")
 
 
+def test_prefill_bf16_fp16_range_gives_nan_rows():
+    """Score operands are fp16: a rotated K element, or a Q element times
+    scale*log2(e), of magnitude 2^14 or more is outside their range.  The
+    rows that would use it come out NaN (every row of the query's group that
+    sees the key; the one query row), and all other rows are unaffected."""
+    B, L, h_q, h_kv, d = 1, 200, 28, 4, 128
+    q, k, v = small_case(B, L, h_q, h_kv, d, torch.bfloat16, 77)
+    k[0, 150, 1, :] = 40000.0          # group 1, position 150
+    q[0, 10, 5, :] = 200000.0          # 200000 * log2(e) / sqrt(128) > 2^14
+    o = host(gqa.prefill(dev(q, torch.bfloat16), dev(k, torch.bfloat16),
+                         dev(v, torch.bfloat16)))
+    torch.cuda.synchronize()
+    g = h_q // h_kv
+    assert np.all(np.isnan(o[0, 150:, g:2 * g])), "rows that see the large key"
+    assert np.all(np.isnan(o[0, 10, 5])), "the large query row"
+    want = oracle.prefill(q, k, v)
+    keep = np.ones((L, h_q), bool)
+    keep[:, g:2 * g] = False            # group 1 (rows before 150 may share a workgroup)
+    keep[10, 5] = False
+    got = o[0][keep]
+    assert np.all(np.isfinite(got))
+    assert_parity(got, want[0][keep], torch.bfloat16, "rows outside the large entries")
+
+
 def test_prefill_bf16_noncausal_and_bf16_out():
     B, L, h_q, h_kv, d = 2, 200, 14, 2, 128
     q, k, v = small_case(B, L, h_q, h_kv, d, torch.bfloat16, 7)
