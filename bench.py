@@ -162,20 +162,28 @@ def clock_warmup(torch, step, seconds):
 
 
 def no_children_left():
-    """Wait for (or end) any child process this run started; returns what
-    was found, for the log."""
+    """Child processes still running at exit, for the log.  The oracle pool's
+    workers are joined when it closes; the "spawn" start method's resource
+    tracker (it ignores SIGTERM) ends by itself when this process exits, as
+    it reads a pipe from it.  Anything else is ended here."""
     try:
         import psutil
     except ImportError:
         return "psutil unavailable"
-    kids = psutil.Process().children(recursive=True)
-    for p in kids:
+    tracker, other = 0, []
+    for p in psutil.Process().children(recursive=True):
         try:
+            cmd = " ".join(p.cmdline())
+            if "resource_tracker" in cmd:
+                tracker += 1
+                continue
+            other.append(cmd[:100])
+            p.kill()
             p.wait(timeout=5)
-        except psutil.TimeoutExpired:
-            p.terminate()
-            p.wait(timeout=5)
-    return f"{len(kids)} child process(es) at exit" if kids else "no child processes at exit"
+        except psutil.Error:
+            pass
+    return (f"child processes at exit: {tracker} resource tracker (ends with this process), "
+            f"{len(other)} other{' (killed: ' + str(other) + ')' if other else ''}")
 
 
 def measure_context(torch, gqa, dev):
