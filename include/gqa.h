@@ -117,6 +117,30 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that must not
+ * call hipMalloc, harnesses that forbid it).  Arguments, layouts, results and
+ * errors are those of gqa_decode; the chunk states live in a static array of
+ * GQA_DECODE_NOALLOC_SCRATCH_BYTES that the library's code object reserves on
+ * every GPU it runs on (held until the process ends).  A step needs
+ *   B * h_q * ceil(kv_len / 1024) * (d + 2) * 4 bytes (each of its three
+ *   parts rounded up to 256) + B * h_q * d * 4 (rounded up to 256);
+ * a step beyond the limit returns GQA_ERR_UNSUPPORTED before anything is
+ * enqueued (for d = 128 about 63,000 pairs of a query head and a 1024-key
+ * chunk: B = 32, h_q = 28 fit up to kv_len = 65536).  The call allocates
+ * nothing.  All calls on one GPU share its scratch: two calls whose work
+ * overlaps on the device (on different streams, or from several threads on
+ * one device without ordering) race and give wrong results; calls ordered
+ * on one stream are safe.  Outputs equal gqa_decode's bit for bit.
+ */
+#define GQA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                       void* o, int in_dtype, int out_dtype,
+                       int64_t B, int h_q, int h_kv, int d, int64_t cap,
+                       int64_t kv_len, int64_t q_pos, double theta, float scale,
+                       void* stream);
+
+/*
  * Autoregressive use around the path (walkthrough §4.1.3 closing note: the
  * per-layer cache keeps only the h_kv groups' K and V, and every step
  * appends the current token's K, V before attending).  The per-sequence

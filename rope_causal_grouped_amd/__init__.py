@@ -16,7 +16,7 @@ import torch
 
 from ._lib import (GQA_BF16, GQA_F32, GQAError, check, lib)
 
-__all__ = ["rope_apply", "prefill", "decode", "prefill_chunk", "decode_ragged",
+__all__ = ["rope_apply", "prefill", "decode", "decode_noalloc", "prefill_chunk", "decode_ragged",
            "decode_append", "qkv_epilogue", "decode_paged", "decode_paged_workspace_size",
            "set_rope_yarn", "prefill_workspace_size", "prefill_chunk_workspace_size",
            "decode_workspace_size", "timing_enable", "timing_read", "stream_read", "version",
@@ -125,6 +125,28 @@ def decode(q, k_cache, v_cache, kv_len: int, q_pos: int, *, theta: float = ROPE_
     check(lib().gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _dt(q), _dt(out), B,
                            h_q, h_kv, d, cap, kv_len, q_pos, theta, scale, _ptr(workspace),
                            workspace.numel(), _stream()))
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_len: int, q_pos: int, *, out, theta: float = ROPE_THETA,
+                   scale: float | None = None):
+    """decode() on the library's static per-GPU scratch: no workspace and no
+    device allocation in the call (the caller passes `out`).  Calls that
+    overlap on one GPU share that scratch and race."""
+    _dev(q, k_cache, v_cache, out)
+    B, h_q, d = q.shape
+    cap, h_kv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, cap, h_kv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, cap, h_kv, d] matching q")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    if out.shape != (B, h_q, d):
+        raise ValueError("out must be [B, h_q, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    check(lib().gqa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _dt(q),
+                                   _dt(out), B, h_q, h_kv, d, cap, kv_len, q_pos, theta, scale,
+                                   _stream()))
     return out
 
 

@@ -29,6 +29,8 @@ SIGNATURES = {
     "gqa_decode_workspace_size": (_SZ, [_I64, _I, _I, _I, _I64]),
     "gqa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I64, _I, _I, _I, _I64, _I64, _I64, _D, _F,
                         _P, _SZ, _P]),
+    "gqa_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I64, _I, _I, _I, _I64, _I64, _I64, _D,
+                                _F, _P]),
     "gqa_prefill_chunk_workspace_size": (_SZ, [_I, _I64, _I64, _I, _I]),
     "gqa_prefill_chunk": (_I, [_P, _P, _P, _P, _I, _I, _I64, _I64, _I, _I, _I, _P, _P, _I64,
                                _D, _F, _I, _P, _P, _I64, _P, _SZ, _P]),

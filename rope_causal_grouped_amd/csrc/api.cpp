@@ -144,6 +144,9 @@ PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
   return w;
 }
 
+static_assert(GQA_DECODE_NOALLOC_SCRATCH_BYTES == gqa::kDecodeScratchBytes,
+              "the header's scratch size is the kernels' one");
+
 struct DecodeWs {
   size_t m_off, l_off, o_off, qr_off, total;
 };
@@ -280,10 +283,16 @@ size_t gqa_decode_workspace_size(int64_t B, int h_q, int h_kv, int d, int64_t ca
   return decode_ws(B, h_q, h_kv, d, cap).total;
 }
 
-int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int in_dtype,
-               int out_dtype, int64_t B, int h_q, int h_kv, int d, int64_t cap, int64_t kv_len,
-               int64_t q_pos, double theta, float scale, void* workspace, size_t workspace_bytes,
-               void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gqa_decode with a caller's workspace, or (noalloc) with the library's
+// static scratch of the current device.
+int decode_call(const void* q, const void* k_cache, const void* v_cache, void* o, int in_dtype,
+                int out_dtype, int64_t B, int h_q, int h_kv, int d, int64_t cap, int64_t kv_len,
+                int64_t q_pos, double theta, float scale, void* workspace,
+                size_t workspace_bytes, void* stream, bool noalloc) {
   g_err.clear();
   if (!q || !k_cache || !v_cache || !o)
     return fail(GQA_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be non-NULL");
@@ -307,10 +316,21 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
       !aligned16(workspace))
     return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  const DecodeWs ws = decode_ws(B, h_q, h_kv, d, cap);
-  if (!workspace || workspace_bytes < ws.total)
+  // the chunk states are laid out for the chunks of kv_len keys (the caller's
+  // workspace is sized by cap, which only leaves room to spare)
+  const DecodeWs ws = decode_ws(B, h_q, h_kv, d, noalloc ? kv_len : cap);
+  if (noalloc) {
+    if (ws.total > gqa::kDecodeScratchBytes)
+      return fail(GQA_ERR_UNSUPPORTED,
+                  "this step needs %zu bytes of scratch; the static scratch holds %zu "
+                  "(use gqa_decode with a workspace)",
+                  ws.total, gqa::kDecodeScratchBytes);
+    const hipError_t e = gqa::decode_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "static decode scratch lookup");
+  } else if (!workspace || workspace_bytes < ws.total) {
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
                 workspace ? workspace_bytes : (size_t)0);
+  }
   gqa::DecodeArgs a{};
   a.q = q;
   a.kc = k_cache;
@@ -328,11 +348,31 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
   a.rp = rope_params(theta, d);
   a.scale = scale;
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
-  if (g_timing.on) ev = g_timing.take();
+  if (g_timing.on && !noalloc) ev = g_timing.take();
   hipError_t e = gqa::launch_decode(a, decode_ws_ptrs(workspace, ws), (hipStream_t)stream,
                                     ev.first, ev.second);
   if (ev.first) g_timing.rec[1].push_back(ev);
   return e == hipSuccess ? GQA_OK : hip_fail(e, "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, int in_dtype,
+               int out_dtype, int64_t B, int h_q, int h_kv, int d, int64_t cap, int64_t kv_len,
+               int64_t q_pos, double theta, float scale, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  return decode_call(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap, kv_len,
+                     q_pos, theta, scale, workspace, workspace_bytes, stream, false);
+}
+
+int gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                       int in_dtype, int out_dtype, int64_t B, int h_q, int h_kv, int d,
+                       int64_t cap, int64_t kv_len, int64_t q_pos, double theta, float scale,
+                       void* stream) {
+  return decode_call(q, k_cache, v_cache, o, in_dtype, out_dtype, B, h_q, h_kv, d, cap, kv_len,
+                     q_pos, theta, scale, nullptr, 0, stream, true);
 }
 
 size_t gqa_prefill_chunk_workspace_size(int in_dtype, int64_t B, int64_t kend, int h_kv, int d) {

@@ -37,6 +37,8 @@
 // (nxmr.cn) §2).  A workgroup reads its chunk's page ids into LDS once; a
 // chunk whose ids fall outside the pool makes the sequence's output NaN.
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -122,6 +124,35 @@ __device__ void write_flat_state(float* pm, float* pl, float* po, int64_t out0, 
 
 int decode_num_splits(int64_t kv_len) {
   return (int)((kv_len + kDecodeChunk - 1) / kDecodeChunk);
+}
+
+// Chunk states of an allocation-free decode call, in device memory that the
+// code object reserves: each device holds its own copy, at its own address,
+// from the library's load until the process ends.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the host-side name of the array is no device address: ask the runtime
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

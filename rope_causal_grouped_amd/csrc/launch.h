@@ -14,6 +14,7 @@ constexpr int kPrefillTileV = 32;      // keys per attention tile; V^T is stored
 constexpr int kPrefillRowsWG = 256;    // stacked (position, head) rows per workgroup
 constexpr int kDecodeChunk = 1024;     // keys per decode split
 constexpr int kDecodeMaxSplits = 8192;  // bound on the chunks of one sequence (8M keys)
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;  // static scratch of gqa_decode_noalloc
 
 hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, int d, int64_t pos0,
                              RopeParams rp, hipStream_t st);
@@ -68,6 +69,9 @@ hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, c
                               hipStream_t st);
 
 int decode_num_splits(int64_t kv_len);
+// Device address of this library's static decode scratch (kDecodeScratchBytes)
+// on the current device, looked up once per device.
+hipError_t decode_scratch(void** ptr);
 
 // One decode call.  Scalar kv_len / q_pos, or per-sequence arrays (then
 // kv_len bounds every length and sets the chunk count); k_new / v_new set:

@@ -7,6 +7,7 @@
  * `gcc -std=c99 -pedantic -Wall -Wextra -Werror`, linked against libgqa.so
  * and run by tests/test_abi.py.
  */
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -41,6 +42,19 @@ int main(void) {
   expect(gqa_decode_workspace_size(32, 28, 4, 128, 32768) > 0, "gqa_decode_workspace_size");
   REJECTS(gqa_decode(NULL, NULL, NULL, NULL, GQA_BF16, GQA_F32, 1, 28, 4, 128, 16, 16, 16,
                      theta, scale, NULL, 0, NULL));
+
+  REJECTS(gqa_decode_noalloc(NULL, NULL, NULL, NULL, GQA_BF16, GQA_F32, 1, 28, 4, 128, 16, 16,
+                             16, theta, scale, NULL));
+  {
+    /* a step past the static scratch is refused before anything touches the
+     * device, so addresses that are never dereferenced serve here */
+    void* fake = (void*)(uintptr_t)4096;
+    expect(gqa_decode_noalloc(fake, fake, fake, fake, GQA_BF16, GQA_F32, 32, 28, 4, 128,
+                              1048576, 1048576, 1048576, theta, scale, NULL) ==
+               GQA_ERR_UNSUPPORTED &&
+               strstr(gqa_last_error(), "scratch") != NULL,
+           "gqa_decode_noalloc past GQA_DECODE_NOALLOC_SCRATCH_BYTES");
+  }
 
   expect(gqa_prefill_chunk_workspace_size(GQA_BF16, 1, 4096, 4, 128) > 0,
          "gqa_prefill_chunk_workspace_size");
