@@ -232,8 +232,11 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
   char* wsb = (char*)workspace;
   float2* cs = (float2*)(wsb + ws.cs_off);
   const gqa::RopeParams rp = rope_params(theta, d);
-  hipError_t e = gqa::launch_rope_table(cs, L, d, 0, rp, st);
-  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  hipError_t e = hipSuccess;
+  if (in_dtype != GQA_BF16) {   // the bf16 preparation kernel writes the table itself
+    e = gqa::launch_rope_table(cs, L, d, 0, rp, st);
+    if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  }
 
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   if (g_timing.on) ev = g_timing.take();
@@ -244,8 +247,8 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
     float* kmax = (float*)(wsb + ws.kmax_off);
     int* kexp = (int*)(wsb + ws.kexp_off);
-    e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, cs, kp, vt, kmax,
-                                    kexp, (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad,
+    e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, &rp, cs, kp, vt,
+                                    kmax, kexp, (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad,
                                     h_kv, d, cap, L, nullptr, nullptr, L, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     if (ev.first) (void)hipEventRecord(ev.first, st);
@@ -439,8 +442,8 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
     float* kmax = (float*)(wsb + ws.kmax_off);
     int* kexp = (int*)(wsb + ws.kexp_off);
     e = gqa::launch_kv_prepare_bf16((const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
-                                    kp, vt, kmax, kexp, nullptr, nullptr, B, C, Lpad, h_kv, d, cap,
-                                    cap, start, len, kend, st);
+                                    nullptr, kp, vt, kmax, kexp, nullptr, nullptr, B, C, Lpad, h_kv,
+                                    d, cap, cap, start, len, kend, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     // 3) the chunk's queries against them
     if (ev.first) (void)hipEventRecord(ev.first, st);

@@ -22,8 +22,8 @@ hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, in
 hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, RopeParams rp,
                              hipStream_t st);
 
-hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
-                                  uint16_t* kp, uint16_t* vt, float* kmax, int* kexp,
+hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const RopeParams* rope,
+                                  float2* cs_out, uint16_t* kp, uint16_t* vt, float* kmax, int* kexp,
                                   uint16_t* kc, uint16_t* vc, int64_t B, int64_t L, int64_t Lpad,
                                   int h_kv, int d, int64_t cap, int64_t src_rows,
                                   const int64_t* kstart, const int64_t* klen, int64_t kend,

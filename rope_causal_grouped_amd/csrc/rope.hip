@@ -61,25 +61,34 @@ hipError_t launch_rope_apply(void* x, int dtype, int64_t B, int64_t L, int h, in
 
 // ---------------------------------------------------------------------------
 // cs[l][j] = (cos, sin)(pos(l) * omega_j) for l < L, j < d/2, pos(l) = pos0 + l.
-__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ cs, int64_t n, int d,
+// A thread keeps one pair j (d/2 divides the block) and fills kTablePosPerThread
+// positions with it, so the fp64 omega_j is formed once per thread.
+constexpr int kTablePosPerThread = 4;
+
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ cs, int64_t L, int d,
                                                          int64_t pos0, RopeParams rp) {
   const int half = d >> 1;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t l = idx / half;
-    const int j = (int)(idx - l * half);
+  const int rows = 256 / half;                       // positions per block and step
+  const int j = threadIdx.x % half;
+  const double omega = rope_omega(j, d, rp);
+  const int64_t l0 = (int64_t)blockIdx.x * rows * kTablePosPerThread + threadIdx.x / half;
+#pragma unroll
+  for (int i = 0; i < kTablePosPerThread; ++i) {
+    const int64_t l = l0 + (int64_t)i * rows;
+    if (l >= L) break;
     float c, s;
-    rope_cs((double)(pos0 + l), j, d, rp, c, s);
-    cs[idx] = make_float2(c, s);
+    rope_cos_sin((double)(pos0 + l), omega, c, s);
+    cs[l * half + j] = make_float2(c * rp.mscale, s * rp.mscale);
   }
 }
 
 hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, RopeParams rp,
                              hipStream_t st) {
-  const int64_t n = L * (d / 2);
-  const int64_t want = (n + 255) / 256;
-  const int grid = (int)(want < 65536 ? want : 65536);
-  rope_table_kernel<<<grid, 256, 0, st>>>(cs, n, d, pos0, rp);
+  if (d < 2 || 256 % (d / 2) != 0) return hipErrorInvalidValue;
+  const int64_t per_block = (int64_t)(256 / (d / 2)) * kTablePosPerThread;
+  const int64_t grid = (L + per_block - 1) / per_block;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  rope_table_kernel<<<(unsigned)grid, 256, 0, st>>>(cs, L, d, pos0, rp);
   return hipGetLastError();
 }
 
@@ -107,30 +116,53 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, RopePar
 // cache [B, cap, h_kv, d].  The source rows of sequence b start at
 // k + b * src_rows * h_kv * d (src_rows = L for the call's own K/V, cap for a
 // cache).  With kstart set, sequence b has kstart[b] + klen[b] rows (0 if
-// that is not within [0, kend]); with cs NULL the source K is taken as
-// already rotated (a cache).
+// that is not within [0, kend]).  With rotate set, key j is turned at
+// position j: the kernel forms each (cos, sin) itself, as the table kernel
+// does, and the workgroups of sequence 0, group 0 also store them to
+// cs_out[j][pair] (if set) for the attention kernel's queries, so no table
+// launch precedes this one; with rotate 0 the source K is taken as already
+// rotated (a cache).
 template <int D>
-__global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float2* __restrict__ cs,
-    uint16_t* __restrict__ kp, uint16_t* __restrict__ vt, float* __restrict__ kmax,
-    int* __restrict__ kexp, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t L,
-    int64_t Lpad, int h_kv, int64_t cap, int64_t src_rows, const int64_t* __restrict__ kstart,
-    const int64_t* __restrict__ klen, int64_t kend) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void kv_prepare_bf16_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rotate, RopeParams rp,
+    float2* __restrict__ cs_out, uint16_t* __restrict__ kp, uint16_t* __restrict__ vt,
+    float* __restrict__ kmax, int* __restrict__ kexp, uint16_t* __restrict__ kc,
+    uint16_t* __restrict__ vc, int64_t L, int64_t Lpad, int h_kv, int64_t cap, int64_t src_rows,
+    const int64_t* __restrict__ kstart, const int64_t* __restrict__ klen, int64_t kend) {
   constexpr int TK = 64;
   constexpr int HALF = D / 2;
   constexpr int PP = HALF / 4;        // RoPE pairs per thread: 4 threads per key row
   constexpr int TV = kPrefillTileV;
   __shared__ __attribute__((aligned(16))) uint16_t vs[TK][D + 8];
   __shared__ float wred[4];
+  __shared__ double om[HALF];
   const int tile = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t key0 = (int64_t)tile * TK;
+  // the pairs' frequencies, before any load is in flight (so the barrier
+  // waits for nothing but them)
+  if (rotate) {
+    if (tid < HALF) om[tid] = rope_omega(tid, D, rp);
+    __syncthreads();
+  }
   if (kstart) {   // keys of sequence b: rows 0 .. kstart[b] + klen[b] - 1 of the source
     const int64_t s0 = kstart[b], n = klen ? klen[b] : L;
     L = (s0 >= 0 && n >= 0 && n <= L && s0 + n <= kend) ? s0 + n : 0;
   }
   const int kk = tid >> 2, part = tid & 3;
   const int64_t key = key0 + kk;
+  // ---- V rows of the tile, 16 bytes per thread and step: issued first, so
+  // that their latency overlaps the K loads and the rotation
+  constexpr int VSTEPS = TK * D / 8 / 256;
+  u32x4 vval[VSTEPS];
+#pragma unroll
+  for (int i = 0; i < VSTEPS; ++i) {
+    const int c = tid + 256 * i;
+    const int64_t vkey = key0 + c / (D / 8);
+    vval[i] = u32x4{0u, 0u, 0u, 0u};
+    if (vkey < L) vval[i] = *(const u32x4*)(v + (((int64_t)b * src_rows + vkey) * h_kv + u) * D +
+                                            (c % (D / 8)) * 8);
+  }
   // ---- this thread's quarter of a K row, rotated (or as given), in fp32
   float y1[PP], y2[PP];
   float amax = 0.f;
@@ -142,14 +174,26 @@ __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
       *(u32x4*)&x1[c * 8] = *(const u32x4*)(src + c * 8);
       *(u32x4*)&x2[c * 8] = *(const u32x4*)(src + HALF + c * 8);
     }
-    if (cs) {   // rotate here; otherwise the source rows are rotated already
-      const float2* csr = cs + key * HALF + part * PP;
+    if (rotate) {   // rotate here; otherwise the source rows are rotated already
+      // (cos, sin) of this thread's pairs at position key, formed while the
+      // loads are in flight
+      float2 r[PP];
 #pragma unroll
       for (int e = 0; e < PP; ++e) {
-        const float2 r = csr[e];
+        float c, sn;
+        rope_cos_sin((double)key, om[part * PP + e], c, sn);
+        r[e] = make_float2(c * rp.mscale, sn * rp.mscale);
+      }
+      if (cs_out && u == 0 && b == 0) {
+        float2* dst = cs_out + key * HALF + part * PP;
+#pragma unroll
+        for (int e = 0; e < PP; e += 2) *(f32x4*)(dst + e) = f32x4{r[e].x, r[e].y, r[e + 1].x, r[e + 1].y};
+      }
+#pragma unroll
+      for (int e = 0; e < PP; ++e) {
         const float a = bf16_bits_to_f32(x1[e]), bb = bf16_bits_to_f32(x2[e]);
-        y1[e] = fmaf(a, r.x, -bb * r.y);
-        y2[e] = fmaf(bb, r.x, a * r.y);
+        y1[e] = fmaf(a, r[e].x, -bb * r[e].y);
+        y2[e] = fmaf(bb, r[e].x, a * r[e].y);
       }
     } else {
 #pragma unroll
@@ -182,16 +226,15 @@ __global__ __launch_bounds__(256) void kv_prepare_bf16_kernel(
   for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
   if ((tid & 63) == 0) wred[tid >> 6] = amax;
 
-  // ---- V rows into LDS (and the cache copy), 16 bytes per thread and step
-  for (int c = tid; c < TK * D / 8; c += 256) {
+  // ---- V rows into LDS (and the cache copy)
+#pragma unroll
+  for (int i = 0; i < VSTEPS; ++i) {
+    const int c = tid + 256 * i;
     const int vk = c / (D / 8), c8 = c % (D / 8);
     const int64_t vkey = key0 + vk;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (vkey < L) {
-      val = *(const u32x4*)(v + (((int64_t)b * src_rows + vkey) * h_kv + u) * D + c8 * 8);
-      if (vc) *(u32x4*)(vc + (((int64_t)b * cap + vkey) * h_kv + u) * D + c8 * 8) = val;
-    }
-    *(u32x4*)&vs[vk][c8 * 8] = val;
+    if (vc && vkey < L)
+      *(u32x4*)(vc + (((int64_t)b * cap + vkey) * h_kv + u) * D + c8 * 8) = vval[i];
+    *(u32x4*)&vs[vk][c8 * 8] = vval[i];
   }
   __syncthreads();
 
@@ -285,21 +328,24 @@ __global__ __launch_bounds__(256) void kv_prepare_f32_kernel(
   }
 }
 
-hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const float2* cs,
-                                  uint16_t* kp, uint16_t* vt, float* kmax, int* kexp,
-                                  uint16_t* kc, uint16_t* vc, int64_t B, int64_t L, int64_t Lpad,
-                                  int h_kv, int d, int64_t cap, int64_t src_rows,
+hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const RopeParams* rope,
+                                  float2* cs_out, uint16_t* kp, uint16_t* vt, float* kmax,
+                                  int* kexp, uint16_t* kc, uint16_t* vc, int64_t B, int64_t L,
+                                  int64_t Lpad, int h_kv, int d, int64_t cap, int64_t src_rows,
                                   const int64_t* kstart, const int64_t* klen, int64_t kend,
                                   hipStream_t st) {
+  if (cs_out && !rope) return hipErrorInvalidValue;
+  const int rotate = rope != nullptr;
+  const RopeParams rp = rope ? *rope : RopeParams{};
   dim3 grid((unsigned)(Lpad / 64), (unsigned)h_kv, (unsigned)B);
   if (d == 128)
-    kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kexp, kc, vc, L,
-                                                      Lpad, h_kv, cap, src_rows, kstart, klen,
-                                                      kend);
+    kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, rotate, rp, cs_out, kp, vt, kmax,
+                                                      kexp, kc, vc, L, Lpad, h_kv, cap, src_rows,
+                                                      kstart, klen, kend);
   else
-    kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, vt, kmax, kexp, kc, vc, L,
-                                                     Lpad, h_kv, cap, src_rows, kstart, klen,
-                                                     kend);
+    kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, rotate, rp, cs_out, kp, vt, kmax,
+                                                     kexp, kc, vc, L, Lpad, h_kv, cap, src_rows,
+                                                     kstart, klen, kend);
   return hipGetLastError();
 }
 
