@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(
 // blocks (another pass over the chunk).  The cache is read once, so its
 // loads are non-temporal (they do not displace reused lines in the caches).
 template <int D, bool PAGED>
-__global__ __launch_bounds__(256) void decode_split_bf16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
     float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int kv_len_max, double q_pos_s,
@@ -260,6 +260,35 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
   } else if (PAGED && !stage_pages(kr, b, chunk0, min(chunk0 + CH, kv_len), pg)) {
     write_flat_state(pm, pl, po, out0, nh, D, __builtin_nanf(""));
   } else {
+    const int kw0 = chunk0 + wave * WK;
+    const int kw1 = min(kw0 + WK, kv_len);
+    // one 32-key step's K and V rows, 16 bytes per load, non-temporal
+    auto load_step = [&](int k0, u32x4 (&ka)[2][NS], u32x4 (&va)[VLD]) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int key = min(k0 + blk * 16 + col, kv_len - 1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          ka[blk][s] = __builtin_nontemporal_load(
+              (const u32x4*)(kc + kv_row<PAGED>(kr, pg, chunk0, b, key, u, h_kv, D) + s * 32 +
+                             h4 * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < VLD; ++i) {
+        const int ch = lane + 64 * i;
+        const int key = min(k0 + ch / (D / 8), kv_len - 1);
+        va[i] = __builtin_nontemporal_load(
+            (const u32x4*)(vc + kv_row<PAGED>(kr, pg, chunk0, b, key, u, h_kv, D) +
+                           (ch % (D / 8)) * 8));
+      }
+    };
+
+    // the first step's loads go out before the query rotation; then each
+    // step's loads go out before the previous step is computed (two register
+    // buffers, the loop unrolled by two so that neither is copied)
+    u32x4 kaA[2][NS], vaA[VLD], kaB[2][NS], vaB[VLD];
+    if (kw0 < kw1) load_step(kw0, kaA, vaA);
+
     // ---- rotated query, B operand: lane holds head `col`, dims
     // s*32 + h4*8 + e (rotated here at the query position unless q_rotated)
     bf16x8 qb[NS];
@@ -288,35 +317,14 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
       }
     }
 
-    const int kw0 = chunk0 + wave * WK;
-    const int kw1 = min(kw0 + WK, kv_len);
-
     float m = -INFINITY, l = 0.f;
     f32x4 oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     uint16_t* vw = vsh[wave];
 
-    for (int k0 = kw0; k0 < kw1; k0 += 32) {
-      u32x4 ka[2][NS];
-      u32x4 va[VLD];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int key = min(k0 + blk * 16 + col, kv_len - 1);
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-          ka[blk][s] = __builtin_nontemporal_load(
-              (const u32x4*)(kc + kv_row<PAGED>(kr, pg, chunk0, b, key, u, h_kv, D) + s * 32 +
-                             h4 * 8));
-      }
-#pragma unroll
-      for (int i = 0; i < VLD; ++i) {
-        const int ch = lane + 64 * i;
-        const int key = min(k0 + ch / (D / 8), kv_len - 1);
-        va[i] = __builtin_nontemporal_load(
-            (const u32x4*)(vc + kv_row<PAGED>(kr, pg, chunk0, b, key, u, h_kv, D) +
-                           (ch % (D / 8)) * 8));
-      }
+    // scores, online softmax and P.V of the step at k0
+    auto compute_step = [&](int k0, const u32x4 (&ka)[2][NS], const u32x4 (&va)[VLD]) {
       // S^T for 2 x 16 keys
       f32x4 sacc[2];
 #pragma unroll
@@ -373,6 +381,14 @@ __global__ __launch_bounds__(256) void decode_split_bf16_kernel(
         }
         oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[db], 0, 0, 0);
       }
+    };
+
+    for (int k0 = kw0; k0 < kw1; k0 += 64) {
+      if (k0 + 32 < kw1) load_step(k0 + 32, kaB, vaB);
+      compute_step(k0, kaA, vaA);
+      if (k0 + 32 >= kw1) break;
+      if (k0 + 64 < kw1) load_step(k0 + 64, kaA, vaA);
+      compute_step(k0 + 32, kaB, vaB);
     }
 
     // ---- combine the four waves of the workgroup
