@@ -56,12 +56,14 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
 # device copy: FETCH x 2.00, WRITE x 1.00).  Each figure is valid only for the
 # kernel source it was measured on (sha256 prefix); otherwise it reports null.
 TRAFFIC = {
-    "prefill": ("prefill_bf16.hip", "a39c81251f7e97a7", (117359.6 * 2.0 + 249996.4) * 1024),
-    "decode": ("decode.hip", "55c3dd751eae0bac", (1058368.0 * 2.0 + 14784.1) * 1024),
-    "prefill_chunk": ("prefill_bf16.hip", "a39c81251f7e97a7", (44209.8 * 2.0 + 61692.1) * 1024),
-    "decode_append": ("decode.hip", "55c3dd751eae0bac", (928761.8 * 2.0 + 14784.1) * 1024),
-    "decode_paged": ("decode.hip", "55c3dd751eae0bac", (1054822.1 * 2.0 + 14784.1) * 1024),
-    "qkv_epilogue": ("rope.hip", "72eefc0ef755f754", (73831.7 * 2.0 + 147459.8) * 1024),
+    "prefill": ("prefill_bf16.hip", "5a0274e7d6375f51", (117414.6 * 2.0 + 250531.0) * 1024),
+    "prefill_c4": ("prefill_bf16.hip", "5a0274e7d6375f51", (324821.7 * 2.0 + 692004.2) * 1024),
+    "prefill_c5": ("prefill_bf16.hip", "5a0274e7d6375f51", (676127.8 * 2.0 + 484678.4) * 1024),
+    "decode": ("decode.hip", "fd82fbbe8f8a4ee2", (1057044.5 * 2.0 + 14784.0) * 1024),
+    "prefill_chunk": ("prefill_bf16.hip", "5a0274e7d6375f51", (44227.1 * 2.0 + 61504.0) * 1024),
+    "decode_append": ("decode.hip", "fd82fbbe8f8a4ee2", (929142.8 * 2.0 + 14784.1) * 1024),
+    "decode_paged": ("decode.hip", "fd82fbbe8f8a4ee2", (1056325.5 * 2.0 + 14784.1) * 1024),
+    "qkv_epilogue": ("rope.hip", "3a77080a2e9aa0cd", (73829.2 * 2.0 + 147461.5) * 1024),
 }
 
 
@@ -259,7 +261,7 @@ def measure_other_prefills(torch, gqa, dev, keys=("c1", "c4", "c5"), warmup=10, 
                     "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": ach,
                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                  "frac": ach / PEAK_BF16_TFLOPS, "kernel_ms": kern_ms,
-                                 "traffic": None}}
+                                 "traffic": traffic_bytes("prefill_" + key)}}
         log(f"[bench] {key}: attention {kern_ms:.3f} ms -> {ach:.0f} TFLOP/s")
         del qd, kd, vd, od, ws
         torch.cuda.empty_cache()
