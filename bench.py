@@ -164,28 +164,23 @@ def clock_warmup(torch, step, seconds):
 
 
 def no_children_left():
-    """Child processes still running at exit, for the log.  The oracle pool's
-    workers are joined when it closes; the "spawn" start method's resource
-    tracker (it ignores SIGTERM) ends by itself when this process exits, as
-    it reads a pipe from it.  Anything else is ended here."""
+    """Child processes still running at exit, for the log; each is ended
+    here.  The oracle pool's workers are joined when it closes, and its
+    semaphore helper process is stopped after the oracle leg, so none is
+    expected."""
     try:
         import psutil
     except ImportError:
         return "psutil unavailable"
-    tracker, other = 0, []
+    left = []
     for p in psutil.Process().children(recursive=True):
         try:
-            cmd = " ".join(p.cmdline())
-            if "resource_tracker" in cmd:
-                tracker += 1
-                continue
-            other.append(cmd[:100])
+            left.append(" ".join(p.cmdline())[:100])
             p.kill()
             p.wait(timeout=5)
         except psutil.Error:
             pass
-    return (f"child processes at exit: {tracker} resource tracker (ends with this process), "
-            f"{len(other)} other{' (killed: ' + str(other) + ')' if other else ''}")
+    return f"child processes at exit: {len(left)}{' (ended: ' + str(left) + ')' if left else ''}"
 
 
 def measure_context(torch, gqa, dev):
@@ -611,6 +606,8 @@ def main():
     if run_p and not args.no_cpu_baseline:
         log("[bench] fp64 oracle on the host cores: CPU baseline and parity of the timed calls")
         out.update(oracle_leg(wp, wd, got_prefill, got_decode))
+        from oracle import pool as opool
+        opool.stop_resource_tracker()
     log(f"[bench] {no_children_left()}")
     print(json.dumps(out), flush=True)
 

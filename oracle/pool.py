@@ -106,6 +106,28 @@ def oracle_pool(workers: int | None = None):
         pool.join()
 
 
+def stop_resource_tracker() -> bool:
+    """End the helper process that the "spawn" start method keeps for the
+    pools' named semaphores, once every pool is closed, so that the caller
+    leaves no process behind.  The closed pools are collected first: their
+    semaphores unregister through the helper while it still runs.  Closing
+    its pipe makes it exit; it is then waited for.  A later pool starts a
+    new one.  Returns whether one was running."""
+    import gc
+    from multiprocessing import resource_tracker
+    gc.collect()
+    tracker = resource_tracker._resource_tracker
+    with tracker._lock:
+        fd, pid = tracker._fd, tracker._pid
+        if fd is None or pid is None:
+            return False
+        os.close(fd)
+        tracker._fd = None
+        tracker._pid = None
+        os.waitpid(pid, 0)
+    return True
+
+
 def prefill_tasks(key: str, overrides: tuple = (), rows_per_piece: int = 512,
                   batches=None, groups=None, theta=None):
     """Pieces (b, u, r0, r1) of a prefill workload, the ones with the most

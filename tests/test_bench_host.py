@@ -53,11 +53,19 @@ def test_traffic_figures_match_the_profile_summary():
     for m in re.finditer(r"^\| `([^`]+)` \(([^)]*)\) \| ([\d,\.]+) \| ([\d,\.]+) \|", text, re.M):
         kern, site = m.group(1), m.group(2)
         rows[(kern, site)] = (float(m.group(3).replace(",", "")), float(m.group(4).replace(",", "")))
+    pk = "prefill_bf16_kernel<128, false, true>"
     sites = {
-        "prefill": ("prefill_bf16_kernel<128, false, true>", "`gqa_prefill`, c2"),
-        "prefill_chunk": ("prefill_bf16_kernel<128, false, true>",
-                          "`gqa_prefill_chunk`, rows 3072..4095"),
+        "prefill": (pk, "`gqa_prefill`, 7B B4 L4096"),
+        "prefill_c4": (pk, "`gqa_prefill`, 72B B2 L8192"),
+        "prefill_c5": (pk, "`gqa_prefill`, 7B B1 L32768"),
+        "prefill_chunk": (pk, "`gqa_prefill_chunk`, rows 3072..4095"),
+        "decode": ("decode_split_bf16_kernel<128, false>", "`gqa_decode`, 7B B32 x 32768"),
+        "decode_append": ("decode_split_bf16_kernel<128, false>", "`gqa_decode_append`"),
+        "decode_paged": ("decode_split_bf16_kernel<128, true>", "`gqa_decode_paged`"),
+        "qkv_epilogue": ("qkv_epilogue_kernel<unsigned short>",
+                         "`gqa_qkv_epilogue`, 7B B4 L4096 projections"),
     }
+    assert set(sites) == set(bench.TRAFFIC)
     for which, key in sites.items():
         assert key in rows, key
         fetch, write = rows[key]

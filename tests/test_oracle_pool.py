@@ -41,3 +41,22 @@ def test_comparison_statistics():
     assert cmp.max_abs == 0.5 and cmp.worst == "a"
     assert cmp.nonfinite == 1
     assert abs(cmp.rel_l2 - 0.5 / np.sqrt(26.0)) < 1e-15
+
+
+def test_pool_leaves_no_process_behind():
+    """After the pools close, stopping the semaphore helper of the "spawn"
+    start method leaves this process without children; a later pool works
+    and starts its own helper."""
+    import psutil
+
+    def one_pool():
+        with opool.oracle_pool(2) as pool:
+            return dict(opool.decode_pieces(pool, "c3", (("L", 64), ("B", 2))))
+
+    assert sorted(one_pool()) == [0, 1]
+    opool.stop_resource_tracker()
+    assert psutil.Process().children(recursive=True) == []
+    assert sorted(one_pool()) == [0, 1]
+    assert opool.stop_resource_tracker()
+    assert not opool.stop_resource_tracker()   # nothing left to stop
+    assert psutil.Process().children(recursive=True) == []
