@@ -123,11 +123,13 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
  * errors are those of gqa_decode; the chunk states live in a static array of
  * GQA_DECODE_NOALLOC_SCRATCH_BYTES that the library's code object reserves on
  * every GPU it runs on (held until the process ends).  A step needs
- *   B * h_q * ceil(kv_len / 1024) * (d + 2) * 4 bytes (each of its three
- *   parts rounded up to 256) + B * h_q * d * 4 (rounded up to 256);
+ *   B * h_q * ceil(kv_len / C) * (d + 2) * 4 bytes (each of its three
+ *   parts rounded up to 256) + B * h_q * d * 4 (rounded up to 256),
+ *   C = 2048 keys per chunk for GQA_BF16 and 1024 for GQA_F32;
  * a step beyond the limit returns GQA_ERR_UNSUPPORTED before anything is
- * enqueued (for d = 128 about 63,000 pairs of a query head and a 1024-key
- * chunk: B = 32, h_q = 28 fit up to kv_len = 65536).  The call allocates
+ * enqueued (for d = 128 about 63,000 pairs of a query head and a chunk:
+ * B = 32, h_q = 28 fit up to kv_len = 131072 in bf16, 65536 in fp32).  The
+ * call allocates
  * nothing.  All calls on one GPU share its scratch: two calls whose work
  * overlaps on the device (on different streams, or from several threads on
  * one device without ordering) race and give wrong results; calls ordered

@@ -153,9 +153,9 @@ struct DecodeWs {
 
 // partial states per (b, u, chunk, head); rotated queries [B, h_q, d] of an
 // appending step (fp32 size, so one layout serves both input types)
-DecodeWs decode_ws(int64_t B, int h_q, int h_kv, int d, int64_t cap) {
+DecodeWs decode_ws(int64_t B, int h_q, int h_kv, int d, int64_t cap, bool bf16 = false) {
   const int g = h_q / h_kv;
-  const size_t n = (size_t)B * h_kv * gqa::decode_num_splits(cap) * g;
+  const size_t n = (size_t)B * h_kv * gqa::decode_num_splits(cap, bf16) * g;
   DecodeWs w{};
   w.m_off = 0;
   w.l_off = align256(n * 4);
@@ -321,7 +321,8 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, void* o
     return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   // the chunk states are laid out for the chunks of kv_len keys (the caller's
   // workspace is sized by cap, which only leaves room to spare)
-  const DecodeWs ws = decode_ws(B, h_q, h_kv, d, noalloc ? kv_len : cap);
+  const DecodeWs ws = noalloc ? decode_ws(B, h_q, h_kv, d, kv_len, in_dtype == GQA_BF16)
+                               : decode_ws(B, h_q, h_kv, d, cap);
   if (noalloc) {
     if (ws.total > gqa::kDecodeScratchBytes)
       return fail(GQA_ERR_UNSUPPORTED,

@@ -5,9 +5,9 @@
 // aicoding.csdn.net, §4.1.3: the cache holds only the h_kv groups' K and V,
 // appended every step).  The query is rotated here at q_pos.
 //
-// The cache of one (batch, group) is cut into chunks of kDecodeChunk keys;
-// a workgroup streams one chunk exactly once for all g query heads of the
-// group (that single pass over the h_kv-group cache is what GQA saves in
+// The cache of one (batch, group) is cut into chunks of kDecodeChunkBf16
+// (bf16) or kDecodeChunk (fp32) keys; a workgroup streams one chunk exactly
+// once for all g query heads of the group (that single pass over the h_kv-group cache is what GQA saves in
 // bandwidth, same page §4.1.1) and leaves an unnormalised partial state
 // (row max m, sum l, weighted sum o).  A second kernel merges the chunks:
 //   M = max_s m_s,  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
@@ -122,8 +122,9 @@ __device__ void write_flat_state(float* pm, float* pl, float* po, int64_t out0, 
 
 }  // namespace
 
-int decode_num_splits(int64_t kv_len) {
-  return (int)((kv_len + kDecodeChunk - 1) / kDecodeChunk);
+int decode_num_splits(int64_t kv_len, bool bf16) {
+  const int ch = bf16 ? kDecodeChunkBf16 : kDecodeChunk;
+  return (int)((kv_len + ch - 1) / ch);
 }
 
 // Chunk states of an allocation-free decode call, in device memory that the
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     float* __restrict__ po, int h_q, int h_kv, int g, int n_hb, int kv_len_max, double q_pos_s,
     RopeParams rp, float sl2, int n_split, const int64_t* __restrict__ kvl_arr,
     const int64_t* __restrict__ qpos_arr, int kvl_from_pos, int q_rotated, KvRows kr) {
-  constexpr int CH = kDecodeChunk;
+  constexpr int CH = kDecodeChunkBf16;
   constexpr int WK = CH / 4;            // keys per wave
   constexpr int NS = D / 32;            // 32-dim k-steps of S^T
   constexpr int NDB = D / 16;           // 16-dim blocks of O^T
@@ -569,7 +570,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t
                          hipEvent_t ev_begin, hipEvent_t ev_end) {
   const int g = a.h_q / a.h_kv;
   const int n_hb = (g + 15) / 16;
-  const int n_split = decode_num_splits(a.kv_len);
+  const int n_split = decode_num_splits(a.kv_len, a.in_bf16);
   const KvRows kr{a.bt, a.ps_log2, a.max_pages, a.num_pages, a.cap};
   const void* q = a.q;
   int q_rotated = a.q_rotated;

@@ -12,7 +12,8 @@ namespace gqa {
 constexpr int kPrefillTileK = 64;      // key padding granule of the prepared K/V
 constexpr int kPrefillTileV = 32;      // keys per attention tile; V^T is stored per such tile
 constexpr int kPrefillRowsWG = 256;    // stacked (position, head) rows per workgroup
-constexpr int kDecodeChunk = 1024;     // keys per decode split
+constexpr int kDecodeChunk = 1024;     // keys per decode split (fp32 cache)
+constexpr int kDecodeChunkBf16 = 2048; // keys per decode split (bf16 cache)
 constexpr int kDecodeMaxSplits = 8192;  // bound on the chunks of one sequence (8M keys)
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;  // static scratch of gqa_decode_noalloc
 
@@ -68,7 +69,9 @@ hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, c
                               const int64_t* qstart, const int64_t* qlen, int64_t kend,
                               hipStream_t st);
 
-int decode_num_splits(int64_t kv_len);
+// chunks of a sequence of kv_len keys; the fp32 count (the larger) sizes
+// workspaces
+int decode_num_splits(int64_t kv_len, bool bf16 = false);
 // Device address of this library's static decode scratch (kDecodeScratchBytes)
 // on the current device, looked up once per device.
 hipError_t decode_scratch(void** ptr);

@@ -47,8 +47,8 @@ def both(q, kc, vc, kv_len, q_pos, out_dtype):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_noalloc_decode_equals_workspace_decode(dtype):
-    # 1) the 7B decode step: B 32, cache 32768, 28/4 heads, d 128 (32 chunks
-    #    per sequence: 14.9 MB of the 32 MiB scratch)
+    # 1) the 7B decode step: B 32, cache 32768, 28/4 heads, d 128 (16 chunks
+    #    per sequence in bf16, 32 in fp32: 7.5 / 14.9 MB of the 32 MiB scratch)
     B, cap, h_q, h_kv, d = 32, 32768, 28, 4, 128
     note(f"noalloc decode {dtype}: B{B} cache {cap} {h_q}/{h_kv} d{d}")
     g = torch.Generator(device="cuda").manual_seed(11)
@@ -62,8 +62,9 @@ def test_noalloc_decode_equals_workspace_decode(dtype):
     del q, kc, vc
     torch.cuda.empty_cache()
 
-    # 2) a smaller step right after (3 chunks; the scratch still holds the
-    #    large step's states): equal to gqa_decode and within the bars
+    # 2) a smaller step right after (2 chunks in bf16, 3 in fp32; the scratch
+    #    still holds the large step's states): equal to gqa_decode and within
+    #    the bars
     B, kv_len, q_pos, h_q, h_kv, d = 3, 2500, 2600, 28, 4, 128
     note(f"noalloc decode {dtype}: B{B} kv {kv_len} qpos {q_pos} {h_q}/{h_kv} d{d}")
     qh, kch, vch = small_inputs(B, kv_len + 37, h_q, h_kv, d, dtype, 1300)
@@ -90,7 +91,7 @@ def test_noalloc_decode_equals_workspace_decode(dtype):
 def test_noalloc_rejects_a_step_past_the_scratch():
     """A step whose chunk states exceed the static scratch is refused before
     anything is enqueued, with a message naming the limit."""
-    B, cap, h_q, h_kv, d = 32, 1 << 17, 28, 4, 128     # 128 chunks: 59.6 MB of states
+    B, cap, h_q, h_kv, d = 32, 1 << 18, 28, 4, 128     # 128 bf16 chunks: 59.6 MB of states
     q = torch.zeros((B, h_q, d), dtype=torch.bfloat16, device="cuda")
     kc = torch.zeros((B, cap, h_kv, d), dtype=torch.bfloat16, device="cuda")
     out = torch.zeros((B, h_q, d), dtype=torch.float32, device="cuda")
