@@ -517,14 +517,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // (every score lies in [-crow, crow]), which the scores need no shift for
   if (crow <= kBoundHeadroom) m_run = 0.f;
 
-  // ---- periods t = 0 .. 2 n_tiles + 1, each ending at a barrier.  Even
-  // period 2i: waves 0-3 run matrix phase i (V(i-1), K(i)), waves 4-7 vector
-  // phase i-1 and load K(i+1).  Odd period 2i+1: waves 0-3 run vector phase
-  // i and load V(i), waves 4-7 matrix phase i.  Tile t sits in slot t % 2; a
-  // load overwrites the tile read two periods before and has landed at the
-  // barrier that ends its period (past the last tile, waves 4-7 load the
-  // last K again, into the slot nobody reads any more).  The loop runs
-  // i = 1 .. n-1 unrolled by two, so every slot is static.
+  // ---- periods t = 0 .. 2 n_tiles + 1, each but the last ending at a
+  // barrier.  Even period 2i: waves 0-3 run matrix phase i (V(i-1), K(i)),
+  // waves 4-7 vector phase i-1 and load K(i+1).  Odd period 2i+1: waves 0-3
+  // run vector phase i and load V(i), waves 4-7 matrix phase i.  Tile t sits
+  // in slot t % 2; a load overwrites the tile read two periods before and
+  // has landed at the barrier that ends its period (past the last tile,
+  // waves 4-7 load the last K again, into the slot nobody reads any more).
+  // The loop runs i = 1 .. n-1 unrolled by two, so every slot is static.
   auto step0 = [&](auto P, int i) {        // waves 0-3, P = i mod 2
     matrix_full(P);                        // period 2i
     bar();
@@ -556,7 +556,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     run(step0);
     matrix_pv(n);                           // period 2n
     bar();
-    bar();                                  // period 2n+1
+    // period 2n+1: this group's O is final; it is written below while
+    // waves 4-7 run the last P.V (no barrier: nothing writes LDS any more)
   } else {
     load_tile(ks1, min(1, n - 1));          // period 0
     bar();
@@ -566,7 +567,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     vector_phase(n - 1);                    // period 2n
     bar();
     matrix_pv(n);                           // period 2n+1
-    bar();
   }
 
   // ---- epilogue: O = O / l; lane holds dims db*32 + gq*8 + hl*4 + (0..3)
