@@ -26,11 +26,11 @@
 // in log2 units.  fp16 ends at 65504: a row whose Q' * scale * log2(e) has
 // an element of magnitude 2^14 or more, and every row of a workgroup whose
 // keys hold such a rotated K element (the preparation pass flags the tile),
-// gets NaN operands and so NaN output; nothing is checked inside the loop.  The
-// probabilities, rounded to bf16, are already in the B-operand
-// layout of O^T += V^T P^T on v_mfma_f32_32x32x16_bf16; V arrives
-// pre-transposed (keys contiguous, in the accumulator's lane order) from the
-// preparation pass, in 32-key sub-tiles.
+// gets NaN operands and so NaN output; nothing is checked inside the loop.
+// The probabilities, rounded to bf16, are already in the B-operand layout of
+// O^T += V^T P^T on v_mfma_f32_32x32x16_bf16; V arrives pre-transposed (keys
+// contiguous, in the accumulator's lane order) from the preparation pass, in
+// 32-key sub-tiles.
 //
 // Ping-pong schedule.  Each wave alternates between a matrix phase (P.V of
 // tile i-1, then S^T of tile i) and a vector phase (softmax of tile i).
