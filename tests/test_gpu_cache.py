@@ -94,8 +94,10 @@ def test_decode_append_ragged(dtype, heads):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_decode_ragged(dtype):
     h_q, h_kv, d = (28, 4, 128) if dtype == torch.bfloat16 else (14, 2, 64)
-    kv_len = np.array([1, 1024, 1025, 3000, 77])
-    q_pos = np.array([0, 1023, 5000, 2999, 200])
+    # lengths on both sides of the chunk boundaries (1024 keys per fp32
+    # chunk, 2048 per bf16 chunk)
+    kv_len = np.array([1, 1024, 1025, 3000, 77, 2048, 2049])
+    q_pos = np.array([0, 1023, 5000, 2999, 200, 2047, 2100])
     B, cap = len(kv_len), 3000
     note(f"decode_ragged {dtype} kv_len={kv_len.tolist()}")
     q, k, v = inputs(B, cap, h_q, h_kv, d, dtype, 32)

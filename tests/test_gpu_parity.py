@@ -217,7 +217,11 @@ def test_prefill_writes_cache_and_decode_continues(dtype):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("shape", [(3, 2500, 2600, 28, 4, 128), (2, 1, 5, 14, 2, 64),
                                    (1, 1024, 1024, 16, 2, 128), (2, 700, 800, 8, 8, 64),
-                                   (1, 300, 301, 40, 2, 128)],
+                                   (1, 300, 301, 40, 2, 128),
+                                   # chunk boundaries (2048 keys per bf16 chunk, 1024 per
+                                   # fp32 chunk): exactly one chunk, one key into the next
+                                   (1, 2048, 2048, 28, 4, 128), (2, 2049, 2049, 28, 4, 128),
+                                   (1, 4095, 5000, 14, 2, 64)],
                          ids=lambda s: "B%d_kv%d_qpos%d_%d/%d_d%d" % s)
 def test_decode_small(dtype, shape):
     B, kv_len, q_pos, h_q, h_kv, d = shape
