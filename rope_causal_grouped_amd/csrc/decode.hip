@@ -263,16 +263,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   } else {
     const int kw0 = chunk0 + wave * WK;
     const int kw1 = min(kw0 + WK, kv_len);
-    // one 32-key step's K and V rows, 16 bytes per load, non-temporal
-    auto load_step = [&](int k0, u32x4 (&ka)[2][NS], u32x4 (&va)[VLD]) {
+    // one 32-key step's K and V rows, 16 bytes per load, non-temporal; D/8
+    // lanes read one whole row, so a load covers a few complete rows (the
+    // rows of a group lie at a stride of h_kv rows in the contiguous cache)
+    auto load_step = [&](int k0, u32x4 (&ka)[VLD], u32x4 (&va)[VLD]) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int key = min(k0 + blk * 16 + col, kv_len - 1);
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-          ka[blk][s] = __builtin_nontemporal_load(
-              (const u32x4*)(kc + kv_row<PAGED>(kr, pg, chunk0, b, key, u, h_kv, D) + s * 32 +
-                             h4 * 8));
+      for (int i = 0; i < VLD; ++i) {
+        const int ch = lane + 64 * i;
+        const int key = min(k0 + ch / (D / 8), kv_len - 1);
+        ka[i] = __builtin_nontemporal_load(
+            (const u32x4*)(kc + kv_row<PAGED>(kr, pg, chunk0, b, key, u, h_kv, D) +
+                           (ch % (D / 8)) * 8));
       }
 #pragma unroll
       for (int i = 0; i < VLD; ++i) {
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // the first step's loads go out before the query rotation; then each
     // step's loads go out before the previous step is computed (two register
     // buffers, the loop unrolled by two so that neither is copied)
-    u32x4 kaA[2][NS], vaA[VLD], kaB[2][NS], vaB[VLD];
+    u32x4 kaA[VLD], vaA[VLD], kaB[VLD], vaB[VLD];
     if (kw0 < kw1) load_step(kw0, kaA, vaA);
 
     // ---- rotated query, B operand: lane holds head `col`, dims
@@ -325,8 +326,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     uint16_t* vw = vsh[wave];
 
     // scores, online softmax and P.V of the step at k0
-    auto compute_step = [&](int k0, const u32x4 (&ka)[2][NS], const u32x4 (&va)[VLD]) {
-      // S^T for 2 x 16 keys
+    auto compute_step = [&](int k0, const u32x4 (&ka)[VLD], const u32x4 (&va)[VLD]) {
+      // K rows -> the wave's LDS slab (row-major), then the A operands of
+      // S^T for 2 x 16 keys: lane (col, h4) takes dims s*32 + h4*8 .. +7 of
+      // key blk*16 + col
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();   // the previous step's V reads are done
+#pragma unroll
+      for (int i = 0; i < VLD; ++i) {
+        const int ch = lane + 64 * i;
+        *(u32x4*)(vw + (ch / (D / 8)) * VPITCH + (ch % (D / 8)) * 8) = ka[i];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       f32x4 sacc[2];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
@@ -334,7 +347,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
         for (int s = 0; s < NS; ++s)
           sacc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, ka[blk][s]), qb[s], sacc[blk], 0, 0, 0);
+              *(const bf16x8*)(vw + (blk * 16 + col) * VPITCH + s * 32 + h4 * 8), qb[s],
+              sacc[blk], 0, 0, 0);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -361,7 +375,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
 
-      // V rows -> wave-private LDS (row-major), then the key-contiguous operand
+      // V rows -> the same slab (the K reads are done), then the
+      // key-contiguous operand
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
