@@ -182,6 +182,37 @@ def test_prefill_chunk_ragged(dtype, heads):
         assert np.array_equal(kc_got[b, s0 + n:], kc[b, s0 + n:])
 
 
+def test_prefill_chunk_fp16_range_gives_nan_rows():
+    """The chunk path has the fp16 score-operand range of gqa_prefill: a
+    cached rotated K element of magnitude 2^14 or more turns the rows of its
+    group that see it into NaN, a query element past the range its own row;
+    every other row matches the oracle."""
+    B, cap, h_q, h_kv, d = 1, 300, 28, 4, 128
+    dtype = torch.bfloat16
+    start, length, C = np.array([200]), np.array([100]), 100
+    q, k, v = inputs(B, cap, h_q, h_kv, d, dtype, 39)
+    kc, vc = prefilled_cache(k, v, start, cap, dtype)
+    kc[0, 150, 1, :] = 40000.0          # cached (rotated) key of group 1, position 150
+    qc, kn, vn = q[:, 200:300].copy(), k[:, 200:300].copy(), v[:, 200:300].copy()
+    qc[0, 10, 5, :] = 200000.0          # position 210, head 5 (group 0)
+    out = torch.full((B, C, h_q, d), 5.0, device="cuda")
+    gqa.prefill_chunk(dev(qc, dtype), dev(kn, dtype), dev(vn, dtype), dev(kc, dtype),
+                      dev(vc, dtype), torch.tensor(start), torch.tensor(length), kend=cap,
+                      out=out)
+    torch.cuda.synchronize()
+    got = host(out)[0]
+    g = h_q // h_kv
+    assert np.all(np.isnan(got[:, g:2 * g])), "group 1 rows see the large key"
+    assert np.all(np.isnan(got[10, 5])), "the large query row"
+    kc_want, vc_want = oracle.cache_append(kc, vc, kn, vn, start, length)
+    want = oracle.prefill_chunk(qc, kc_want, vc_want, start, length)[0]
+    keep = np.ones((C, h_q), bool)
+    keep[:, g:2 * g] = False
+    keep[10, 5] = False
+    assert np.all(np.isfinite(got[keep]))
+    assert_parity(got[keep], want[keep], dtype, "chunk rows outside the large entries")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_chunks_equal_one_shot_prefill(dtype):
     """Three chunks through the cache give the rows and the cache of one
