@@ -221,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       loff[n] = sub * D * TV + vr * TV + ((vslot ^ ((vr / VRPB) % VCPR)) * 8);
     }
   }
-  auto load_tile = [&](uint16_t* ring, int tile) {
+  auto load_tile = [&](uint16_t* ring, int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < LPG; ++n)
       __builtin_amdgcn_global_load_lds(
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   f16x8 qb[NS];
   float qcap;      // bound on |q'| in score units, with a margin for rounding
   bool qbad;       // this row's Q' is outside the fp16 operand range
-  auto rotate_q = [&] {
+  auto rotate_q = [&]() __attribute__((always_inline)) {
     float amax = 0.f, ss = 0.f;
     auto put = [&](int s, int e, float y) {
       const _Float16 h = (_Float16)y;
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         __builtin_bit_cast(f16x8, a), qb[s], s == 0 ? zero16 : sacc[c], 0, 0, 0);
   };
   // P.V of tile i-1 and S^T of tile i (P = i mod 2)
-  auto matrix_full = [&](auto P) {
+  auto matrix_full = [&](auto P) __attribute__((always_inline)) {
     const uint16_t* vt0 = vslot(Slot<decltype(P)::value + 1>{});
     const uint16_t* kt0 = kslot(P);
     bf16x8 fr[NR];
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);   // the MFMAs stay in this phase
   };
   // S^T of tile 0 only
-  auto matrix_qk = [&] {
+  auto matrix_qk = [&]() __attribute__((always_inline)) {
     const uint16_t* kt0 = ks0;
     bf16x8 fr[NQK];
 #pragma unroll
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     for (int j = 0; j < NQK; ++j) mma_qk(fr[j], j);
   };
   // P.V of the last tile only (tile i - 1, slot (i - 1) mod 2)
-  auto matrix_pv = [&](int i) {
+  auto matrix_pv = [&](int i) __attribute__((always_inline)) {
     const uint16_t* vt0 = (i - 1) % 2 == 0 ? vs0 : vs1;
     bf16x8 fr[NPV];
 #pragma unroll
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   };
 
   // ---- vector phase i: probabilities of tile i into pb, row sums into l
-  auto rescale = [&](float m_new) {
+  auto rescale = [&](float m_new) __attribute__((always_inline)) {
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
   };
   // SH: the reference m of some row in the wave is not 0
-  auto probs = [&](const f32x16& s0, const f32x16& s1, auto SH) {
+  auto probs = [&](const f32x16& s0, const f32x16& s1, auto SH) __attribute__((always_inline)) {
     float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   };
   float crow = 0.f;   // bound on this row's scores, score units (set after the prologue)
   float m_raise = 0.f;  // raise of m owed by the previous tile's large sum (applied lazily)
-  auto vector_phase = [&](int i) {
+  auto vector_phase = [&](int i) __attribute__((always_inline)) {
     if (!active(i)) {   // keys beyond this wave's rows: contribute nothing
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -525,45 +525,42 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // has landed at the barrier that ends its period (past the last tile,
   // waves 4-7 load the last K again, into the slot nobody reads any more).
   // The loop runs i = 1 .. n-1 unrolled by two, so every slot is static.
-  auto step0 = [&](auto P, int i) {        // waves 0-3, P = i mod 2
-    matrix_full(P);                        // period 2i
-    bar();
-    load_tile(vslot(P), i);                // period 2i+1
-    vector_phase(i);
-    bar();
-  };
-  auto step1 = [&](auto P, int i) {        // waves 4-7
-    load_tile(kslot(Slot<decltype(P)::value + 1>{}), min(i + 1, n - 1));   // period 2i
+  auto step = [&](auto P, int i) __attribute__((always_inline)) {         // P = i mod 2
+    // period 2i-1 (waves 0-3) or 2i (waves 4-7): slot (i-1) mod 2 takes V(i-1)
+    // or K(i+1), read by the other group's matrix phase of the next period
+    constexpr int Q = decltype(P)::value + 1;
+    load_tile(grp ? kslot(Slot<Q>{}) : vslot(Slot<Q>{}), grp ? min(i + 1, n - 1) : i - 1);
     vector_phase(i - 1);
     bar();
-    matrix_full(P);                        // period 2i+1
+    matrix_full(P);                        // period 2i (waves 0-3) or 2i+1
     bar();
   };
-  auto run = [&](auto step) {
+  if (grp == 0) {
+    matrix_qk();                            // period 0
+    bar();
+  } else {
+    load_tile(ks1, min(1, n - 1));          // period 0
+    bar();
+    matrix_qk();                            // period 1
+    bar();
+  }
+  {
     int i = 1;
     for (; i + 1 < n; i += 2) {
       step(Slot<1>{}, i);
       step(Slot<0>{}, i + 1);
     }
     if (i < n) step(Slot<1>{}, i);
-  };
+  }
   if (grp == 0) {
-    matrix_qk();                            // period 0
+    load_tile(n % 2 == 1 ? vs0 : vs1, n - 1);   // period 2n-1
+    vector_phase(n - 1);
     bar();
-    load_tile(vs0, 0);                      // period 1
-    vector_phase(0);
-    bar();
-    run(step0);
     matrix_pv(n);                           // period 2n
     bar();
     // period 2n+1: this group's O is final; it is written below while
     // waves 4-7 run the last P.V (no barrier: nothing writes LDS any more)
   } else {
-    load_tile(ks1, min(1, n - 1));          // period 0
-    bar();
-    matrix_qk();                            // period 1
-    bar();
-    run(step1);
     vector_phase(n - 1);                    // period 2n
     bar();
     matrix_pv(n);                           // period 2n+1
