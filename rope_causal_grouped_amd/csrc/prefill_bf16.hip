@@ -214,18 +214,26 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int P = (wg4 * LPG + n) * 64 + lane;
     if (grp) {
       const int kr = P / KCPR, kslot = P % KCPR;
-      loff[n] = kr * D + ((kslot ^ ((kr / KRPB) % KCPR)) * 8);
+      loff[n] = (kr * D + ((kslot ^ ((kr / KRPB) % KCPR)) * 8)) * 2;   // bytes
     } else {
       const int sub = P / (D * VCPR), rem = P % (D * VCPR);
       const int vr = rem / VCPR, vslot = rem % VCPR;
-      loff[n] = sub * D * TV + vr * TV + ((vslot ^ ((vr / VRPB) % VCPR)) * 8);
+      loff[n] = (sub * D * TV + vr * TV + ((vslot ^ ((vr / VRPB) % VCPR)) * 8)) * 2;
     }
   }
+  // the lane's byte offset as a 32-bit value at the load, so that the load
+  // takes the uniform tile base in scalar registers (no 64-bit vector add)
+  auto lane_off = [](int v) __attribute__((always_inline)) {
+    uint32_t u = (uint32_t)v;
+    asm volatile("" : "+v"(u));
+    return u;
+  };
   auto load_tile = [&](uint16_t* ring, int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < LPG; ++n)
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(src + (int64_t)tile * TK * D + loff[n]),
+          (const void __attribute__((address_space(1)))*)((const char*)(src + (int64_t)tile * TK * D) +
+                                                          lane_off(loff[n])),
           (void __attribute__((address_space(3)))*)&ring[(wg4 * LPG + n) * 64 * 8], 16, 0, 0);
   };
   auto kslot = [&](auto P) -> uint16_t* {
@@ -434,6 +442,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   };
   float crow = 0.f;   // bound on this row's scores, score units (set after the prologue)
   float m_raise = 0.f;  // raise of m owed by the previous tile's large sum (applied lazily)
+  // fast: every row of the wave has m = 0 within reach of its bound and no
+  // raise owed, so a tile needs neither its max nor a rescale; wave-uniform,
+  // recomputed only when a tile leaves that state
+  bool fast = false;
   auto vector_phase = [&](int i) __attribute__((always_inline)) {
     if (!active(i)) {   // keys beyond this wave's rows: contribute nothing
 #pragma unroll
@@ -461,17 +473,18 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     }
     // new reference: the owed raise (O and l already hold the tile that
     // caused it), or the tile max while the bound is not yet usable
+    const bool was_fast = fast;
     float m_new = m_run + m_raise;
-    if (__builtin_amdgcn_ballot_w64(crow > m_run + kBoundHeadroom)) {   // max first
+    if (!was_fast && __builtin_amdgcn_ballot_w64(crow > m_run + kBoundHeadroom)) {   // max first
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
       mx = max_xor32(mx);
       if (mx > m_new + kRescaleThreshold) m_new = mx;
     }
-    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) rescale(m_new);
+    if (!was_fast && __builtin_amdgcn_ballot_w64(m_new != m_run)) rescale(m_new);
     float psum;
-    if (__builtin_amdgcn_ballot_w64(m_run != 0.f))
+    if (!was_fast && __builtin_amdgcn_ballot_w64(m_run != 0.f))
       psum = probs(s0, s1, std::true_type{});
     else
       psum = probs(s0, s1, std::false_type{});
@@ -479,8 +492,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     // probabilities here are <= 2^64; a sum past 2^32 owes a raise of m by
     // its (integral) log2, taken at the next tile once P.V has added it
     m_raise = 0.f;
-    if (__builtin_amdgcn_ballot_w64(psum > kSumCap))
+    if (__builtin_amdgcn_ballot_w64(psum > kSumCap)) {
       m_raise = ceilf(__builtin_amdgcn_logf(fmaxf(max_xor32(psum), 1.0f)));
+      fast = false;
+    } else if (!was_fast) {
+      fast = __builtin_amdgcn_ballot_w64(m_run != 0.f || crow > m_run + kBoundHeadroom) == 0;
+    }
   };
 
   // ---- prologue part 2: largest K norm this workgroup will see (per-tile
@@ -516,6 +533,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // a bound within the headroom makes 0 a valid reference from the start
   // (every score lies in [-crow, crow]), which the scores need no shift for
   if (crow <= kBoundHeadroom) m_run = 0.f;
+  fast = __builtin_amdgcn_ballot_w64(crow > kBoundHeadroom) == 0;
 
   // ---- periods t = 0 .. 2 n_tiles + 1, each but the last ending at a
   // barrier.  Even period 2i: waves 0-3 run matrix phase i (V(i-1), K(i)),
