@@ -584,38 +584,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     matrix_pv(n);                           // period 2n+1
   }
 
-  // ---- epilogue: O = O / l; lane holds dims db*32 + gq*8 + hl*4 + (0..3)
+  // ---- epilogue: O = O / l; lane holds dims db*32 + gq*8 + hl*4 + (0..3).
+  // O goes out in whole 128-byte pieces of rows with non-temporal stores (so
+  // it does not linger in the caches as dirty lines for the next kernel to
+  // write back): the wave's 32 rows are turned row-major, 128 bytes of each
+  // row at a time (32 dims in fp32, 64 in bf16), through a quarter of a
+  // tile slot that nothing reads any more (K slot 0 for waves 0-3; for waves
+  // 4-7 the V slot their last P.V does not read), RP rows per pass, with the
+  // 16-byte chunks of a row XOR-swizzled by the row.
   const float inv = 1.0f / sum_xor32(l_run);
-  if constexpr (OUT_BF16) {
-    if (row_valid) {
-      const int64_t orow = ((int64_t)((int64_t)b * L + pl) * h_q + head) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int dim = db * 32 + gq * 8 + hl * 4;
-          u32x2 w;
-          w[0] = (uint32_t)f32_to_bf16_bits(oacc[db][gq * 4 + 0] * inv) |
-                 ((uint32_t)f32_to_bf16_bits(oacc[db][gq * 4 + 1] * inv) << 16);
-          w[1] = (uint32_t)f32_to_bf16_bits(oacc[db][gq * 4 + 2] * inv) |
-                 ((uint32_t)f32_to_bf16_bits(oacc[db][gq * 4 + 3] * inv) << 16);
-          *(u32x2*)((uint16_t*)o + orow + dim) = w;
-        }
-    }
-  } else {
-    // fp32 O goes out in whole 128-byte pieces of rows with non-temporal
-    // stores (so it does not linger in the caches as dirty lines for the
-    // next kernel to write back): each 32-dim block of the wave's 32 rows is
-    // turned row-major through a quarter of a tile slot that nothing reads
-    // any more (K slot 0 for waves 0-3; for waves 4-7 the V slot their last
-    // P.V does not read), RP rows at a time, 16-byte chunks XOR-swizzled by
-    // the row
+  {
     constexpr int SB = TK * D / 2;          // bytes per wave: a quarter of a slot
     constexpr int RP = SB / 128;            // rows per pass (32 for d = 128, 16 for d = 64)
     constexpr int NPASS = RW / RP;
     constexpr int TPL = RP / 8;             // chunks per lane per pass
-    float* stage = (float*)((grp == 0 ? (char*)ks0 : (char*)(n % 2 == 0 ? vs0 : vs1)) +
-                            (wave & 3) * SB);
+    constexpr int DPB = OUT_BF16 ? 64 : 32; // dims per 128-byte piece
+    constexpr int EB = OUT_BF16 ? 2 : 4;    // bytes per element
+    char* stage = (grp == 0 ? (char*)ks0 : (char*)(n % 2 == 0 ? vs0 : vs1)) + (wave & 3) * SB;
     int64_t orow_t[NPASS][TPL];
     bool ok_t[NPASS][TPL];
 #pragma unroll
@@ -628,16 +613,30 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         orow_t[ps][t] = ((int64_t)((int64_t)b * L + rr / g) * h_q + u * g + rr % g) * D;
       }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int pc = 0; pc < D / DPB; ++pc)
 #pragma unroll
       for (int ps = 0; ps < NPASS; ++ps) {
         if (c32 / RP == ps) {
+          char* srow = stage + (c32 % RP) * 128;
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int qc = gq * 2 + hl;
-            *(f32x4*)(stage + (c32 % RP) * 32 + ((qc ^ (c32 & 7)) * 4)) =
-                f32x4{oacc[db][gq * 4 + 0] * inv, oacc[db][gq * 4 + 1] * inv,
-                      oacc[db][gq * 4 + 2] * inv, oacc[db][gq * 4 + 3] * inv};
+          for (int db2 = 0; db2 < DPB / 32; ++db2) {
+            const int db = pc * (DPB / 32) + db2;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              // bytes (db2*32 + gq*8 + hl*4) * EB of the row's piece
+              const int byte = (db2 * 32 + gq * 8 + hl * 4) * EB;
+              char* dst = srow + (((byte >> 4) ^ (c32 & 7)) << 4) + (byte & 15);
+              const float y0 = oacc[db][gq * 4 + 0] * inv, y1 = oacc[db][gq * 4 + 1] * inv;
+              const float y2 = oacc[db][gq * 4 + 2] * inv, y3 = oacc[db][gq * 4 + 3] * inv;
+              if constexpr (OUT_BF16) {
+                u32x2 w;
+                w[0] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
+                w[1] = (uint32_t)f32_to_bf16_bits(y2) | ((uint32_t)f32_to_bf16_bits(y3) << 16);
+                *(u32x2*)dst = w;
+              } else {
+                *(f32x4*)dst = f32x4{y0, y1, y2, y3};
+              }
+            }
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -646,9 +645,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
         for (int t = 0; t < TPL; ++t) {
           const int r = lane / 8 + 8 * t, c = lane % 8;
-          const f32x4 w = *(const f32x4*)(stage + r * 32 + ((c ^ (r & 7)) * 4));
+          const u32x4 w = *(const u32x4*)(stage + r * 128 + ((c ^ (r & 7)) << 4));
           if (ok_t[ps][t])
-            __builtin_nontemporal_store(w, (f32x4*)((float*)o + orow_t[ps][t] + db * 32 + c * 4));
+            __builtin_nontemporal_store(
+                w, (u32x4*)((char*)o + (orow_t[ps][t] + pc * DPB) * EB + c * 16));
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();   // reads done before the next writes
