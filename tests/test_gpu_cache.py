@@ -145,11 +145,12 @@ def test_decode_invalid_sequence_is_nan():
 
 # ----------------------------------------------------- chunked prefill ---
 
-@pytest.mark.parametrize("dtype,heads", [(torch.bfloat16, (28, 4, 128)),
-                                         (torch.bfloat16, (16, 2, 64)),
-                                         (torch.float32, (14, 2, 64))],
-                         ids=["bf16_28_4", "bf16_d64_g8", "f32_14_2"])
-def test_prefill_chunk_ragged(dtype, heads):
+@pytest.mark.parametrize("dtype,heads,odt", [(torch.bfloat16, (28, 4, 128), torch.float32),
+                                             (torch.bfloat16, (16, 2, 64), torch.float32),
+                                             (torch.bfloat16, (16, 2, 64), torch.bfloat16),
+                                             (torch.float32, (14, 2, 64), torch.float32)],
+                         ids=["bf16_28_4", "bf16_d64_g8", "bf16_d64_g8_bf16out", "f32_14_2"])
+def test_prefill_chunk_ragged(dtype, heads, odt):
     h_q, h_kv, d = heads
     start = np.array([0, 300, 1000, 64])
     length = np.array([200, 1, 137, 0])
@@ -162,7 +163,7 @@ def test_prefill_chunk_ragged(dtype, heads):
         s0, n = int(start[b]), int(length[b])
         qc[b, :n], kn[b, :n], vn[b, :n] = q[b, s0:s0 + n], k[b, s0:s0 + n], v[b, s0:s0 + n]
     kcd, vcd = dev(kc, dtype), dev(vc, dtype)
-    out = torch.full((B, C, h_q, d), 5.0, device="cuda")
+    out = torch.full((B, C, h_q, d), 5.0, device="cuda", dtype=odt)
     gqa.prefill_chunk(dev(qc, dtype), dev(kn, dtype), dev(vn, dtype), kcd, vcd,
                       torch.tensor(start), torch.tensor(length), kend=1200, out=out)
     torch.cuda.synchronize()

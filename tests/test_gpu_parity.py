@@ -158,8 +158,14 @@ def test_prefill_bf16_fp16_range_gives_nan_rows():
     assert_parity(got, want[0][keep], torch.bfloat16, "rows outside the large entries")
 
 
-def test_prefill_bf16_noncausal_and_bf16_out():
-    B, L, h_q, h_kv, d = 2, 200, 14, 2, 128
+@pytest.mark.parametrize("shape", [(2, 200, 14, 2, 128), (2, 203, 16, 2, 64)],
+                         ids=lambda s: "B%d_L%d_%d/%d_d%d" % s)
+def test_prefill_bf16_noncausal_and_bf16_out(shape):
+    """Full attention, and bf16 output; O leaves the kernel in 128-byte row
+    pieces staged through LDS (32 fp32 or 64 bf16 dims; at d = 64 in two
+    passes of 16 rows), with a ragged last row block (203 * 8 rows)."""
+    B, L, h_q, h_kv, d = shape
+    note(f"prefill bf16 non-causal / bf16 out {shape}")
     q, k, v = small_case(B, L, h_q, h_kv, d, torch.bfloat16, 7)
     qd, kd, vd = (dev(x, torch.bfloat16) for x in (q, k, v))
     o = gqa.prefill(qd, kd, vd, causal=False)
