@@ -37,8 +37,10 @@
 // Waves 0-3 and waves 4-7 (one of each on every SIMD) run the two phases in
 // opposite order and every phase ends at a workgroup barrier, so on each
 // SIMD one wave's matrix-core work always runs against the other wave's
-// softmax.  A matrix phase reads 32 operand fragments from LDS; they are
-// issued a few MFMAs ahead of their use so that LDS latency stays hidden.
+// softmax.  Both groups run one loop body (softmax of tile i-1, barrier,
+// matrix phase i, barrier), one period apart.  A matrix phase reads 32
+// operand fragments from LDS; they are issued a few MFMAs ahead of their use
+// so that LDS latency stays hidden.
 // The wave group in its vector phase also streams the next tile from HBM
 // straight into LDS (global_load_lds_dwordx4, no staging registers): K by
 // waves 4-7, V by waves 0-3, each into a two-slot ring.
@@ -56,7 +58,14 @@
 // Otherwise the tile max is taken first, until m is within reach of the
 // bound, and m follows it lazily (raised when the max grows by more than
 // 8); m then never exceeds the true running max by more than log2(64), so
-// the largest probability cannot underflow.
+// the largest probability cannot underflow.  While every row of a wave has
+// m = 0 within its bound and owes no raise, a wave-uniform flag skips the
+// per-tile checks altogether.
+//
+// Output.  O = O / l leaves in whole 128-byte pieces of rows with
+// non-temporal stores: each wave turns its rows row-major through LDS the
+// loop no longer reads, so O does not sit in the caches as partly written
+// dirty lines that the next kernels would have to write back.
 
 #include <type_traits>
 
