@@ -226,7 +226,14 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(
 // key-contiguous operand.  Heads beyond 16 per group run as extra head
 // blocks (another pass over the chunk).  The cache is read once, so its
 // loads are non-temporal (they do not displace reused lines in the caches).
-template <int D, bool PAGED>
+// GRP (h_kv a multiple of 4): the workgroup takes one chunk for four KV
+// groups, wave w group 4*ub + w over the whole chunk, so that the
+// workgroup's loads cover whole cache rows (all groups of a key are
+// adjacent in the contiguous cache): 7.0 against 6.6 TB/s for the split's
+// load pattern alone.  Each wave then writes its group's state itself.
+// Otherwise the four waves take a quarter of the chunk of one group each and
+// their states are combined through LDS.
+template <int D, bool PAGED, bool GRP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ pm, float* __restrict__ pl,
@@ -245,24 +252,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   __shared__ int pg[CH];                // page ids of this chunk (paged cache)
 
   const int split = blockIdx.x;
-  const int u = blockIdx.y / n_hb, hb = blockIdx.y % n_hb;
+  const int hb = blockIdx.y % n_hb;
   const int b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int u = GRP ? (blockIdx.y / n_hb) * 4 + wave : blockIdx.y / n_hb;
   const int col = lane & 15, h4 = lane >> 4;
   const int c = hb * 16 + col;
   const int nh = min(16, g - hb * 16);
   const SeqLen sq = seq_len(b, kv_len_max, q_pos_s, kvl_arr, qpos_arr, kvl_from_pos);
   const int kv_len = sq.kv_len;
   const int chunk0 = split * CH;
-  const int64_t out0 = (((int64_t)b * h_kv + u) * n_split + split) * g + hb * 16;
+  auto state0 = [&](int uu) { return (((int64_t)b * h_kv + uu) * n_split + split) * g + hb * 16; };
+  const int64_t out0 = state0(u);
+  // an empty or unreadable chunk: the state of every group of the workgroup
+  auto flat_states = [&](float mval) {
+    if constexpr (GRP) {
+      for (int w = 0; w < 4; ++w)
+        write_flat_state(pm, pl, po, state0((blockIdx.y / n_hb) * 4 + w), nh, D, mval);
+    } else {
+      write_flat_state(pm, pl, po, out0, nh, D, mval);
+    }
+  };
 
   if (chunk0 >= kv_len) {   // chunk past this sequence's keys: empty state
-    write_flat_state(pm, pl, po, out0, nh, D, -INFINITY);
+    flat_states(-INFINITY);
   } else if (PAGED && !stage_pages(kr, b, chunk0, min(chunk0 + CH, kv_len), pg)) {
-    write_flat_state(pm, pl, po, out0, nh, D, __builtin_nanf(""));
+    flat_states(__builtin_nanf(""));
   } else {
-    const int kw0 = chunk0 + wave * WK;
-    const int kw1 = min(kw0 + WK, kv_len);
+    const int kw0 = GRP ? chunk0 : chunk0 + wave * WK;
+    const int kw1 = min(kw0 + (GRP ? CH : WK), kv_len);
     // one 32-key step's K and V rows, 16 bytes per load, non-temporal; D/8
     // lanes read one whole row, so a load covers a few complete rows (the
     // rows of a group lie at a stride of h_kv rows in the contiguous cache)
@@ -407,9 +426,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       compute_step(k0 + 32, kaB, vaB);
     }
 
-    // ---- combine the four waves of the workgroup
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
+    if constexpr (GRP) {   // this wave's group state (m is the same in the four h4 lanes)
+      if (col < nh) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          *(f32x4*)(po + (out0 + col) * D + db * 16 + h4 * 4) = oacc[db];
+        if (h4 == 0) {
+          pm[out0 + col] = m;
+          pl[out0 + col] = l;
+        }
+      }
+      return;
+    }
+    // ---- combine the four waves of the workgroup
     if (h4 == 0) {
       cm[wave][col] = m;
       cl[wave][col] = l;
@@ -606,28 +637,36 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t
     q = w.qr;
     q_rotated = 1;
   }
-  // 1) split-K streaming
-  dim3 grid((unsigned)n_split, (unsigned)(a.h_kv * n_hb), (unsigned)a.B);
+  // 1) split-K streaming (bf16 with h_kv a multiple of 4: a workgroup per
+  // four groups of a chunk)
+  const bool grp4 = a.in_bf16 && a.h_kv % 4 == 0;
+  dim3 grid((unsigned)n_split, (unsigned)((grp4 ? a.h_kv / 4 : a.h_kv) * n_hb), (unsigned)a.B);
   const float sl2 = a.scale * 1.4426950408889634f;
   if (ev_begin) (void)hipEventRecord(ev_begin, st);
-#define GQA_SPLIT(KERNEL, T, DD, PG, SC)                                                      \
-  KERNEL<DD, PG><<<grid, 256, 0, st>>>((const T*)q, (const T*)a.kc, (const T*)a.vc, w.m, w.l, \
-                                       w.o, a.h_q, a.h_kv, g, n_hb, (int)a.kv_len,           \
-                                       (double)a.q_pos, a.rp, SC, n_split, a.kvl_arr,         \
-                                       a.qpos_arr, a.kvl_from_pos, q_rotated, kr)
-#define GQA_SPLIT_PG(KERNEL, T, DD, SC)                   \
-  do {                                                    \
-    if (a.bt) GQA_SPLIT(KERNEL, T, DD, true, SC);         \
-    else GQA_SPLIT(KERNEL, T, DD, false, SC);             \
+#define GQA_SPLIT(KERNEL, T, TPL, SC)                                                        \
+  KERNEL<TPL><<<grid, 256, 0, st>>>((const T*)q, (const T*)a.kc, (const T*)a.vc, w.m, w.l,   \
+                                    w.o, a.h_q, a.h_kv, g, n_hb, (int)a.kv_len,              \
+                                    (double)a.q_pos, a.rp, SC, n_split, a.kvl_arr,            \
+                                    a.qpos_arr, a.kvl_from_pos, q_rotated, kr)
+#define GQA_BF16(DD, PG)                                                             \
+  do {                                                                               \
+    if (grp4) GQA_SPLIT(decode_split_bf16_kernel, uint16_t, GQA_TPL3(DD, PG, true), sl2); \
+    else GQA_SPLIT(decode_split_bf16_kernel, uint16_t, GQA_TPL3(DD, PG, false), sl2);     \
   } while (0)
+#define GQA_TPL3(DD, PG, GR) DD, PG, GR
+#define GQA_F32(DD, PG) GQA_SPLIT(decode_split_f32_kernel, float, GQA_TPL2(DD, PG), a.scale)
+#define GQA_TPL2(DD, PG) DD, PG
   if (a.in_bf16) {
-    if (a.d == 128) GQA_SPLIT_PG(decode_split_bf16_kernel, uint16_t, 128, sl2);
-    else GQA_SPLIT_PG(decode_split_bf16_kernel, uint16_t, 64, sl2);
+    if (a.d == 128) { if (a.bt) GQA_BF16(128, true); else GQA_BF16(128, false); }
+    else { if (a.bt) GQA_BF16(64, true); else GQA_BF16(64, false); }
   } else {
-    if (a.d == 128) GQA_SPLIT_PG(decode_split_f32_kernel, float, 128, a.scale);
-    else GQA_SPLIT_PG(decode_split_f32_kernel, float, 64, a.scale);
+    if (a.d == 128) { if (a.bt) GQA_F32(128, true); else GQA_F32(128, false); }
+    else { if (a.bt) GQA_F32(64, true); else GQA_F32(64, false); }
   }
-#undef GQA_SPLIT_PG
+#undef GQA_TPL2
+#undef GQA_F32
+#undef GQA_TPL3
+#undef GQA_BF16
 #undef GQA_SPLIT
   err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, st);
