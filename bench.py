@@ -56,14 +56,14 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
 # device copy: FETCH x 2.00, WRITE x 1.00).  Each figure is valid only for the
 # kernel source it was measured on (sha256 prefix); otherwise it reports null.
 TRAFFIC = {
-    "prefill": ("prefill_bf16.hip", "c2201e53d59a187f", (102253.6 * 2.0 + 229377.4) * 1024),
-    "prefill_c4": ("prefill_bf16.hip", "c2201e53d59a187f", (299294.8 * 2.0 + 524313.7) * 1024),
-    "prefill_c5": ("prefill_bf16.hip", "c2201e53d59a187f", (677530.8 * 2.0 + 458752.0) * 1024),
-    "decode": ("decode.hip", "5d4aa32bfc09f139", (1049761.5 * 2.0 + 7392.2) * 1024),
-    "prefill_chunk": ("prefill_bf16.hip", "c2201e53d59a187f", (41376.5 * 2.0 + 57344.0) * 1024),
-    "decode_append": ("decode.hip", "5d4aa32bfc09f139", (922610.1 * 2.0 + 7392.1) * 1024),
-    "decode_paged": ("decode.hip", "5d4aa32bfc09f139", (1049885.5 * 2.0 + 7392.2) * 1024),
-    "qkv_epilogue": ("rope.hip", "3a77080a2e9aa0cd", (73829.1 * 2.0 + 147465.5) * 1024),
+    "prefill": ("prefill_bf16.hip", "c2201e53d59a187f", (102271.0 * 2.0 + 229376.0) * 1024),
+    "prefill_c4": ("prefill_bf16.hip", "c2201e53d59a187f", (299274.9 * 2.0 + 524322.9) * 1024),
+    "prefill_c5": ("prefill_bf16.hip", "c2201e53d59a187f", (677259.7 * 2.0 + 458752.0) * 1024),
+    "decode": ("decode.hip", "59d72d113061ace5", (1049752.1 * 2.0 + 7392.0) * 1024),
+    "prefill_chunk": ("prefill_bf16.hip", "c2201e53d59a187f", (41487.0 * 2.0 + 57344.0) * 1024),
+    "decode_append": ("decode.hip", "59d72d113061ace5", (922586.2 * 2.0 + 7392.1) * 1024),
+    "decode_paged": ("decode.hip", "59d72d113061ace5", (1049877.6 * 2.0 + 7392.1) * 1024),
+    "qkv_epilogue": ("rope.hip", "3a77080a2e9aa0cd", (73829.2 * 2.0 + 147459.5) * 1024),
 }
 
 

@@ -59,9 +59,9 @@ def test_traffic_figures_match_the_profile_summary():
         "prefill_c4": (pk, "`gqa_prefill`, 72B B2 L8192"),
         "prefill_c5": (pk, "`gqa_prefill`, 7B B1 L32768"),
         "prefill_chunk": (pk, "`gqa_prefill_chunk`, rows 3072..4095"),
-        "decode": ("decode_split_bf16_kernel<128, false>", "`gqa_decode`, 7B B32 x 32768"),
-        "decode_append": ("decode_split_bf16_kernel<128, false>", "`gqa_decode_append`"),
-        "decode_paged": ("decode_split_bf16_kernel<128, true>", "`gqa_decode_paged`"),
+        "decode": ("decode_split_bf16_kernel<128, false, true>", "`gqa_decode`, 7B B32 x 32768"),
+        "decode_append": ("decode_split_bf16_kernel<128, false, true>", "`gqa_decode_append`"),
+        "decode_paged": ("decode_split_bf16_kernel<128, true, true>", "`gqa_decode_paged`"),
         "qkv_epilogue": ("qkv_epilogue_kernel<unsigned short>",
                          "`gqa_qkv_epilogue`, 7B B4 L4096 projections"),
     }
