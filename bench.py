@@ -59,10 +59,10 @@ TRAFFIC = {
     "prefill": ("prefill_bf16.hip", "c2201e53d59a187f", (102271.0 * 2.0 + 229376.0) * 1024),
     "prefill_c4": ("prefill_bf16.hip", "c2201e53d59a187f", (299274.9 * 2.0 + 524322.9) * 1024),
     "prefill_c5": ("prefill_bf16.hip", "c2201e53d59a187f", (677259.7 * 2.0 + 458752.0) * 1024),
-    "decode": ("decode.hip", "59d72d113061ace5", (1049752.1 * 2.0 + 7392.0) * 1024),
+    "decode": ("decode.hip", "b14634ccd2269562", (1049752.1 * 2.0 + 7392.0) * 1024),
     "prefill_chunk": ("prefill_bf16.hip", "c2201e53d59a187f", (41487.0 * 2.0 + 57344.0) * 1024),
-    "decode_append": ("decode.hip", "59d72d113061ace5", (922586.2 * 2.0 + 7392.1) * 1024),
-    "decode_paged": ("decode.hip", "59d72d113061ace5", (1049877.6 * 2.0 + 7392.1) * 1024),
+    "decode_append": ("decode.hip", "b14634ccd2269562", (922586.2 * 2.0 + 7392.1) * 1024),
+    "decode_paged": ("decode.hip", "b14634ccd2269562", (1049877.6 * 2.0 + 7392.1) * 1024),
     "qkv_epilogue": ("rope.hip", "3a77080a2e9aa0cd", (73829.2 * 2.0 + 147459.5) * 1024),
 }
 

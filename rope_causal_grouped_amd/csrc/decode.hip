@@ -218,14 +218,14 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(
 }
 
 
-// bf16 cache, matrix cores.  Workgroup = (chunk, group u x head block, b);
-// four waves take a quarter of the chunk each.  Per 32-key step a wave
-// computes S^T = K q^T (v_mfma_f32_16x16x32_bf16: 16 keys x 16 heads, K
-// rows straight from HBM into the A operand), then O^T += V^T P^T with V
-// staged through a wave-private LDS slab to turn key-major rows into the
-// key-contiguous operand.  Heads beyond 16 per group run as extra head
-// blocks (another pass over the chunk).  The cache is read once, so its
-// loads are non-temporal (they do not displace reused lines in the caches).
+// bf16 cache, matrix cores.  Workgroup = (chunk, group(s) x head block, b).
+// Per 32-key step a wave loads the K and V rows of its keys whole (D/8
+// lanes to a row, into registers one step ahead) and passes them through a
+// wave-private LDS slab in turn: K to form the A operands of S^T = K q^T
+// (v_mfma_f32_16x16x32_bf16: 16 keys x 16 heads), V to read it back
+// key-contiguous for O^T += V^T P^T.  Heads beyond 16 per group run as extra head blocks
+// (another pass over the chunk).  The cache is read once, so its loads are
+// non-temporal (they do not displace reused lines in the caches).
 // GRP (h_kv a multiple of 4): the workgroup takes one chunk for four KV
 // groups, wave w group 4*ub + w over the whole chunk, so that the
 // workgroup's loads cover whole cache rows (all groups of a key are
