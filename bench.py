@@ -19,11 +19,13 @@ on the other prefill workloads (72B heads at L 8192; 7B heads at L 32768;
 the small fp32 0.5B case as a latency) under "other_prefill", and the HBM
 context figures under "context".
 `value` is the prefill rate in TFLOP/s over the causal pairs only
-(4 * B * h_q * d * L(L+1)/2 flop per call) measured around the whole call;
-the decode rate (K/V cache bytes read once per KV group / call time) is
-reported beside it.  Kernel durations for the roofline objects come from HIP
-events that the library records on the launch stream around its attention
-and split-K kernels.  Before the W warm-up steps the step runs for a fixed
+(4 * B * h_q * d * L(L+1)/2 flop per call) over the whole call, from the
+start of its first kernel to the end of its last; the decode rate (K/V
+cache bytes read once per KV group / call time) is reported beside it.
+Call and kernel durations (the latter for the roofline objects) come from
+HIP events that the library binds to its own kernel dispatches on the
+launch stream (hipExtLaunchKernel), so no marker packet sits between the
+kernels of a step; `ms_per_step` is the whole timed loop over K.  Before the W warm-up steps the step runs for a fixed
 stretch of time (--clock-warmup-s), so that the timed steps see the
 sustained shader clock rather than the ramp from idle, whatever W is.
 After timing, the outputs of the timed calls are compared with the fp64
@@ -56,14 +58,14 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
 # device copy: FETCH x 2.00, WRITE x 1.00).  Each figure is valid only for the
 # kernel source it was measured on (sha256 prefix); otherwise it reports null.
 TRAFFIC = {
-    "prefill": ("prefill_bf16.hip", "c2201e53d59a187f", (102271.0 * 2.0 + 229376.0) * 1024),
-    "prefill_c4": ("prefill_bf16.hip", "c2201e53d59a187f", (299274.9 * 2.0 + 524322.9) * 1024),
-    "prefill_c5": ("prefill_bf16.hip", "c2201e53d59a187f", (677259.7 * 2.0 + 458752.0) * 1024),
-    "decode": ("decode.hip", "b14634ccd2269562", (1049752.1 * 2.0 + 7392.0) * 1024),
-    "prefill_chunk": ("prefill_bf16.hip", "c2201e53d59a187f", (41487.0 * 2.0 + 57344.0) * 1024),
-    "decode_append": ("decode.hip", "b14634ccd2269562", (922586.2 * 2.0 + 7392.1) * 1024),
-    "decode_paged": ("decode.hip", "b14634ccd2269562", (1049877.6 * 2.0 + 7392.1) * 1024),
-    "qkv_epilogue": ("rope.hip", "3a77080a2e9aa0cd", (73829.2 * 2.0 + 147459.5) * 1024),
+    "prefill": ("prefill_bf16.hip", "1c498196ad4dce9f", (102271.0 * 2.0 + 229376.0) * 1024),
+    "prefill_c4": ("prefill_bf16.hip", "1c498196ad4dce9f", (299274.9 * 2.0 + 524322.9) * 1024),
+    "prefill_c5": ("prefill_bf16.hip", "1c498196ad4dce9f", (677259.7 * 2.0 + 458752.0) * 1024),
+    "decode": ("decode.hip", "5d5c44530499b2f8", (1049752.1 * 2.0 + 7392.0) * 1024),
+    "prefill_chunk": ("prefill_bf16.hip", "1c498196ad4dce9f", (41487.0 * 2.0 + 57344.0) * 1024),
+    "decode_append": ("decode.hip", "5d5c44530499b2f8", (922586.2 * 2.0 + 7392.1) * 1024),
+    "decode_paged": ("decode.hip", "5d5c44530499b2f8", (1049877.6 * 2.0 + 7392.1) * 1024),
+    "qkv_epilogue": ("rope.hip", "1ca3b24e2d614795", (73829.2 * 2.0 + 147459.5) * 1024),
 }
 
 
@@ -163,6 +165,24 @@ def clock_warmup(torch, step, seconds):
     return n
 
 
+def timed_calls(torch, gqa, fam, fn, reps):
+    """Runs fn() reps times back to back with the library's call timing on;
+    returns the mean duration of the calls' main kernel (fam 0: prefill
+    attention, 1: decode split-K) and of the whole calls (first kernel's
+    start to last kernel's end), both in ms from HIP events bound to those
+    kernel dispatches."""
+    gqa.timing_enable(True)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    gqa.timing_enable(False)
+    k_ms, k_n = gqa.timing_read(fam)
+    c_ms, c_n = gqa.timing_read(fam + 2)
+    if k_n != reps or c_n != reps:
+        raise RuntimeError(f"timed {k_n}/{c_n} calls, expected {reps}")
+    return k_ms / reps, c_ms / reps
+
+
 def no_children_left():
     """Child processes still running at exit, for the log; each is ended
     here.  The oracle pool's workers are joined when it closes, and its
@@ -230,18 +250,8 @@ def measure_other_prefills(torch, gqa, dev, keys=("c1", "c4", "c5"), warmup=10, 
         for _ in range(warmup):
             gqa.prefill(qd, kd, vd, out=od, workspace=ws)
         torch.cuda.synchronize()
-        gqa.timing_read(0)
-        gqa.timing_enable(True)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            gqa.prefill(qd, kd, vd, out=od, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        gqa.timing_enable(False)
-        call_ms = e0.elapsed_time(e1) / reps
-        attn_ms, attn_n = gqa.timing_read(0)
-        kern_ms = attn_ms / max(attn_n, 1)
+        kern_ms, call_ms = timed_calls(
+            torch, gqa, 0, lambda: gqa.prefill(qd, kd, vd, out=od, workspace=ws), reps)
         flops = w.prefill_flops()
         ach = flops / (kern_ms * 1e-3) / 1e12
         if w.dtype != "bf16":
@@ -294,18 +304,7 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
     for _ in range(args.warmup):
         chunk()
     torch.cuda.synchronize()
-    gqa.timing_read(0)
-    gqa.timing_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(K):
-        chunk()
-    e1.record()
-    torch.cuda.synchronize()
-    gqa.timing_enable(False)
-    call_ms = e0.elapsed_time(e1) / K
-    attn_ms, attn_n = gqa.timing_read(0)
-    attn_avg = attn_ms / max(attn_n, 1)
+    attn_avg, call_ms = timed_calls(torch, gqa, 0, chunk, K)
     pos = np.arange(s0, wp.L, dtype=np.float64)
     flops = 4.0 * wp.B * wp.h_q * wp.d * float(np.sum(pos + 1))
     ach = flops / (attn_avg * 1e-3) / 1e12
@@ -347,17 +346,7 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
     for _ in range(args.warmup):
         app()
     torch.cuda.synchronize()
-    gqa.timing_read(1)
-    gqa.timing_enable(True)
-    e0.record()
-    for _ in range(K):
-        app()
-    e1.record()
-    torch.cuda.synchronize()
-    gqa.timing_enable(False)
-    call_ms = e0.elapsed_time(e1) / K
-    split_ms, split_n = gqa.timing_read(1)
-    split_avg = split_ms / max(split_n, 1)
+    split_avg, call_ms = timed_calls(torch, gqa, 1, app, K)
     kvb = float(np.sum(pos + 1)) * wd.h_kv * wd.d * 2 * 2
     dach = kvb / (split_avg * 1e-3) / 1e9
     res["decode_append"] = {
@@ -395,17 +384,7 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
     for _ in range(args.warmup):
         paged()
     torch.cuda.synchronize()
-    gqa.timing_read(1)
-    gqa.timing_enable(True)
-    e0.record()
-    for _ in range(K):
-        paged()
-    e1.record()
-    torch.cuda.synchronize()
-    gqa.timing_enable(False)
-    call_ms = e0.elapsed_time(e1) / K
-    split_ms, split_n = gqa.timing_read(1)
-    split_avg = split_ms / max(split_n, 1)
+    split_avg, call_ms = timed_calls(torch, gqa, 1, paged, K)
     kvb = wd.decode_kv_bytes()
     dach = kvb / (split_avg * 1e-3) / 1e9
     res["decode_paged"] = {
@@ -435,6 +414,7 @@ def measure_next(args, torch, gqa, dev, wp, wd, pre=None, dec=None):
     for _ in range(args.warmup):
         epi()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(K):
         epi()
@@ -508,28 +488,23 @@ def main():
         f"warmup done ({args.warmup} steps)")
 
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K)]
+    # the calls time themselves (HIP events bound to their kernel dispatches:
+    # no marker packets between the kernels of a step)
     gqa.timing_enable(True)
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record()
     for s in range(K):
-        ev[3 * s].record()
-        if run_p:
-            gqa.prefill(qd, kd, vd, out=od, workspace=wsp)
-        ev[3 * s + 1].record()
-        if run_d:
-            gqa.decode(qh, kc, vc, kv_len=wd.L, q_pos=wd.q_pos, out=odd, workspace=wsd)
-        ev[3 * s + 2].record()
+        step()
     t_end.record()
     torch.cuda.synchronize()
     gqa.timing_enable(False)
     total_ms = t_start.elapsed_time(t_end)
-    pre_ms = sum(ev[3 * s].elapsed_time(ev[3 * s + 1]) for s in range(K)) / K
-    dec_ms = sum(ev[3 * s + 1].elapsed_time(ev[3 * s + 2]) for s in range(K)) / K
     attn_ms, attn_n = gqa.timing_read(0)
     split_ms, split_n = gqa.timing_read(1)
+    pre_ms = gqa.timing_read(2)[0] / K
+    dec_ms = gqa.timing_read(3)[0] / K
     log(f"[bench] timed {K} steps: {total_ms:.2f} ms total")
     # outputs of the last timed calls, for the parity check after all timing
     got_prefill = od.cpu().numpy() if run_p else None

@@ -298,11 +298,20 @@ const char* gqa_version(void);
 
 /*
  * Kernel timing for benchmarks.  While enabled, each gqa_prefill and
- * gqa_prefill_chunk records a HIP event pair around its attention kernel
- * (which = 0) and each decode call (contiguous or paged) around its split-K
- * streaming kernel (which = 1), on the caller's stream.  gqa_timing_read waits for the recorded events, returns
- * the summed milliseconds and the launch count for `which`, and clears
- * them.  Not thread-safe; meant for a single benchmarking thread.
+ * gqa_prefill_chunk call, and each decode call (contiguous or paged) except
+ * gqa_decode_noalloc, binds HIP events to its own kernel dispatches on the
+ * caller's stream (the event takes the dispatch's start or end time; no
+ * marker is enqueued between the kernels): the start of its first kernel,
+ * the end of its last, and the interval of its main kernel (prefill: the
+ * attention kernel; decode: the split-K streaming kernel), which opens at
+ * that kernel's start when it is the call's first kernel and otherwise at
+ * the end of the kernel launched just before it (so it also holds the
+ * launch gap between the two).  gqa_timing_read waits for them and returns
+ * the summed milliseconds and the call count for `which`: 0 prefill main
+ * kernels, 1 decode main kernels, 2 whole prefill calls (first kernel's
+ * start to last kernel's end), 3 whole decode calls.  gqa_timing_enable(1)
+ * drops earlier records.  Not thread-safe; meant for a single benchmarking
+ * thread.
  */
 int gqa_timing_enable(int on);
 int gqa_timing_read(int which, double* total_ms, int64_t* count);

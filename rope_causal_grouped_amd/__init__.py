@@ -352,8 +352,10 @@ def timing_enable(on: bool) -> None:
 
 
 def timing_read(which: int):
-    """(total_ms, count) of the kernels timed since the last read; which = 0
-    for the prefill attention kernel, 1 for the decode streaming kernel."""
+    """(total_ms, count) of the calls timed while timing was last enabled:
+    which = 0 the prefill attention kernel, 1 the decode streaming kernel,
+    2 whole prefill calls, 3 whole decode calls (first kernel's start to
+    last kernel's end; events bound to the kernel dispatches)."""
     ms = ctypes.c_double()
     n = ctypes.c_int64()
     check(lib().gqa_timing_read(which, ctypes.byref(ms), ctypes.byref(n)))

@@ -15,6 +15,15 @@
 #include "gqa.h"
 #include "launch.h"
 
+namespace gqa {
+
+LaunchEvents& next_launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+
+}  // namespace gqa
+
 namespace {
 
 thread_local std::string g_err;
@@ -39,24 +48,86 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool dtype_ok(int dt) { return dt == GQA_F32 || dt == GQA_BF16; }
 
-// ---- benchmark timing: HIP event pairs around the main kernel of a call
+// ---- benchmark timing: HIP events bound to the dispatches of a call (its
+// first kernel's start, its main kernel's start and end, its last kernel's
+// end); see gqa::launch_kernel
 struct Timing {
   bool on = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[2];
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
-  std::pair<hipEvent_t, hipEvent_t> take() {
+  std::vector<gqa::CallEvents> rec[2];   // 0: prefill calls, 1: decode calls
+  std::vector<hipEvent_t> pool;
+  hipEvent_t one() {
     if (!pool.empty()) {
-      auto p = pool.back();
+      hipEvent_t e = pool.back();
       pool.pop_back();
-      return p;
+      return e;
     }
-    std::pair<hipEvent_t, hipEvent_t> p{nullptr, nullptr};
-    if (hipEventCreate(&p.first) != hipSuccess || hipEventCreate(&p.second) != hipSuccess)
-      return {nullptr, nullptr};
-    return p;
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+  }
+  // events of one call; own_start / own_stop: the call's first / last
+  // kernel is not its main kernel
+  bool take(gqa::CallEvents& ev, bool own_start, bool own_stop) {
+    ev.kernel_start = one();
+    ev.kernel_stop = one();
+    ev.call_start = own_start ? one() : ev.kernel_start;
+    ev.call_stop = own_stop ? one() : ev.kernel_stop;
+    if (ev.kernel_start && ev.kernel_stop && ev.call_start && ev.call_stop) return true;
+    release(ev);
+    ev = gqa::CallEvents{};
+    return false;
+  }
+  void release(const gqa::CallEvents& ev) {
+    for (hipEvent_t e : {ev.kernel_start, ev.kernel_stop})
+      if (e) pool.push_back(e);
+    if (ev.call_start && ev.call_start != ev.kernel_start) pool.push_back(ev.call_start);
+    if (ev.call_stop && ev.call_stop != ev.kernel_stop) pool.push_back(ev.call_stop);
+  }
+  void clear() {
+    for (auto& r : rec) {
+      for (auto& ev : r) release(ev);
+      r.clear();
+    }
   }
 };
 Timing g_timing;
+
+// Timing of one API call while timing is on.  The call's first kernel takes
+// call_start as its start event and its last kernel call_stop as its stop
+// event.  The main kernel's interval opens at its own start when it is the
+// call's first kernel, else at the end of the kernel launched just before it
+// (a stop event: a start event bound inside the call would hold the main
+// kernel back by a few microseconds, a stop event does not), so that
+// interval also holds the launch gap between the two.  bind() hands events
+// to the next launch_kernel; done() keeps the record.  A call that returns
+// before done() gives its events back, and no pending binding outlives it.
+class TimedCall {
+ public:
+  TimedCall(int which, bool own_start, bool own_stop, bool allow = true) : which_(which) {
+    if (g_timing.on && allow) on_ = g_timing.take(ev_, own_start, own_stop);
+  }
+  ~TimedCall() {
+    gqa::next_launch_events() = gqa::LaunchEvents{};
+    if (on_ && !kept_) g_timing.release(ev_);
+  }
+  TimedCall(const TimedCall&) = delete;
+  TimedCall& operator=(const TimedCall&) = delete;
+  const gqa::CallEvents* events() const { return on_ ? &ev_ : nullptr; }
+  const gqa::CallEvents& ev() const { return ev_; }
+  void bind(hipEvent_t start, hipEvent_t stop) {
+    if (on_) gqa::next_launch_events() = gqa::LaunchEvents{start, stop};
+  }
+  void done() {
+    if (on_ && !kept_) {
+      g_timing.rec[which_].push_back(ev_);
+      kept_ = true;
+    }
+  }
+
+ private:
+  int which_;
+  bool on_ = false, kept_ = false;
+  gqa::CallEvents ev_;
+};
 
 // YaRN context extension of RoPE (gqa_set_rope_yarn), per thread like the
 // error message; factor 1 is plain RoPE.
@@ -233,13 +304,16 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
   float2* cs = (float2*)(wsb + ws.cs_off);
   const gqa::RopeParams rp = rope_params(theta, d);
   hipError_t e = hipSuccess;
+  // timing: the first kernel (the table, or the bf16 K/V preparation) opens
+  // the call; the kernel before the attention kernel opens the latter's
+  // interval; the attention kernel ends both
+  TimedCall tc(0, true, false);
+  const gqa::CallEvents& te = tc.ev();
   if (in_dtype != GQA_BF16) {   // the bf16 preparation kernel writes the table itself
+    tc.bind(te.call_start, k_cache ? nullptr : te.kernel_start);
     e = gqa::launch_rope_table(cs, L, d, 0, rp, st);
     if (e != hipSuccess) return hip_fail(e, "rope table launch");
   }
-
-  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
-  if (g_timing.on) ev = g_timing.take();
 
   if (in_dtype == GQA_BF16) {
     const int64_t Lpad = prefill_lpad(L);
@@ -247,11 +321,12 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
     float* kmax = (float*)(wsb + ws.kmax_off);
     int* kexp = (int*)(wsb + ws.kexp_off);
+    tc.bind(te.call_start, te.kernel_start);
     e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, &rp, cs, kp, vt,
                                     kmax, kexp, (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad,
                                     h_kv, d, cap, L, nullptr, nullptr, L, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
-    if (ev.first) (void)hipEventRecord(ev.first, st);
+    tc.bind(nullptr, te.kernel_stop);
     e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, kexp, cs, o,
                                  out_dtype == GQA_BF16, B, L, Lpad, h_q, h_kv, d, scale, causal,
                                  nullptr, nullptr, L, st);
@@ -259,26 +334,25 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     const gqa::KvStrides vsd{L * h_kv * d, d, (int64_t)h_kv * d};       // [B, L, h_kv, d]
     if (k_cache) {   // rotated K and V into the cache; attention reads the rotated copy
       float* kp = (float*)(wsb + ws.kp_off);
+      tc.bind(nullptr, te.kernel_start);
       e = gqa::launch_kv_prepare_f32((const float*)k, (const float*)v, cs, kp, (float*)k_cache,
                                      (float*)v_cache, B, L, h_kv, d, cap, st);
       if (e != hipSuccess) return hip_fail(e, "K preparation launch");
-      if (ev.first) (void)hipEventRecord(ev.first, st);
+      tc.bind(nullptr, te.kernel_stop);
       const gqa::KvStrides ksd{(int64_t)h_kv * L * d, L * d, d};        // [B][h_kv][L][d]
       e = gqa::launch_prefill_f32((const float*)q, kp, (const float*)v, cs, nullptr, o,
                                   out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, ksd,
                                   vsd, nullptr, nullptr, L, st);
     } else {         // no cache: the attention kernel rotates K as it stages each tile
-      if (ev.first) (void)hipEventRecord(ev.first, st);
+      tc.bind(nullptr, te.kernel_stop);
       e = gqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, cs, cs, o,
                                   out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, vsd,
                                   vsd, nullptr, nullptr, L, st);
     }
   }
-  if (ev.second) {
-    (void)hipEventRecord(ev.second, st);
-    g_timing.rec[0].push_back(ev);
-  }
-  return e == hipSuccess ? GQA_OK : hip_fail(e, "prefill attention launch");
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  tc.done();
+  return GQA_OK;
 }
 
 size_t gqa_decode_workspace_size(int64_t B, int h_q, int h_kv, int d, int64_t cap) {
@@ -351,12 +425,12 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, void* o
   a.q_pos = q_pos;
   a.rp = rope_params(theta, d);
   a.scale = scale;
-  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
-  if (g_timing.on && !noalloc) ev = g_timing.take();
+  TimedCall tc(1, false, true, !noalloc);
   hipError_t e = gqa::launch_decode(a, decode_ws_ptrs(workspace, ws), (hipStream_t)stream,
-                                    ev.first, ev.second);
-  if (ev.first) g_timing.rec[1].push_back(ev);
-  return e == hipSuccess ? GQA_OK : hip_fail(e, "decode launch");
+                                    tc.events());
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  tc.done();
+  return GQA_OK;
 }
 
 }  // namespace
@@ -423,18 +497,23 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
   const PrefillWs ws = prefill_ws(in_dtype, B, kend, h_kv, d);
   float2* cs = (float2*)(wsb + ws.cs_off);
   const gqa::RopeParams rp = rope_params(theta, d);
+  // timing: the table opens the call; the kernel before the attention
+  // kernel opens the latter's interval; the attention kernel ends both
+  TimedCall tc(0, true, false);
+  const gqa::CallEvents& te = tc.ev();
+  const bool f32_attn_next = in_dtype != GQA_BF16;   // no preparation pass before attention
+  tc.bind(te.call_start, f32_attn_next && !k ? te.kernel_start : nullptr);
   hipError_t e = gqa::launch_rope_table(cs, kend, d, 0, rp, st);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   // 1) the chunk's rotated K and its V into the cache rows start[b] + i
   //    (k, v NULL: an earlier call, e.g. gqa_qkv_epilogue, put them there)
   if (k) {
+    tc.bind(nullptr, f32_attn_next ? te.kernel_start : nullptr);
     e = gqa::launch_cache_append(k, v, k_cache, v_cache, in_dtype == GQA_BF16, start, len, B, C,
                                  h_kv, d, cap, kend, rp, st);
     if (e != hipSuccess) return hip_fail(e, "cache append launch");
   }
 
-  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
-  if (g_timing.on) ev = g_timing.take();
   if (in_dtype == GQA_BF16) {
     // 2) keys 0 .. start[b] + len[b] - 1 of the cache into the attention layout
     const int64_t Lpad = prefill_lpad(kend);
@@ -442,28 +521,27 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
     uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
     float* kmax = (float*)(wsb + ws.kmax_off);
     int* kexp = (int*)(wsb + ws.kexp_off);
+    tc.bind(nullptr, te.kernel_start);
     e = gqa::launch_kv_prepare_bf16((const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
                                     nullptr, kp, vt, kmax, kexp, nullptr, nullptr, B, C, Lpad, h_kv,
                                     d, cap, cap, start, len, kend, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     // 3) the chunk's queries against them
-    if (ev.first) (void)hipEventRecord(ev.first, st);
+    tc.bind(nullptr, te.kernel_stop);
     e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, kexp, q_rotated ? nullptr : cs, o,
                                  out_dtype == GQA_BF16, B, C, Lpad, h_q, h_kv, d, scale, 1, start,
                                  len, kend, st);
   } else {
     // 2) the chunk's queries against the cache itself
     const gqa::KvStrides csd{cap * h_kv * d, d, (int64_t)h_kv * d};   // [B, cap, h_kv, d]
-    if (ev.first) (void)hipEventRecord(ev.first, st);
+    tc.bind(nullptr, te.kernel_stop);
     e = gqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache,
                                 q_rotated ? nullptr : cs, nullptr, o, out_dtype == GQA_BF16, B, C,
                                 h_q, h_kv, d, scale, 1, csd, csd, start, len, kend, st);
   }
-  if (ev.second) {
-    (void)hipEventRecord(ev.second, st);
-    g_timing.rec[0].push_back(ev);
-  }
-  return e == hipSuccess ? GQA_OK : hip_fail(e, "chunked prefill launch");
+  if (e != hipSuccess) return hip_fail(e, "chunked prefill launch");
+  tc.done();
+  return GQA_OK;
 }
 
 namespace {
@@ -533,11 +611,11 @@ int decode_ragged_launch(const void* q, const void* k_cache, const void* v_cache
   a.append_end = append_end;
   a.rp = rope_params(theta, d);
   a.scale = scale;
-  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
-  if (g_timing.on) ev = g_timing.take();
-  hipError_t e = gqa::launch_decode(a, decode_ws_ptrs(workspace, ws), st, ev.first, ev.second);
-  if (ev.first) g_timing.rec[1].push_back(ev);
-  return e == hipSuccess ? GQA_OK : hip_fail(e, "decode launch");
+  TimedCall tc(1, k_new != nullptr, true);
+  hipError_t e = gqa::launch_decode(a, decode_ws_ptrs(workspace, ws), st, tc.events());
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  tc.done();
+  return GQA_OK;
 }
 
 }  // namespace
@@ -672,27 +750,28 @@ int gqa_set_rope_yarn(double factor, double original_max_position, double beta_f
 }
 
 int gqa_timing_enable(int on) {
+  if (on) g_timing.clear();
   g_timing.on = on != 0;
   return GQA_OK;
 }
 
 int gqa_timing_read(int which, double* total_ms, int64_t* count) {
   g_err.clear();
-  if (which < 0 || which > 1 || !total_ms || !count)
+  if (which < 0 || which > 3 || !total_ms || !count)
     return fail(GQA_ERR_INVALID_ARG, "bad timing query");
   double tot = 0.0;
   int64_t n = 0;
-  for (auto& p : g_timing.rec[which]) {
-    hipError_t e = hipEventSynchronize(p.second);
+  for (const auto& ev : g_timing.rec[which & 1]) {
+    const hipEvent_t t0 = which < 2 ? ev.kernel_start : ev.call_start;
+    const hipEvent_t t1 = which < 2 ? ev.kernel_stop : ev.call_stop;
+    hipError_t e = hipEventSynchronize(t1);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     float ms = 0.f;
-    e = hipEventElapsedTime(&ms, p.first, p.second);
+    e = hipEventElapsedTime(&ms, t0, t1);
     if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
     tot += ms;
     ++n;
-    g_timing.pool.push_back(p);
   }
-  g_timing.rec[which].clear();
   *total_ms = tot;
   *count = n;
   return GQA_OK;

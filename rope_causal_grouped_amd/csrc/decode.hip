@@ -613,7 +613,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t st,
-                         hipEvent_t ev_begin, hipEvent_t ev_end) {
+                         const CallEvents* ev) {
   const int g = a.h_q / a.h_kv;
   const int n_hb = (g + 15) / 16;
   const int n_split = decode_num_splits(a.kv_len, a.in_bf16);
@@ -622,17 +622,17 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t
   int q_rotated = a.q_rotated;
   hipError_t err;
   if (a.k_new) {   // 0) append the new token; the query, rotated once, into the workspace
+    if (ev) next_launch_events() = LaunchEvents{ev->call_start, ev->kernel_start};
     if (a.in_bf16)
-      decode_prep_kernel<uint16_t><<<(unsigned)a.B, 256, 0, st>>>(
-          (const uint16_t*)a.q, (uint16_t*)w.qr, (const uint16_t*)a.k_new,
-          (const uint16_t*)a.v_new, (uint16_t*)a.kc, (uint16_t*)a.vc, a.h_q, a.h_kv, a.d,
-          a.append_end, a.qpos_arr, a.q_rotated, a.rp, kr);
+      err = launch_kernel(decode_prep_kernel<uint16_t>, dim3((unsigned)a.B), dim3(256), st,
+                          (const uint16_t*)a.q, (uint16_t*)w.qr, (const uint16_t*)a.k_new,
+                          (const uint16_t*)a.v_new, (uint16_t*)a.kc, (uint16_t*)a.vc, a.h_q,
+                          a.h_kv, a.d, a.append_end, a.qpos_arr, a.q_rotated, a.rp, kr);
     else
-      decode_prep_kernel<float><<<(unsigned)a.B, 256, 0, st>>>(
-          (const float*)a.q, (float*)w.qr, (const float*)a.k_new, (const float*)a.v_new,
-          (float*)a.kc, (float*)a.vc, a.h_q, a.h_kv, a.d, a.append_end, a.qpos_arr,
-          a.q_rotated, a.rp, kr);
-    err = hipGetLastError();
+      err = launch_kernel(decode_prep_kernel<float>, dim3((unsigned)a.B), dim3(256), st,
+                          (const float*)a.q, (float*)w.qr, (const float*)a.k_new,
+                          (const float*)a.v_new, (float*)a.kc, (float*)a.vc, a.h_q, a.h_kv, a.d,
+                          a.append_end, a.qpos_arr, a.q_rotated, a.rp, kr);
     if (err != hipSuccess) return err;
     q = w.qr;
     q_rotated = 1;
@@ -642,12 +642,12 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t
   const bool grp4 = a.in_bf16 && a.h_kv % 4 == 0;
   dim3 grid((unsigned)n_split, (unsigned)((grp4 ? a.h_kv / 4 : a.h_kv) * n_hb), (unsigned)a.B);
   const float sl2 = a.scale * 1.4426950408889634f;
-  if (ev_begin) (void)hipEventRecord(ev_begin, st);
+  if (ev) next_launch_events() = LaunchEvents{a.k_new ? nullptr : ev->kernel_start, ev->kernel_stop};
 #define GQA_SPLIT(KERNEL, T, TPL, SC)                                                        \
-  KERNEL<TPL><<<grid, 256, 0, st>>>((const T*)q, (const T*)a.kc, (const T*)a.vc, w.m, w.l,   \
-                                    w.o, a.h_q, a.h_kv, g, n_hb, (int)a.kv_len,              \
-                                    (double)a.q_pos, a.rp, SC, n_split, a.kvl_arr,            \
-                                    a.qpos_arr, a.kvl_from_pos, q_rotated, kr)
+  err = launch_kernel(KERNEL<TPL>, grid, dim3(256), st, (const T*)q, (const T*)a.kc,         \
+                      (const T*)a.vc, w.m, w.l, w.o, a.h_q, a.h_kv, g, n_hb, (int)a.kv_len,  \
+                      (double)a.q_pos, a.rp, SC, n_split, a.kvl_arr, a.qpos_arr,             \
+                      a.kvl_from_pos, q_rotated, kr)
 #define GQA_BF16(DD, PG)                                                             \
   do {                                                                               \
     if (grp4) GQA_SPLIT(decode_split_bf16_kernel, uint16_t, GQA_TPL3(DD, PG, true), sl2); \
@@ -668,20 +668,20 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t
 #undef GQA_TPL3
 #undef GQA_BF16
 #undef GQA_SPLIT
-  err = hipGetLastError();
-  if (ev_end) (void)hipEventRecord(ev_end, st);
   if (err != hipSuccess) return err;
   // 2) merge of the chunks
   dim3 mgrid((unsigned)a.h_q, (unsigned)a.B);
-#define GQA_MERGE(DD, OB) \
-  decode_merge_kernel<DD, OB><<<mgrid, DD, 0, st>>>(w.m, w.l, w.o, a.o, a.h_q, a.h_kv, g, n_split)
+  if (ev) next_launch_events() = LaunchEvents{nullptr, ev->call_stop};
+#define GQA_MERGE(DD, OB)                                                                 \
+  err = launch_kernel(decode_merge_kernel<DD, OB>, mgrid, dim3(DD), st, w.m, w.l, w.o, a.o, \
+                      a.h_q, a.h_kv, g, n_split)
   if (a.d == 128) {
     if (a.out_bf16) GQA_MERGE(128, true); else GQA_MERGE(128, false);
   } else {
     if (a.out_bf16) GQA_MERGE(64, true); else GQA_MERGE(64, false);
   }
 #undef GQA_MERGE
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace gqa

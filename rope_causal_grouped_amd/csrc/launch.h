@@ -2,12 +2,55 @@
 // assumes the API layer has validated its arguments and enqueues on `st`.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <cstddef>
+#include <tuple>
+#include <type_traits>
+#include <utility>
 
 #include "common.h"
 
 namespace gqa {
+
+// ---- benchmark timing bound to kernel dispatches
+// HIP events that the next launch_kernel of this host thread attaches to its
+// dispatch (hipExtLaunchKernel): the start event takes the kernel's start
+// time, the stop event its end.  Unlike hipEventRecord, which enqueues a
+// marker that the next kernel then waits behind, this adds no packet to the
+// stream between the kernels of a call.  Taken (and cleared) by that launch.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& next_launch_events();
+
+// Events of one timed call: its first kernel's start and last kernel's end,
+// and the opening and end of its main kernel's interval (call_start may be
+// kernel_start, call_stop may be kernel_stop).
+struct CallEvents {
+  hipEvent_t call_start = nullptr, kernel_start = nullptr, kernel_stop = nullptr,
+             call_stop = nullptr;
+};
+
+// Launches kernel k on st with the arguments converted to its parameter
+// types, binding the pending LaunchEvents (if any) to the dispatch.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A&&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  const LaunchEvents ev = std::exchange(next_launch_events(), LaunchEvents{});
+  std::tuple<std::decay_t<P>...> vals{static_cast<std::decay_t<P>>(std::forward<A>(a))...};
+  void* args[sizeof...(P) > 0 ? sizeof...(P) : 1];
+  std::apply([&](auto&... v) {
+    size_t i = 0;
+    ((args[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  if (ev.start || ev.stop)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, st, ev.start,
+                              ev.stop, 0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, st);
+}
 
 constexpr int kPrefillTileK = 64;      // key padding granule of the prepared K/V
 constexpr int kPrefillTileV = 32;      // keys per attention tile; V^T is stored per such tile
@@ -114,8 +157,13 @@ struct DecodeWsPtrs {
   void* qr;
 };
 
+// ev (may be NULL): call_start opens the call's first kernel (the append
+// step's preparation, else the split kernel); kernel_start is the split
+// kernel's start, or the preparation's end when that precedes it (a start
+// event inside the call would delay the split kernel); kernel_stop ends the
+// split kernel, call_stop the merge.
 hipError_t launch_decode(const DecodeArgs& a, const DecodeWsPtrs& w, hipStream_t st,
-                         hipEvent_t ev_begin, hipEvent_t ev_end);
+                         const CallEvents* ev);
 
 // streaming read of `bytes` (a multiple of 16) at p, for benchmark context
 hipError_t launch_stream_read(const void* p, size_t bytes, unsigned* sink, hipStream_t st);

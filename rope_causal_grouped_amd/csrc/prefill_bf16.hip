@@ -681,11 +681,11 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   const int s_parts = low >= kXcds ? 1 : kXcds / low;
   const int ppx = n_bu * s_parts / kXcds;
   const unsigned grid = (unsigned)((int64_t)kXcds * ppx * ((n_rb + s_parts - 1) / s_parts));
+  hipError_t e;
 #define GQA_LAUNCH(DD, OB, PR)                                                               \
-  prefill_bf16_kernel<DD, OB, PR><<<grid, NW * 64, 0, st>>>(q, kp, vt, kmax, kexp, cs, o, (int)L, \
-                                                            (int)Lpad, h_q, h_kv, g, n_rb,   \
-                                                            n_bu, sl2, causal, qstart, qlen, \
-                                                            (int)kend)
+  e = launch_kernel(prefill_bf16_kernel<DD, OB, PR>, dim3(grid), dim3(NW * 64), st, q, kp, vt, \
+                    kmax, kexp, cs, o, (int)L, (int)Lpad, h_q, h_kv, g, n_rb, n_bu, sl2,       \
+                    causal, qstart, qlen, (int)kend)
 #define GQA_LAUNCH_D(DD, OB) \
   do { if (cs) GQA_LAUNCH(DD, OB, true); else GQA_LAUNCH(DD, OB, false); } while (0)
   if (d == 128) {
@@ -695,7 +695,7 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   }
 #undef GQA_LAUNCH_D
 #undef GQA_LAUNCH
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace gqa

@@ -242,17 +242,17 @@ hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, c
                               int64_t kend, hipStream_t st) {
   const int g = h_q / h_kv;
   dim3 grid((unsigned)((L + 15) / 16), (unsigned)h_q, (unsigned)B);
-#define GQA_LAUNCH(DD, OB)                                                               \
-  prefill_f32_kernel<DD, OB><<<grid, 256, 0, st>>>(q, kp, v, cs, kcs, o, (int)L, h_q, h_kv, g, \
-                                                   scale, causal, ks, vs, qstart, qlen,       \
-                                                   (int)kend)
+  hipError_t e;
+#define GQA_LAUNCH(DD, OB)                                                                  \
+  e = launch_kernel(prefill_f32_kernel<DD, OB>, grid, dim3(256), st, q, kp, v, cs, kcs, o,  \
+                    (int)L, h_q, h_kv, g, scale, causal, ks, vs, qstart, qlen, (int)kend)
   if (d == 128) {
     if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);
   } else {
     if (out_bf16) GQA_LAUNCH(64, true); else GQA_LAUNCH(64, false);
   }
 #undef GQA_LAUNCH
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace gqa

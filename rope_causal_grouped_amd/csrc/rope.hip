@@ -88,8 +88,7 @@ hipError_t launch_rope_table(float2* cs, int64_t L, int d, int64_t pos0, RopePar
   const int64_t per_block = (int64_t)(256 / (d / 2)) * kTablePosPerThread;
   const int64_t grid = (L + per_block - 1) / per_block;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  rope_table_kernel<<<(unsigned)grid, 256, 0, st>>>(cs, L, d, pos0, rp);
-  return hipGetLastError();
+  return launch_kernel(rope_table_kernel, dim3((unsigned)grid), dim3(256), st, cs, L, d, pos0, rp);
 }
 
 // ---------------------------------------------------------------------------
@@ -339,14 +338,12 @@ hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const Ro
   const RopeParams rp = rope ? *rope : RopeParams{};
   dim3 grid((unsigned)(Lpad / 64), (unsigned)h_kv, (unsigned)B);
   if (d == 128)
-    kv_prepare_bf16_kernel<128><<<grid, 256, 0, st>>>(k, v, rotate, rp, cs_out, kp, vt, kmax,
-                                                      kexp, kc, vc, L, Lpad, h_kv, cap, src_rows,
-                                                      kstart, klen, kend);
-  else
-    kv_prepare_bf16_kernel<64><<<grid, 256, 0, st>>>(k, v, rotate, rp, cs_out, kp, vt, kmax,
-                                                     kexp, kc, vc, L, Lpad, h_kv, cap, src_rows,
-                                                     kstart, klen, kend);
-  return hipGetLastError();
+    return launch_kernel(kv_prepare_bf16_kernel<128>, grid, dim3(256), st, k, v, rotate, rp,
+                         cs_out, kp, vt, kmax, kexp, kc, vc, L, Lpad, h_kv, cap, src_rows, kstart,
+                         klen, kend);
+  return launch_kernel(kv_prepare_bf16_kernel<64>, grid, dim3(256), st, k, v, rotate, rp, cs_out,
+                       kp, vt, kmax, kexp, kc, vc, L, Lpad, h_kv, cap, src_rows, kstart, klen,
+                       kend);
 }
 
 // ---------------------------------------------------------------------------
@@ -414,15 +411,13 @@ hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc,
   const int64_t want = (n_pairs + 255) / 256;
   const int grid = (int)(want < 65536 ? want : 65536);
   if (bf16)
-    cache_append_kernel<uint16_t><<<grid, 256, 0, st>>>(
-        (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kc, (uint16_t*)vc, start, len, n_pairs,
-        C, h_kv, d, cap, end, rp, bt, ps_log2, max_pages, num_pages);
-  else
-    cache_append_kernel<float><<<grid, 256, 0, st>>>((const float*)k, (const float*)v, (float*)kc,
-                                                     (float*)vc, start, len, n_pairs, C, h_kv, d,
-                                                     cap, end, rp, bt, ps_log2, max_pages,
-                                                     num_pages);
-  return hipGetLastError();
+    return launch_kernel(cache_append_kernel<uint16_t>, dim3(grid), dim3(256), st,
+                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kc, (uint16_t*)vc,
+                         start, len, n_pairs, C, h_kv, d, cap, end, rp, bt, ps_log2, max_pages,
+                         num_pages);
+  return launch_kernel(cache_append_kernel<float>, dim3(grid), dim3(256), st, (const float*)k,
+                       (const float*)v, (float*)kc, (float*)vc, start, len, n_pairs, C, h_kv, d,
+                       cap, end, rp, bt, ps_log2, max_pages, num_pages);
 }
 
 hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* cs, float* kp,
@@ -430,10 +425,10 @@ hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* c
                                  int64_t cap, hipStream_t st) {
   dim3 grid((unsigned)((L + 63) / 64), (unsigned)h_kv, (unsigned)B);
   if (d == 128)
-    kv_prepare_f32_kernel<128><<<grid, 256, 0, st>>>(k, v, cs, kp, kc, vc, L, h_kv, cap);
-  else
-    kv_prepare_f32_kernel<64><<<grid, 256, 0, st>>>(k, v, cs, kp, kc, vc, L, h_kv, cap);
-  return hipGetLastError();
+    return launch_kernel(kv_prepare_f32_kernel<128>, grid, dim3(256), st, k, v, cs, kp, kc, vc, L,
+                         h_kv, cap);
+  return launch_kernel(kv_prepare_f32_kernel<64>, grid, dim3(256), st, k, v, cs, kp, kc, vc, L,
+                       h_kv, cap);
 }
 
 // ---------------------------------------------------------------------------

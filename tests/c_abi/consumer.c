@@ -80,6 +80,9 @@ int main(void) {
   expect(gqa_timing_enable(0) == GQA_OK, "gqa_timing_enable");
   expect(gqa_timing_read(0, &ms, &count) == GQA_OK && count == 0 && ms == 0.0,
          "gqa_timing_read with nothing recorded");
+  expect(gqa_timing_read(3, &ms, &count) == GQA_OK && count == 0,
+         "gqa_timing_read of whole decode calls");
+  REJECTS(gqa_timing_read(4, &ms, &count));
 
   REJECTS(gqa_stream_read(NULL, 16, NULL, NULL));
 

@@ -249,6 +249,41 @@ def test_decode_small(dtype, shape):
         assert_parity(host(ob), want, dtype, "decode bf16 out")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_timing_bound_to_dispatches(dtype):
+    """With timing on, every call records its main kernel and the whole call
+    through events bound to its own dispatches; the outputs are the same
+    bits as with timing off, and each call spans at least its main kernel."""
+    B, L, h_q, h_kv, d = 2, 300, 14, 2, 128
+    q, k, v = small_case(B, L, h_q, h_kv, d, dtype, 41)
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    cap = L + 16
+    kc = torch.zeros((B, cap, h_kv, d), dtype=dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    ref_p = gqa.prefill(qd, kd, vd, k_cache=kc, v_cache=vc)
+    ref_d = gqa.decode(qd[:, L - 1].contiguous(), kc, vc, kv_len=L, q_pos=L - 1)
+    torch.cuda.synchronize()
+    gqa.timing_enable(True)
+    outs = []
+    for _ in range(3):
+        outs.append((gqa.prefill(qd, kd, vd, k_cache=kc, v_cache=vc),
+                     gqa.decode(qd[:, L - 1].contiguous(), kc, vc, kv_len=L, q_pos=L - 1)))
+    torch.cuda.synchronize()
+    gqa.timing_enable(False)
+    t = [gqa.timing_read(w) for w in range(4)]
+    note(f"timing {dtype}: {t}")
+    for op, od in outs:
+        assert torch.equal(op, ref_p) and torch.equal(od, ref_d)
+    for w in range(4):
+        assert t[w][1] == 3 and t[w][0] > 0.0, (w, t[w])
+    assert t[2][0] >= t[0][0] and t[3][0] >= t[1][0]
+    # records stay readable until timing is enabled again, which drops them
+    assert gqa.timing_read(0) == t[0]
+    gqa.timing_enable(True)
+    gqa.timing_enable(False)
+    assert gqa.timing_read(2) == (0.0, 0)
+
+
 def test_stream_read_runs():
     """The benchmark's streaming-read helper reads a buffer and leaves the
     sink alone for data whose XOR is not its marker value."""
