@@ -14,10 +14,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// 2*pi split in two doubles (head + tail) for argument reduction.
-constexpr double kTwoPiHi = 6.283185307179586232;
-constexpr double kTwoPiLo = 2.449293598294706414e-16;
-constexpr double kInvTwoPi = 0.15915494309189533577;
+// pi/2 split in two doubles (head + tail) for argument reduction, and 2/pi.
+constexpr double kHalfPiHi = 1.570796326794896558;
+constexpr double kHalfPiLo = 6.123233995736766036e-17;
+constexpr double kTwoOverPi = 0.63661977236758134308;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
@@ -49,16 +49,32 @@ __device__ __forceinline__ double rope_omega(int j, int d, const RopeParams& rp)
   return w * (1.0 - r) + w * rp.inv_factor * r;
 }
 
-// cos and sin of pos * omega.  The angle is formed and reduced to
-// [-pi, pi] in fp64 (at position 32768 an fp32 angle would already be off
-// by ~2e-3 rad), then evaluated in fp32.
-__device__ __forceinline__ void rope_cos_sin(double pos, double omega, float& c,
-                                             float& s) {
-  double a = pos * omega;
-  double n = rint(a * kInvTwoPi);
-  double r = fma(-n, kTwoPiHi, a);
-  r = fma(-n, kTwoPiLo, r);
-  sincosf((float)r, &s, &c);
+// cos and sin of pos * omega.  The angle a is formed and reduced in fp64
+// (at position 32768 an fp32 angle would already be off by ~2e-3 rad):
+// n = rint(a * 2/pi), r = a - n * pi/2 with pi/2 in two parts, so
+// |r| <= pi/4 and the quadrant is n mod 4.  sin r and cos r then come from
+// their Taylor series in fp32, through r^9 and r^8 (the first omitted terms,
+// r^11/11! and r^10/10!, stay below 3e-8 for |r| <= pi/4), and the quadrant
+// swaps and negates them.  A library sincosf would also carry its own
+// large-argument reduction, which the compiler evaluates on every call.
+__device__ __forceinline__ void rope_cos_sin(double pos, double omega, float& c, float& s) {
+  const double a = pos * omega;
+  const double n = rint(a * kTwoOverPi);
+  double rd = fma(-n, kHalfPiHi, a);
+  rd = fma(-n, kHalfPiLo, rd);
+  const float r = (float)rd, r2 = r * r;
+  float sr = fmaf(r2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+  sr = fmaf(r2, sr, 1.0f / 120.0f);
+  sr = fmaf(r2, sr, -1.0f / 6.0f);
+  sr = fmaf(r2 * r, sr, r);
+  float cr = fmaf(r2, 1.0f / 40320.0f, -1.0f / 720.0f);
+  cr = fmaf(r2, cr, 1.0f / 24.0f);
+  cr = fmaf(r2, cr, -0.5f);
+  cr = fmaf(r2, cr, 1.0f);
+  const int q = (int)(int64_t)n & 3;   // two's complement: also right for n < 0
+  const float sv = (q & 1) ? cr : sr, cv = (q & 1) ? sr : cr;
+  s = (q & 2) ? -sv : sv;
+  c = ((q + 1) & 2) ? -cv : cv;
 }
 
 // cos and sin of pair j at position pos under rp (YaRN's mscale included).

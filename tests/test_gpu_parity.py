@@ -81,6 +81,28 @@ def test_rope_apply(dtype, d, pos0):
         assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-5)
 
 
+@pytest.mark.parametrize("pos0", [0, 32768 - 2048, (1 << 24) - 2048])
+def test_rope_cos_sin_error_bound(pos0):
+    """Unit vectors (1 in the first half of each pair, 0 in the second) come
+    out of an fp32 rotation as (cos, sin) of pos * omega_j themselves; every
+    value lies within 2.5e-7 (about two fp32 ulps at 1) of cos and sin taken
+    in extended precision of the fp64 angle, at positions up to 2^24."""
+    d, L = 128, 2048
+    note(f"rope cos/sin bound pos0={pos0}")
+    x = torch.zeros((1, L, 1, d), dtype=torch.float32, device="cuda")
+    x[..., : d // 2] = 1.0
+    gqa.rope_apply(x, pos0=pos0)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy().astype(np.float64)[0, :, 0]
+    j = np.arange(d // 2, dtype=np.float64)
+    omega = np.float64(gqa.ROPE_THETA) ** (-2.0 * j / d)
+    ang = np.longdouble(np.arange(pos0, pos0 + L, dtype=np.float64))[:, None] * np.longdouble(omega)
+    err_c = np.abs(got[:, : d // 2] - np.cos(ang).astype(np.float64)).max()
+    err_s = np.abs(got[:, d // 2:] - np.sin(ang).astype(np.float64)).max()
+    note(f"  max error cos {err_c:.3e} sin {err_s:.3e}")
+    assert err_c <= 2.5e-7 and err_s <= 2.5e-7
+
+
 # ------------------------------------------------------- prefill, small --
 
 SMALL_BF16 = [
