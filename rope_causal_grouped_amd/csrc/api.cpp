@@ -304,18 +304,13 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
   float2* cs = (float2*)(wsb + ws.cs_off);
   const gqa::RopeParams rp = rope_params(theta, d);
   hipError_t e = hipSuccess;
-  // timing: the first kernel (the table, or the bf16 K/V preparation) opens
-  // the call; the kernel before the attention kernel opens the latter's
-  // interval; the attention kernel ends both
-  TimedCall tc(0, true, false);
+  // timing: the first kernel opens the call; the attention kernel's
+  // interval opens at its own start when it is the first kernel, else at
+  // the end of the preparation pass before it; the attention kernel ends both
+  const bool bf16_in = in_dtype == GQA_BF16;
+  TimedCall tc(0, bf16_in || k_cache != nullptr, false);
   const gqa::CallEvents& te = tc.ev();
-  if (in_dtype != GQA_BF16) {   // the bf16 preparation kernel writes the table itself
-    tc.bind(te.call_start, k_cache ? nullptr : te.kernel_start);
-    e = gqa::launch_rope_table(cs, L, d, 0, rp, st);
-    if (e != hipSuccess) return hip_fail(e, "rope table launch");
-  }
-
-  if (in_dtype == GQA_BF16) {
+  if (bf16_in) {   // the preparation kernel also writes the queries' cos/sin table
     const int64_t Lpad = prefill_lpad(L);
     uint16_t* kp = (uint16_t*)(wsb + ws.kp_off);
     uint16_t* vt = (uint16_t*)(wsb + ws.vt_off);
@@ -330,22 +325,22 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, kexp, cs, o,
                                  out_dtype == GQA_BF16, B, L, Lpad, h_q, h_kv, d, scale, causal,
                                  nullptr, nullptr, L, st);
-  } else {
+  } else {         // fp32: the kernels form their cos/sin themselves
     const gqa::KvStrides vsd{L * h_kv * d, d, (int64_t)h_kv * d};       // [B, L, h_kv, d]
     if (k_cache) {   // rotated K and V into the cache; attention reads the rotated copy
       float* kp = (float*)(wsb + ws.kp_off);
-      tc.bind(nullptr, te.kernel_start);
-      e = gqa::launch_kv_prepare_f32((const float*)k, (const float*)v, cs, kp, (float*)k_cache,
+      tc.bind(te.call_start, te.kernel_start);
+      e = gqa::launch_kv_prepare_f32((const float*)k, (const float*)v, rp, kp, (float*)k_cache,
                                      (float*)v_cache, B, L, h_kv, d, cap, st);
       if (e != hipSuccess) return hip_fail(e, "K preparation launch");
       tc.bind(nullptr, te.kernel_stop);
       const gqa::KvStrides ksd{(int64_t)h_kv * L * d, L * d, d};        // [B][h_kv][L][d]
-      e = gqa::launch_prefill_f32((const float*)q, kp, (const float*)v, cs, nullptr, o,
+      e = gqa::launch_prefill_f32((const float*)q, kp, (const float*)v, 1, 0, rp, o,
                                   out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, ksd,
                                   vsd, nullptr, nullptr, L, st);
-    } else {         // no cache: the attention kernel rotates K as it stages each tile
-      tc.bind(nullptr, te.kernel_stop);
-      e = gqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, cs, cs, o,
+    } else {         // no cache: one kernel, which rotates K as it stages each tile
+      tc.bind(te.kernel_start, te.kernel_stop);
+      e = gqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, 1, 1, rp, o,
                                   out_dtype == GQA_BF16, B, L, h_q, h_kv, d, scale, causal, vsd,
                                   vsd, nullptr, nullptr, L, st);
     }
@@ -497,24 +492,28 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
   const PrefillWs ws = prefill_ws(in_dtype, B, kend, h_kv, d);
   float2* cs = (float2*)(wsb + ws.cs_off);
   const gqa::RopeParams rp = rope_params(theta, d);
-  // timing: the table opens the call; the kernel before the attention
-  // kernel opens the latter's interval; the attention kernel ends both
-  TimedCall tc(0, true, false);
+  // timing: the first kernel opens the call; the attention kernel's
+  // interval opens at its own start when it is the first kernel, else at
+  // the end of the kernel before it; the attention kernel ends both
+  const bool bf16_in = in_dtype == GQA_BF16;
+  TimedCall tc(0, bf16_in || k != nullptr, false);
   const gqa::CallEvents& te = tc.ev();
-  const bool f32_attn_next = in_dtype != GQA_BF16;   // no preparation pass before attention
-  tc.bind(te.call_start, f32_attn_next && !k ? te.kernel_start : nullptr);
-  hipError_t e = gqa::launch_rope_table(cs, kend, d, 0, rp, st);
-  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  hipError_t e = hipSuccess;
+  if (bf16_in) {   // the queries' cos/sin table (the fp32 kernel forms its own)
+    tc.bind(te.call_start, nullptr);
+    e = gqa::launch_rope_table(cs, kend, d, 0, rp, st);
+    if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  }
   // 1) the chunk's rotated K and its V into the cache rows start[b] + i
   //    (k, v NULL: an earlier call, e.g. gqa_qkv_epilogue, put them there)
   if (k) {
-    tc.bind(nullptr, f32_attn_next ? te.kernel_start : nullptr);
+    tc.bind(bf16_in ? nullptr : te.call_start, bf16_in ? nullptr : te.kernel_start);
     e = gqa::launch_cache_append(k, v, k_cache, v_cache, in_dtype == GQA_BF16, start, len, B, C,
                                  h_kv, d, cap, kend, rp, st);
     if (e != hipSuccess) return hip_fail(e, "cache append launch");
   }
 
-  if (in_dtype == GQA_BF16) {
+  if (bf16_in) {
     // 2) keys 0 .. start[b] + len[b] - 1 of the cache into the attention layout
     const int64_t Lpad = prefill_lpad(kend);
     uint16_t* kp = (uint16_t*)(wsb + ws.kp_off);
@@ -534,10 +533,10 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
   } else {
     // 2) the chunk's queries against the cache itself
     const gqa::KvStrides csd{cap * h_kv * d, d, (int64_t)h_kv * d};   // [B, cap, h_kv, d]
-    tc.bind(nullptr, te.kernel_stop);
+    tc.bind(k ? nullptr : te.kernel_start, te.kernel_stop);
     e = gqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache,
-                                q_rotated ? nullptr : cs, nullptr, o, out_dtype == GQA_BF16, B, C,
-                                h_q, h_kv, d, scale, 1, csd, csd, start, len, kend, st);
+                                q_rotated ? 0 : 1, 0, rp, o, out_dtype == GQA_BF16, B, C, h_q, h_kv,
+                                d, scale, 1, csd, csd, start, len, kend, st);
   }
   if (e != hipSuccess) return hip_fail(e, "chunked prefill launch");
   tc.done();

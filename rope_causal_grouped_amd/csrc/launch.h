@@ -73,7 +73,7 @@ hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const Ro
                                   const int64_t* kstart, const int64_t* klen, int64_t kend,
                                   hipStream_t st);
 
-hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* cs, float* kp,
+hipError_t launch_kv_prepare_f32(const float* k, const float* v, RopeParams rp, float* kp,
                                  float* kc, float* vc, int64_t B, int64_t L, int h_kv, int d,
                                  int64_t cap, hipStream_t st);
 
@@ -103,10 +103,10 @@ struct KvStrides {
   int64_t batch, head, row;
 };
 
-// cs: the queries' cos/sin table (NULL: q is rotated already); kcs: the
-// keys' table, position = key index (NULL: kp holds rotated keys)
-hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, const float2* cs,
-                              const float2* kcs, void* o, int out_bf16, int64_t B, int64_t L,
+// rot_q: rotate the queries at their positions under rp (0: q is rotated
+// already); rot_k: rotate the keys at their index (0: kp holds rotated keys)
+hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, int rot_q,
+                              int rot_k, RopeParams rp, void* o, int out_bf16, int64_t B, int64_t L,
                               int h_q, int h_kv, int d, float scale, int causal, KvStrides ks,
                               KvStrides vs,
                               const int64_t* qstart, const int64_t* qlen, int64_t kend,

@@ -6,9 +6,11 @@
 // Same operation as the bf16 kernel (Qwen2 technical-report walkthrough,
 // aicoding.csdn.net, §4.1.3 steps 3-4).  A workgroup owns 16 positions of
 // one query head; four lanes share a row, each holding a quarter of its dims
-// (dims j and j + d/2 of a RoPE pair stay in one lane).  K' and V tiles of
-// 64 keys are staged in LDS (K rotated while staging, from the cos/sin
-// table, or rotated already by the pass that wrote the cache); each of the
+// (dims j and j + d/2 of a RoPE pair stay in one lane).  The workgroup forms
+// the pairs' frequencies once (fp64, in LDS) and each lane the cos/sin of
+// its own pairs, so the call needs no table kernel.  K' and V tiles of 64
+// keys are staged in LDS (K rotated while staging, or rotated already by the
+// pass that wrote the cache); each of the
 // four waves holds all 16 rows and takes a quarter of every tile's keys,
 // updating its own online softmax four keys at a time, and the quarters are
 // merged exactly at the end.  The small shapes this serves are latency-
@@ -37,15 +39,20 @@ __device__ __forceinline__ float quad_swap(float x) {
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kp, const float* __restrict__ v,
-    const float2* __restrict__ cs, const float2* __restrict__ kcs, void* __restrict__ o, int L,
-    int h_q, int h_kv, int g, float scale, int causal, KvStrides ks_, KvStrides vs_,
-    const int64_t* __restrict__ qstart, const int64_t* __restrict__ qlen, int kend) {
+    int rot_q, int rot_k, RopeParams rp, void* __restrict__ o, int L, int h_q, int h_kv, int g,
+    float scale, int causal, KvStrides ks_, KvStrides vs_, const int64_t* __restrict__ qstart,
+    const int64_t* __restrict__ qlen, int kend) {
   constexpr int TK = 64;                 // keys per staged tile
   constexpr int RB = 16;                 // rows (positions) per workgroup
   constexpr int KQ = TK / 4;             // keys of a tile per wave
   constexpr int E = D / 8;               // pair count per lane
   __shared__ __attribute__((aligned(16))) float ks[TK][D + 4];
   __shared__ __attribute__((aligned(16))) float vs[TK][D + 4];
+  __shared__ double om[D / 2];           // pair frequencies
+  if (rot_q || rot_k) {
+    if (threadIdx.x < D / 2) om[threadIdx.x] = rope_omega(threadIdx.x, D, rp);
+    __syncthreads();
+  }
 
   const int pbk = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int u = t / g;
@@ -82,14 +89,18 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   float qr[2 * E];
   {
     const float* src = q + ((int64_t)((int64_t)b * L + pl) * h_q + t) * D;
-    const float2* csr = cs + (int64_t)pos * (D / 2);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = part * E + e;
       const float x1 = src[j], x2 = src[j + D / 2];
-      const float2 r2 = cs ? csr[j] : make_float2(1.f, 0.f);   // cs NULL: q is rotated
-      qr[e] = fmaf(x1, r2.x, -x2 * r2.y);
-      qr[E + e] = fmaf(x2, r2.x, x1 * r2.y);
+      float c = 1.f, sn = 0.f;   // rot_q = 0: q is rotated already
+      if (rot_q) {
+        rope_cos_sin((double)pos, om[j], c, sn);
+        c *= rp.mscale;
+        sn *= rp.mscale;
+      }
+      qr[e] = fmaf(x1, c, -x2 * sn);
+      qr[E + e] = fmaf(x2, c, x1 * sn);
     }
   }
 
@@ -107,7 +118,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   for (int k0 = 0; k0 < n_keys; k0 += TK) {
     // stage the tile: every 16-byte load issued before the first store.  A
     // thread takes four RoPE pairs (dims j4..j4+3 and j4+d/2..) of a key, so
-    // with kcs set it rotates K here, at the key's position (= its index)
+    // with rot_k set it rotates K here, at the key's position (= its index)
     constexpr int CP = TK * (D / 8) / 256;   // four-pair chunks per thread
     float4 k1[CP], k2[CP], v1[CP], v2[CP];
 #pragma unroll
@@ -123,10 +134,14 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
         k2[r] = *(const float4*)(kr + D / 2);
         v1[r] = *(const float4*)vr;
         v2[r] = *(const float4*)(vr + D / 2);
-        if (kcs) {
-          const float4* c4p = (const float4*)(kcs + (int64_t)key * (D / 2) + j4);
-          const float4 ca = c4p[0], cb = c4p[1];   // (cos, sin) of pairs j4 .. j4+3
-          const float c[4] = {ca.x, ca.z, cb.x, cb.z}, sn[4] = {ca.y, ca.w, cb.y, cb.w};
+        if (rot_k) {
+          float c[4], sn[4];   // (cos, sin) of pairs j4 .. j4+3
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            rope_cos_sin((double)key, om[j4 + e], c[e], sn[e]);
+            c[e] *= rp.mscale;
+            sn[e] *= rp.mscale;
+          }
           float x1[4] = {k1[r].x, k1[r].y, k1[r].z, k1[r].w};
           float x2[4] = {k2[r].x, k2[r].y, k2[r].z, k2[r].w};
           float y1[4], y2[4];
@@ -235,8 +250,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(
   }
 }
 
-hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, const float2* cs,
-                              const float2* kcs, void* o, int out_bf16, int64_t B, int64_t L,
+hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, int rot_q,
+                              int rot_k, RopeParams rp, void* o, int out_bf16, int64_t B, int64_t L,
                               int h_q, int h_kv, int d, float scale, int causal, KvStrides ks,
                               KvStrides vs, const int64_t* qstart, const int64_t* qlen,
                               int64_t kend, hipStream_t st) {
@@ -244,7 +259,7 @@ hipError_t launch_prefill_f32(const float* q, const float* kp, const float* v, c
   dim3 grid((unsigned)((L + 15) / 16), (unsigned)h_q, (unsigned)B);
   hipError_t e;
 #define GQA_LAUNCH(DD, OB)                                                                  \
-  e = launch_kernel(prefill_f32_kernel<DD, OB>, grid, dim3(256), st, q, kp, v, cs, kcs, o,  \
+  e = launch_kernel(prefill_f32_kernel<DD, OB>, grid, dim3(256), st, q, kp, v, rot_q, rot_k, rp, o, \
                     (int)L, h_q, h_kv, g, scale, causal, ks, vs, qstart, qlen, (int)kend)
   if (d == 128) {
     if (out_bf16) GQA_LAUNCH(128, true); else GQA_LAUNCH(128, false);

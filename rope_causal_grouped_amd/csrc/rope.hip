@@ -288,14 +288,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 }
 
 // K preparation for the fp32 prefill: kp[b][u][key][:] = rotated K (fp32),
-// optional cache copies of rotated K and V.
+// optional cache copies of rotated K and V.  The pairs' frequencies are
+// formed once per workgroup (fp64, in LDS).
 template <int D>
 __global__ __launch_bounds__(256) void kv_prepare_f32_kernel(
-    const float* __restrict__ k, const float* __restrict__ v, const float2* __restrict__ cs,
+    const float* __restrict__ k, const float* __restrict__ v, RopeParams rp,
     float* __restrict__ kp, float* __restrict__ kc, float* __restrict__ vc, int64_t L, int h_kv,
     int64_t cap) {
   constexpr int TK = 64;
   constexpr int HALF = D / 2;
+  __shared__ double om[HALF];
+  if (threadIdx.x < HALF) om[threadIdx.x] = rope_omega(threadIdx.x, D, rp);
+  __syncthreads();
   const int tile = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
   const int64_t key0 = (int64_t)tile * TK;
   for (int idx = threadIdx.x; idx < TK * HALF; idx += 256) {
@@ -304,9 +308,12 @@ __global__ __launch_bounds__(256) void kv_prepare_f32_kernel(
     if (key >= L) continue;
     const float* src = k + (((int64_t)b * L + key) * h_kv + u) * D;
     const float x1 = src[j], x2 = src[j + HALF];
-    const float2 r = cs[key * HALF + j];
-    const float o1 = fmaf(x1, r.x, -x2 * r.y);
-    const float o2 = fmaf(x2, r.x, x1 * r.y);
+    float c, sn;
+    rope_cos_sin((double)key, om[j], c, sn);
+    c *= rp.mscale;
+    sn *= rp.mscale;
+    const float o1 = fmaf(x1, c, -x2 * sn);
+    const float o2 = fmaf(x2, c, x1 * sn);
     float* kdst = kp + (((int64_t)b * h_kv + u) * L + key) * D;
     kdst[j] = o1;
     kdst[j + HALF] = o2;
@@ -420,14 +427,14 @@ hipError_t launch_cache_append(const void* k, const void* v, void* kc, void* vc,
                        cap, end, rp, bt, ps_log2, max_pages, num_pages);
 }
 
-hipError_t launch_kv_prepare_f32(const float* k, const float* v, const float2* cs, float* kp,
+hipError_t launch_kv_prepare_f32(const float* k, const float* v, RopeParams rp, float* kp,
                                  float* kc, float* vc, int64_t B, int64_t L, int h_kv, int d,
                                  int64_t cap, hipStream_t st) {
   dim3 grid((unsigned)((L + 63) / 64), (unsigned)h_kv, (unsigned)B);
   if (d == 128)
-    return launch_kernel(kv_prepare_f32_kernel<128>, grid, dim3(256), st, k, v, cs, kp, kc, vc, L,
+    return launch_kernel(kv_prepare_f32_kernel<128>, grid, dim3(256), st, k, v, rp, kp, kc, vc, L,
                          h_kv, cap);
-  return launch_kernel(kv_prepare_f32_kernel<64>, grid, dim3(256), st, k, v, cs, kp, kc, vc, L,
+  return launch_kernel(kv_prepare_f32_kernel<64>, grid, dim3(256), st, k, v, rp, kp, kc, vc, L,
                        h_kv, cap);
 }
 
