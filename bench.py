@@ -58,14 +58,14 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
 # device copy: FETCH x 2.00, WRITE x 1.00).  Each figure is valid only for the
 # kernel source it was measured on (sha256 prefix); otherwise it reports null.
 TRAFFIC = {
-    "prefill": ("prefill_bf16.hip", "1c498196ad4dce9f", (102271.0 * 2.0 + 229376.0) * 1024),
-    "prefill_c4": ("prefill_bf16.hip", "1c498196ad4dce9f", (299274.9 * 2.0 + 524322.9) * 1024),
-    "prefill_c5": ("prefill_bf16.hip", "1c498196ad4dce9f", (677259.7 * 2.0 + 458752.0) * 1024),
-    "decode": ("decode.hip", "5d5c44530499b2f8", (1049752.1 * 2.0 + 7392.0) * 1024),
-    "prefill_chunk": ("prefill_bf16.hip", "1c498196ad4dce9f", (41487.0 * 2.0 + 57344.0) * 1024),
-    "decode_append": ("decode.hip", "5d5c44530499b2f8", (922586.2 * 2.0 + 7392.1) * 1024),
-    "decode_paged": ("decode.hip", "5d5c44530499b2f8", (1049877.6 * 2.0 + 7392.1) * 1024),
-    "qkv_epilogue": ("rope.hip", "1ca3b24e2d614795", (73829.2 * 2.0 + 147459.5) * 1024),
+    "prefill": ("prefill_bf16.hip", "1c498196ad4dce9f", (102281.5 * 2.0 + 229376.2) * 1024),
+    "prefill_c4": ("prefill_bf16.hip", "1c498196ad4dce9f", (299292.7 * 2.0 + 524327.8) * 1024),
+    "prefill_c5": ("prefill_bf16.hip", "1c498196ad4dce9f", (677014.5 * 2.0 + 458752.0) * 1024),
+    "decode": ("decode.hip", "5d5c44530499b2f8", (1049670.6 * 2.0 + 7392.1) * 1024),
+    "prefill_chunk": ("prefill_bf16.hip", "1c498196ad4dce9f", (41343.1 * 2.0 + 57344.0) * 1024),
+    "decode_append": ("decode.hip", "5d5c44530499b2f8", (922583.2 * 2.0 + 7392.0) * 1024),
+    "decode_paged": ("decode.hip", "5d5c44530499b2f8", (1049801.9 * 2.0 + 7392.0) * 1024),
+    "qkv_epilogue": ("rope.hip", "c7875c5d3665dbb8", (73822.5 * 2.0 + 147457.6) * 1024),
 }
 
 
