@@ -206,7 +206,8 @@ def test_decode_append_rejects(lib, kw, code):
 
 
 def test_chunk_workspace_sizes(lib):
-    # bf16: the one-shot layout sized for kend keys; fp32: only the cos/sin table
+    # bf16: the one-shot layout sized for kend keys; fp32: the size of a cos/sin
+    # table, a region the fp32 kernels (which form their own cos/sin) leave unused
     assert (lib.gqa_prefill_chunk_workspace_size(1, 4, 4096, 4, 128)
             == lib.gqa_prefill_workspace_size(1, 4, 4096, 4, 128))
     assert lib.gqa_prefill_chunk_workspace_size(0, 1, 1000, 2, 64) == 1000 * 32 * 8
