@@ -335,11 +335,12 @@ def to_pages(kc, page_size, num_pages, seed, poison=4096.0):
     return pool, perm.astype(np.int32)
 
 
-@pytest.mark.parametrize("dtype,page_size", [(torch.bfloat16, 16), (torch.bfloat16, 256),
-                                             (torch.float32, 64)],
-                         ids=["bf16_ps16", "bf16_ps256", "f32_ps64"])
-def test_decode_paged(dtype, page_size):
-    h_q, h_kv, d = (28, 4, 128) if dtype == torch.bfloat16 else (14, 2, 64)
+@pytest.mark.parametrize("dtype,page_size,heads",
+                         [(torch.bfloat16, 16, (28, 4, 128)), (torch.bfloat16, 256, (28, 4, 128)),
+                          (torch.bfloat16, 32, (64, 8, 128)), (torch.float32, 64, (14, 2, 64))],
+                         ids=["bf16_ps16", "bf16_ps256", "bf16_ps32_72b_heads", "f32_ps64"])
+def test_decode_paged(dtype, page_size, heads):
+    h_q, h_kv, d = heads
     kv_len = np.array([1, 1024, 1025, 3000])
     q_pos = np.array([0, 1500, 1024, 2999])
     B, cap = len(kv_len), 3072

@@ -249,7 +249,11 @@ def test_prefill_writes_cache_and_decode_continues(dtype):
                                    # chunk boundaries (2048 keys per bf16 chunk, 1024 per
                                    # fp32 chunk): exactly one chunk, one key into the next
                                    (1, 2048, 2048, 28, 4, 128), (2, 2049, 2049, 28, 4, 128),
-                                   (1, 4095, 5000, 14, 2, 64)],
+                                   (1, 4095, 5000, 14, 2, 64),
+                                   # four KV groups per workgroup (h_kv a multiple of 4)
+                                   # with two 16-head blocks per group (g = 20), and
+                                   # with g = 8 over two workgroup rows of groups
+                                   (1, 2100, 2101, 80, 4, 128), (2, 3000, 3000, 64, 8, 64)],
                          ids=lambda s: "B%d_kv%d_qpos%d_%d/%d_d%d" % s)
 def test_decode_small(dtype, shape):
     B, kv_len, q_pos, h_q, h_kv, d = shape
