@@ -71,6 +71,8 @@ TRAFFIC = {
 
 def traffic_bytes(which):
     import hashlib
+    if which not in TRAFFIC:   # no counter figure taken for this call site
+        return None
     src, digest, nbytes = TRAFFIC[which]
     path = os.path.join(ROOT, "rope_causal_grouped_amd", "csrc", src)
     with open(path, "rb") as f:
@@ -229,16 +231,31 @@ def measure_context(torch, gqa, dev):
     return res
 
 
-def measure_other_prefills(torch, gqa, dev, keys=("c1", "c4", "c5"), warmup=10, reps=20):
+# One GPU's share of the 72B prefill under 8-way tensor parallelism over KV
+# heads (each GPU owns one KV group and its 8 query heads): the 72B recipe
+# drawn at 8/1 heads.
+TP8_SHARE = ("c4", (("h_q", 8), ("h_kv", 1)))
+
+
+def measure_other_prefills(torch, gqa, dev, keys=("c1", "c4", "c5", "c4_tp8"), warmup=10,
+                           reps=20):
     """The same gqa_prefill call on the other prefill workloads, outside the
     timed step: the larger ones (72B heads at L 8192; 7B heads at L 32768
-    with boosted rows), for the scaling of the attention kernel with L, and
-    the small fp32 one (0.5B heads, L 128), whose 29.6 MFLOP make it a
-    latency figure (no roofline)."""
+    with boosted rows), for the scaling of the attention kernel with L, the
+    small fp32 one (0.5B heads, L 128), whose 29.6 MFLOP make it a latency
+    figure (no roofline), and one GPU's share of the 72B prefill at 8-way
+    tensor parallelism (B2 L8192, 8 query heads over 1 KV head)."""
+    import dataclasses
+
     from synthetic import WORKLOADS, gen_prefill
     res = {}
     for key in keys:
-        w = WORKLOADS[key]
+        if key == "c4_tp8":
+            base, over = TP8_SHARE
+            w = dataclasses.replace(WORKLOADS[base], name=WORKLOADS[base].name + "-tp8-share",
+                                    **dict(over))
+        else:
+            w = WORKLOADS[key]
         log(f"[bench] generating {w.name}")
         q, k, v = gen_prefill(w)
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32

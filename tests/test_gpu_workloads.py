@@ -1,4 +1,5 @@
-"""Whole-output parity of the five workloads at full size.
+"""Whole-output parity of the five workloads at full size, and of one GPU's
+share of the 72B prefill at 8-way tensor parallelism over KV heads.
 
 Each workload runs through the C ABI in the launch configuration the
 benchmark times (``gqa.prefill`` / ``gqa.decode`` with default arguments);
@@ -10,6 +11,7 @@ Tolerances (over the whole output): fp32 inputs max-abs <= 1e-4; bf16
 inputs (fp32 accumulation) max-abs <= 2e-2 and relative L2 <= 1e-2.
 """
 
+import dataclasses
 import time
 
 import numpy as np
@@ -49,6 +51,11 @@ def check(cmp, dtype, what, capsys):
         assert cmp.rel_l2 <= TOL_BF16_REL, f"{what}: rel-L2 {cmp.rel_l2:.3e}"
 
 
+# one GPU's share of the 72B prefill at 8-way tensor parallelism over KV
+# heads: the 72B recipe drawn at 8 query heads over 1 KV head
+OVERRIDES = {"c4_tp8": ("c4", (("h_q", 8), ("h_kv", 1)))}
+
+
 def gpu_prefill(w):
     """The benchmark's call on the workload; returns O as host float32."""
     q, k, v = gen_prefill(w)
@@ -63,13 +70,14 @@ def gpu_prefill(w):
     return out
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c4", "c5"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c4", "c5", "c4_tp8"])
 def test_prefill_workload_whole_output(key, pool, capsys):
-    w = WORKLOADS[key]
+    base, over = OVERRIDES.get(key, (key, ()))
+    w = dataclasses.replace(WORKLOADS[base], **dict(over))
     say(capsys, f"\n[{key}] {w.name}: B{w.B} L{w.L} {w.h_q}/{w.h_kv} d{w.d} {w.dtype}")
     got = gpu_prefill(w)
     assert got.shape == (w.B, w.L, w.h_q, w.d)
-    tasks = opool.prefill_tasks(key)
+    tasks = opool.prefill_tasks(base, over)
     cmp = opool.Comparison()
     seen = np.zeros((w.B, w.h_kv, w.L), bool)
     t0 = last = time.monotonic()
