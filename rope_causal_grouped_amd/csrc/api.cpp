@@ -49,8 +49,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 bool dtype_ok(int dt) { return dt == GQA_F32 || dt == GQA_BF16; }
 
 // ---- benchmark timing: HIP events bound to the dispatches of a call (its
-// first kernel's start, its main kernel's start and end, its last kernel's
-// end); see gqa::launch_kernel
+// first kernel's start, the opening and end of its main kernel's interval,
+// its last kernel's end); see gqa::launch_kernel and TimedCall
 struct Timing {
   bool on = false;
   std::vector<gqa::CallEvents> rec[2];   // 0: prefill calls, 1: decode calls
