@@ -234,6 +234,27 @@ def pin_future_invariance(orc):
     assert np.max(np.abs(o2[:, i + 1:] - o[:, i + 1:])) > 1e-3, "later rows must move"
 
 
+def pin_softmax_extreme_logits(orc):
+    """Scores far outside exp's range (|s| ~ 1e3, beyond fp64's e^709): with
+    d = 2 the only pair turns by its position in radians, so the scores are
+    set by hand.  Query 0 sees key 0 alone (score 1000; the masked key 1
+    would score 3000), so its row is V[0] exactly; query 1 scores about
+    -841 and -2524, so its weights are 1 and e^-1683 and its row is V[0]
+    too.  The softmax must subtract the row max over the visible keys only."""
+    c1, s1 = math.cos(1.0), math.sin(1.0)
+    q = np.zeros((1, 2, 1, 2))
+    q[0, 0, 0] = (1000.0, 0.0)
+    q[0, 1, 0] = (0.0, 1000.0)            # turned by 1 rad: (-1000 sin 1, 1000 cos 1)
+    k = np.zeros((1, 2, 1, 2))
+    k[0, 0, 0] = (1.0, 0.0)
+    k[0, 1, 0] = (3.0 * c1, -3.0 * s1)    # turned by 1 rad: (3, 0)
+    v = np.zeros((1, 2, 1, 2))
+    v[0, 0, 0] = (1.0, 2.0)
+    v[0, 1, 0] = (5.0, -7.0)
+    o = orc.prefill(q, k, v, scale=1.0)
+    close(o[0, :, 0], np.repeat(v[0, :1, 0], 2, axis=0), 1e-12, "extreme logits")
+
+
 def pin_shift_invariance(orc):
     """Moving every position by c leaves the prefill output unchanged."""
     rng = _rng(11)
@@ -601,7 +622,8 @@ def pin_yarn_attention_factor(orc):
 ALL_PINS = [pin_inv_freq_closed_form, pin_rope_d2_is_plane_rotation,
             pin_rope_half_split_pairing, pin_rope_norm, pin_rope_relative,
             pin_rope_group_law, pin_group_example, pin_repeat_interleave,
-            pin_sdpa, pin_brute, pin_softmax_causal, pin_future_invariance,
+            pin_sdpa, pin_brute, pin_softmax_causal, pin_softmax_extreme_logits,
+            pin_future_invariance,
             pin_shift_invariance, pin_decode_is_prefill_row, pin_prefill_rows,
             pin_prefill_group_rows,
             pin_chunked_prefill_is_prefill, pin_decode_append_is_prefill_row,

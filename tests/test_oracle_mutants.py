@@ -248,6 +248,25 @@ def m_group_rows_short_keys(mod):
     mod.prefill_group_rows = prefill_group_rows
 
 
+def m_softmax_no_max(mod):
+    """exp of the raw scores (no max subtraction): overflows for large scores."""
+    def softmax_rows(s, vis):
+        s = np.where(vis, s, -np.inf)
+        e = np.exp(s)
+        return e / np.sum(e, axis=-1, keepdims=True)
+    mod.softmax_rows = softmax_rows
+
+
+def m_softmax_max_over_masked(mod):
+    """Row max taken before masking, so a masked key's score can underflow
+    every visible weight."""
+    def softmax_rows(s, vis):
+        m = np.max(s, axis=-1, keepdims=True)
+        e = np.where(vis, np.exp(s - m), 0.0)
+        return e / np.sum(e, axis=-1, keepdims=True)
+    mod.softmax_rows = softmax_rows
+
+
 MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
            m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
@@ -256,7 +275,8 @@ MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_qkv_k_v_swapped, m_qkv_bias_dropped, m_qkv_heads_transposed,
            m_paged_row_major_page, m_paged_page_of_next_block, m_yarn_ramp_reversed,
            m_yarn_no_attention_factor, m_yarn_factor_squared, m_yarn_round_bounds,
-           m_yarn_blend_in_turns, m_group_rows_short_keys]
+           m_yarn_blend_in_turns, m_group_rows_short_keys, m_softmax_no_max,
+           m_softmax_max_over_masked]
 
 
 def failing_pins(mod):
