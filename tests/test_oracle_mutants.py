@@ -267,6 +267,69 @@ def m_softmax_max_over_masked(mod):
     mod.softmax_rows = softmax_rows
 
 
+def m_cache_v_rotated(mod):
+    """The appended V rows are rotated like K."""
+    orig = mod.cache_append
+
+    def cache_append(k_cache, v_cache, k_new, v_new, start, length=None,
+                     theta=mod.ROPE_THETA):
+        B, C = np.shape(k_new)[:2]
+        kc, vc = orig(k_cache, v_cache, k_new, v_new, start, length, theta)
+        st = mod.per_sequence(start, B)
+        nn = mod.per_sequence(C if length is None else length, B)
+        for b in range(B):
+            n = int(nn[b])
+            if n:
+                pos = mod.chunk_positions(int(st[b]), n)
+                vc[b, pos] = mod.rope(np.asarray(v_new[b, :n], np.float64), pos, theta)
+        return kc, vc
+    mod.cache_append = cache_append
+
+
+def m_qkv_bias_after_rope(mod):
+    """The QKV bias is added after the rotation instead of before it."""
+    orig = mod.qkv_epilogue
+
+    def qkv_epilogue(qkv, bias, k_cache, v_cache, h_q, h_kv, start, length=None,
+                     theta=mod.ROPE_THETA):
+        x = np.asarray(bias, np.float64)
+        q_out, kc, vc = orig(qkv, np.zeros_like(x), k_cache, v_cache, h_q, h_kv, start,
+                             length, theta)
+        d = x.shape[-1] // (h_q + 2 * h_kv)
+        (q0, q1), (k0, k1), (v0, v1) = mod.qkv_sections(h_q, h_kv, d)
+        q_out = q_out + x[q0:q1].reshape(h_q, d)
+        B, C = np.shape(qkv)[:2]
+        st = mod.per_sequence(start, B)
+        nn = mod.per_sequence(C if length is None else length, B)
+        for b in range(B):
+            n = int(nn[b])
+            if n:
+                pos = mod.chunk_positions(int(st[b]), n)
+                kc[b, pos] += x[k0:k1].reshape(h_kv, d)
+                vc[b, pos] += x[v0:v1].reshape(h_kv, d)
+        return q_out, kc, vc
+    mod.qkv_epilogue = qkv_epilogue
+
+
+def m_cached_query_misses_own_key(mod):
+    """Queries against the cache see keys strictly before their position
+    (position 0 keeps its own key, so no row is empty)."""
+    orig, orig_vis = mod.attend_cached, mod.visible
+
+    def strict(qp, kp):
+        kp, qp = np.asarray(kp)[None, :], np.asarray(qp)[:, None]
+        return (kp < qp) | ((kp == 0) & (qp == 0))
+
+    def attend_cached(q, q_pos, k_cache, v_cache, kv_len, theta=mod.ROPE_THETA, scale=None,
+                      q_rotated=False):
+        mod.visible = strict
+        try:
+            return orig(q, q_pos, k_cache, v_cache, kv_len, theta, scale, q_rotated)
+        finally:
+            mod.visible = orig_vis
+    mod.attend_cached = attend_cached
+
+
 MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_rope_clockwise, m_rope_dropped_term, m_freq_no_factor_two,
            m_theta_1e4, m_mask_strict, m_mask_transposed, m_no_scale,
@@ -276,7 +339,8 @@ MUTANTS = [m_group_tiled, m_group_off_by_one, m_rope_interleaved,
            m_paged_row_major_page, m_paged_page_of_next_block, m_yarn_ramp_reversed,
            m_yarn_no_attention_factor, m_yarn_factor_squared, m_yarn_round_bounds,
            m_yarn_blend_in_turns, m_group_rows_short_keys, m_softmax_no_max,
-           m_softmax_max_over_masked]
+           m_softmax_max_over_masked, m_cache_v_rotated, m_qkv_bias_after_rope,
+           m_cached_query_misses_own_key]
 
 
 def failing_pins(mod):
