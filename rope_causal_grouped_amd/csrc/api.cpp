@@ -190,7 +190,7 @@ int64_t prefill_lpad(int64_t L) { return (L + gqa::kPrefillTileK - 1) / gqa::kPr
 
 // workspace pieces of gqa_prefill
 struct PrefillWs {
-  size_t cs_off, kp_off, vt_off, kmax_off, kexp_off, total;
+  size_t cs_off, kp_off, vt_off, kmax_off, kexp_off, ctr_off, total;
 };
 
 PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
@@ -204,12 +204,14 @@ PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
     const size_t tiles = align256((size_t)B * h_kv * (prefill_lpad(L) / gqa::kPrefillTileK) * 4);
     w.kmax_off = cs + 2 * kp;
     w.kexp_off = w.kmax_off + tiles;
-    w.total = w.kexp_off + tiles;
+    w.ctr_off = w.kexp_off + tiles;     // the attention kernel's ticket counter
+    w.total = w.ctr_off + 256;
   } else {
     const size_t kp = align256((size_t)B * h_kv * L * d * 4);
     w.vt_off = cs + kp;
     w.kmax_off = cs + kp;
     w.kexp_off = cs + kp;
+    w.ctr_off = cs + kp;
     w.total = cs + kp;
   }
   return w;
@@ -317,14 +319,15 @@ int gqa_prefill(const void* q, const void* k, const void* v, void* o, int in_dty
     float* kmax = (float*)(wsb + ws.kmax_off);
     int* kexp = (int*)(wsb + ws.kexp_off);
     tc.bind(te.call_start, te.kernel_start);
+    int* ctr = (int*)(wsb + ws.ctr_off);
     e = gqa::launch_kv_prepare_bf16((const uint16_t*)k, (const uint16_t*)v, &rp, cs, kp, vt,
                                     kmax, kexp, (uint16_t*)k_cache, (uint16_t*)v_cache, B, L, Lpad,
-                                    h_kv, d, cap, L, nullptr, nullptr, L, st);
+                                    h_kv, d, cap, L, nullptr, nullptr, L, ctr, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     tc.bind(nullptr, te.kernel_stop);
     e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, kexp, cs, o,
                                  out_dtype == GQA_BF16, B, L, Lpad, h_q, h_kv, d, scale, causal,
-                                 nullptr, nullptr, L, st);
+                                 nullptr, nullptr, L, ctr, st);
   } else {         // fp32: the kernels form their cos/sin themselves
     const gqa::KvStrides vsd{L * h_kv * d, d, (int64_t)h_kv * d};       // [B, L, h_kv, d]
     if (k_cache) {   // rotated K and V into the cache; attention reads the rotated copy
@@ -521,15 +524,16 @@ int gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, int 
     float* kmax = (float*)(wsb + ws.kmax_off);
     int* kexp = (int*)(wsb + ws.kexp_off);
     tc.bind(nullptr, te.kernel_start);
+    int* ctr = (int*)(wsb + ws.ctr_off);
     e = gqa::launch_kv_prepare_bf16((const uint16_t*)k_cache, (const uint16_t*)v_cache, nullptr,
                                     nullptr, kp, vt, kmax, kexp, nullptr, nullptr, B, C, Lpad, h_kv,
-                                    d, cap, cap, start, len, kend, st);
+                                    d, cap, cap, start, len, kend, ctr, st);
     if (e != hipSuccess) return hip_fail(e, "K/V preparation launch");
     // 3) the chunk's queries against them
     tc.bind(nullptr, te.kernel_stop);
     e = gqa::launch_prefill_bf16((const uint16_t*)q, kp, vt, kmax, kexp, q_rotated ? nullptr : cs, o,
                                  out_dtype == GQA_BF16, B, C, Lpad, h_q, h_kv, d, scale, 1, start,
-                                 len, kend, st);
+                                 len, kend, ctr, st);
   } else {
     // 2) the chunk's queries against the cache itself
     const gqa::KvStrides csd{cap * h_kv * d, d, (int64_t)h_kv * d};   // [B, cap, h_kv, d]

@@ -71,7 +71,7 @@ hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const Ro
                                   uint16_t* kc, uint16_t* vc, int64_t B, int64_t L, int64_t Lpad,
                                   int h_kv, int d, int64_t cap, int64_t src_rows,
                                   const int64_t* kstart, const int64_t* klen, int64_t kend,
-                                  hipStream_t st);
+                                  int* pool_ctr, hipStream_t st);
 
 hipError_t launch_kv_prepare_f32(const float* k, const float* v, RopeParams rp, float* kp,
                                  float* kc, float* vc, int64_t B, int64_t L, int h_kv, int d,
@@ -90,12 +90,15 @@ hipError_t launch_qkv_epilogue(const void* x, const void* bias, void* q_out, voi
                                int64_t C, int h_q, int h_kv, int d, int64_t cap, int64_t end,
                                RopeParams rp, hipStream_t st);
 
+// pool_ctr (nullable): a workspace int, zeroed by the preparation kernel
+// launched before this one, for the ticket of the shared tail of the work
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
                                const float* kmax, const int* kexp, const float2* cs, void* o,
                                int out_bf16,
                                int64_t B, int64_t L, int64_t Lpad, int h_q, int h_kv, int d,
                                float scale, int causal, const int64_t* qstart,
-                               const int64_t* qlen, int64_t kend, hipStream_t st);
+                               const int64_t* qlen, int64_t kend, int* pool_ctr,
+                               hipStream_t st);
 
 // element strides of a K or V operand: sequence b, group u, key j start at
 // base + b * batch + u * head + j * row

@@ -67,6 +67,7 @@
 // loop no longer reads, so O does not sit in the caches as partly written
 // dirty lines that the next kernels would have to write back.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int* __restrict__ kexp, const float2* __restrict__ cs, void* __restrict__ o, int L,
     int Lpad, int h_q, int h_kv,
     int g, int n_rb, int n_bu, float sl2, int causal, const int64_t* __restrict__ qstart,
-    const int64_t* __restrict__ qlen, int kend) {
+    const int64_t* __restrict__ qlen, int kend, int* __restrict__ pool_ctr, int pool_t) {
   constexpr int NS = D / 16;                  // 16-dim k-steps of S^T
   constexpr int NDB = D / 32;                 // 32-dim blocks of O^T
   constexpr int NPV = 4 * NDB;                // P.V MFMAs per tile
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ks0[TK * D], ks1[TK * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs0[TK * D], vs1[TK * D];
   __shared__ float wred[NW];
-  __shared__ int wexp[NW];
+  __shared__ int wexp[NW + 1];               // [NW]: the shared-tail ticket
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,10 +152,33 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // the same share of the work on every XCD (causal row blocks differ in
   // cost), and within a part the heaviest row blocks (latest positions,
   // most keys) first.  Ids past an XCD's items exit at once.
-  const int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+  //
+  // Shared tail (pool_t > 0): the last pool_t items of every XCD's list
+  // (its lightest) form one pool of 8 * pool_t items, taken in order
+  // through a device-scope ticket by the workgroups with ids from an XCD's
+  // own item count - pool_t on (each XCD also has pool_t extra ids, which
+  // exit once the pool is empty).  The XCDs do not all run at the same
+  // speed, so with a fixed split the faster ones would idle at the end;
+  // this way they take more of the pool.  The counter is zeroed by the
+  // preparation kernel that runs before this one.
+  int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
   const int low = n_bu & -n_bu;               // largest power of two dividing n_bu
   const int s_parts = low >= kXcds ? 1 : kXcds / low;
   const int ppx = n_bu * s_parts / kXcds;     // parts per XCD
+  auto xcd_items = [&](int x) {
+    int c = 0;
+    for (int t = 0; t < ppx; ++t) c += (n_rb - (x * ppx + t) % s_parts + s_parts - 1) / s_parts;
+    return c;
+  };
+  if (pool_t > 0 && j >= xcd_items(xcd) - pool_t) {
+    if (tid == 0)
+      wexp[NW] = __hip_atomic_fetch_add(pool_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = wexp[NW];
+    if (t >= kXcds * pool_t) return;          // pool empty
+    xcd = t % kXcds;
+    j = xcd_items(xcd) - pool_t + t / kXcds;
+  }
   int part = xcd * ppx, jj = j;
   for (int t = 0; t < ppx; ++t) {
     const int cnt = (n_rb - part % s_parts + s_parts - 1) / s_parts;
@@ -671,7 +695,8 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
                                int out_bf16,
                                int64_t B, int64_t L, int64_t Lpad, int h_q, int h_kv, int d,
                                float scale, int causal, const int64_t* qstart,
-                               const int64_t* qlen, int64_t kend, hipStream_t st) {
+                               const int64_t* qlen, int64_t kend, int* pool_ctr,
+                               hipStream_t st) {
   const int g = h_q / h_kv;
   const int n_rb = (int)((L * g + kPrefillRowsWG - 1) / kPrefillRowsWG);
   const int n_bu = (int)(B * h_kv);
@@ -680,12 +705,20 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   const int low = n_bu & -n_bu;
   const int s_parts = low >= kXcds ? 1 : kXcds / low;
   const int ppx = n_bu * s_parts / kXcds;
-  const unsigned grid = (unsigned)((int64_t)kXcds * ppx * ((n_rb + s_parts - 1) / s_parts));
+  // shared tail: a quarter of the smallest XCD share, at most 64 items per
+  // XCD, and as many extra ids per XCD (56 / 64 / 64 items per XCD at 7B
+  // L4096 / 72B L8192 / 7B L32768; measured against 28-32 and 224: the
+  // small pools leave most of the tail at the longer shapes, the large one
+  // loses it again to the tickets and to the extra ids that exit)
+  const int min_items = ppx * (n_rb / s_parts);
+  const int pool_t = pool_ctr ? std::min(64, min_items / 4) : 0;
+  const unsigned grid =
+      (unsigned)((int64_t)kXcds * (ppx * ((n_rb + s_parts - 1) / s_parts) + pool_t));
   hipError_t e;
 #define GQA_LAUNCH(DD, OB, PR)                                                               \
   e = launch_kernel(prefill_bf16_kernel<DD, OB, PR>, dim3(grid), dim3(NW * 64), st, q, kp, vt, \
                     kmax, kexp, cs, o, (int)L, (int)Lpad, h_q, h_kv, g, n_rb, n_bu, sl2,       \
-                    causal, qstart, qlen, (int)kend)
+                    causal, qstart, qlen, (int)kend, pool_ctr, pool_t)
 #define GQA_LAUNCH_D(DD, OB) \
   do { if (cs) GQA_LAUNCH(DD, OB, true); else GQA_LAUNCH(DD, OB, false); } while (0)
   if (d == 128) {

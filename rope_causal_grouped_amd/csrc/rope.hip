@@ -127,7 +127,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     float2* __restrict__ cs_out, uint16_t* __restrict__ kp, uint16_t* __restrict__ vt,
     float* __restrict__ kmax, int* __restrict__ kexp, uint16_t* __restrict__ kc,
     uint16_t* __restrict__ vc, int64_t L, int64_t Lpad, int h_kv, int64_t cap, int64_t src_rows,
-    const int64_t* __restrict__ kstart, const int64_t* __restrict__ klen, int64_t kend) {
+    const int64_t* __restrict__ kstart, const int64_t* __restrict__ klen, int64_t kend,
+    int* __restrict__ pool_ctr) {
   constexpr int TK = 64;
   constexpr int HALF = D / 2;
   constexpr int PP = HALF / 4;        // RoPE pairs per thread: 4 threads per key row
@@ -144,6 +145,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     if (tid < HALF) om[tid] = rope_omega(tid, D, rp);
     __syncthreads();
   }
+  // the attention kernel's ticket counter for its shared tail starts at 0
+  if (pool_ctr && tile == 0 && u == 0 && b == 0 && tid == 0)
+    __hip_atomic_store(pool_ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (kstart) {   // keys of sequence b: rows 0 .. kstart[b] + klen[b] - 1 of the source
     const int64_t s0 = kstart[b], n = klen ? klen[b] : L;
     L = (s0 >= 0 && n >= 0 && n <= L && s0 + n <= kend) ? s0 + n : 0;
@@ -339,7 +343,7 @@ hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const Ro
                                   int* kexp, uint16_t* kc, uint16_t* vc, int64_t B, int64_t L,
                                   int64_t Lpad, int h_kv, int d, int64_t cap, int64_t src_rows,
                                   const int64_t* kstart, const int64_t* klen, int64_t kend,
-                                  hipStream_t st) {
+                                  int* pool_ctr, hipStream_t st) {
   if (cs_out && !rope) return hipErrorInvalidValue;
   const int rotate = rope != nullptr;
   const RopeParams rp = rope ? *rope : RopeParams{};
@@ -347,10 +351,10 @@ hipError_t launch_kv_prepare_bf16(const uint16_t* k, const uint16_t* v, const Ro
   if (d == 128)
     return launch_kernel(kv_prepare_bf16_kernel<128>, grid, dim3(256), st, k, v, rotate, rp,
                          cs_out, kp, vt, kmax, kexp, kc, vc, L, Lpad, h_kv, cap, src_rows, kstart,
-                         klen, kend);
+                         klen, kend, pool_ctr);
   return launch_kernel(kv_prepare_bf16_kernel<64>, grid, dim3(256), st, k, v, rotate, rp, cs_out,
                        kp, vt, kmax, kexp, kc, vc, L, Lpad, h_kv, cap, src_rows, kstart, klen,
-                       kend);
+                       kend, pool_ctr);
 }
 
 // ---------------------------------------------------------------------------

@@ -131,6 +131,41 @@ def test_prefill_bf16_small(shape):
     assert_parity(host(o), oracle.prefill(q, k, v), torch.bfloat16, f"prefill bf16 {shape}")
 
 
+@pytest.mark.parametrize("shape", [(2, 2048, 28, 4, 128), (1, 3000, 16, 2, 64)],
+                         ids=lambda s: "B%d_L%d_%d/%d_d%d" % s)
+def test_prefill_shared_tail_repeated_calls(shape):
+    """Shapes whose work lists have a shared tail (items taken through a
+    ticket counter in the workspace): three calls in a row on one workspace,
+    the output poisoned with NaN before each, give the same bits every time
+    (the counter starts over each call and every item is done exactly
+    once), and sampled rows match the oracle -- the last rows of each group
+    among them, which sit in the tail."""
+    B, L, h_q, h_kv, d = shape
+    note(f"prefill shared tail {shape}")
+    q, k, v = small_case(B, L, h_q, h_kv, d, torch.bfloat16, 77 + L)
+    qd, kd, vd = (dev(x, torch.bfloat16) for x in (q, k, v))
+    ws = torch.empty(gqa.prefill_workspace_size(torch.bfloat16, B, L, h_kv, d), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((B, L, h_q, d), dtype=torch.float32, device="cuda")
+    outs = []
+    for _ in range(3):
+        o.fill_(float("nan"))
+        gqa.prefill(qd, kd, vd, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(o.clone())
+    assert not torch.isnan(outs[0]).any(), "rows left unwritten"
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    rng = np.random.default_rng(5)
+    rows = [(b, i, t) for b in range(B) for i in (0, 1, L // 2, L - 2, L - 1)
+            for t in (0, h_q - 1)]
+    rows += [(int(rng.integers(B)), int(rng.integers(L)), int(rng.integers(h_q)))
+             for _ in range(24)]
+    got = host(outs[0])
+    want = oracle.prefill_rows(q, k, v, rows)
+    assert_parity(np.stack([got[b, i, t] for b, i, t in rows]), want, torch.bfloat16,
+                  f"shared tail {shape}")
+
+
 @pytest.mark.parametrize("sigma,boosted", [(3.0, 0), (0.5, 12)], ids=["sigma3", "boosted"])
 @pytest.mark.parametrize("shape", [(1, 333, 28, 4, 128), (2, 300, 14, 2, 64)],
                          ids=lambda s: "B%d_L%d_%d/%d_d%d" % s)
