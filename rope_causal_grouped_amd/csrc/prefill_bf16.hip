@@ -710,8 +710,11 @@ hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint
   // L4096 / 72B L8192 / 7B L32768; measured against 28-32 and 224: the
   // small pools leave most of the tail at the longer shapes, the large one
   // loses it again to the tickets and to the extra ids that exit)
+  // Only a causal whole prompt gets one: its row blocks range from one tile
+  // to all of them, while a chunk's (or a full mask's) are alike, and
+  // moving those off their XCD's L2 cost 4% on the 7B chunk.
   const int min_items = ppx * (n_rb / s_parts);
-  const int pool_t = pool_ctr ? std::min(64, min_items / 4) : 0;
+  const int pool_t = pool_ctr && causal && !qstart ? std::min(64, min_items / 4) : 0;
   const unsigned grid =
       (unsigned)((int64_t)kXcds * (ppx * ((n_rb + s_parts - 1) / s_parts) + pool_t));
   hipError_t e;
