@@ -204,8 +204,8 @@ PrefillWs prefill_ws(int in_dtype, int64_t B, int64_t L, int h_kv, int d) {
     const size_t tiles = align256((size_t)B * h_kv * (prefill_lpad(L) / gqa::kPrefillTileK) * 4);
     w.kmax_off = cs + 2 * kp;
     w.kexp_off = w.kmax_off + tiles;
-    w.ctr_off = w.kexp_off + tiles;     // the attention kernel's ticket counter
-    w.total = w.ctr_off + 256;
+    w.ctr_off = w.kexp_off + tiles;     // the attention kernel's ticket counters
+    w.total = w.ctr_off + align256(gqa::kPrefillPoolXcds * gqa::kPrefillPoolStride * sizeof(int));
   } else {
     const size_t kp = align256((size_t)B * h_kv * L * d * 4);
     w.vt_off = cs + kp;

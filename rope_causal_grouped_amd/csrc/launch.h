@@ -55,6 +55,8 @@ hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st,
 constexpr int kPrefillTileK = 64;      // key padding granule of the prepared K/V
 constexpr int kPrefillTileV = 32;      // keys per attention tile; V^T is stored per such tile
 constexpr int kPrefillRowsWG = 256;    // stacked (position, head) rows per workgroup
+constexpr int kPrefillPoolXcds = 8;    // per-XCD shared-tail counters of the attention kernel
+constexpr int kPrefillPoolStride = 16; // ints between them (one 64-byte line each)
 constexpr int kDecodeChunk = 1024;     // keys per decode split (fp32 cache)
 constexpr int kDecodeChunkBf16 = 2048; // keys per decode split (bf16 cache)
 constexpr int kDecodeMaxSplits = 8192;  // bound on the chunks of one sequence (8M keys)
@@ -90,8 +92,9 @@ hipError_t launch_qkv_epilogue(const void* x, const void* bias, void* q_out, voi
                                int64_t C, int h_q, int h_kv, int d, int64_t cap, int64_t end,
                                RopeParams rp, hipStream_t st);
 
-// pool_ctr (nullable): a workspace int, zeroed by the preparation kernel
-// launched before this one, for the ticket of the shared tail of the work
+// pool_ctr (nullable): kPrefillPoolXcds workspace ints kPrefillPoolStride
+// apart, zeroed by the preparation kernel launched before this one, for the
+// tickets of the shared tail of the work
 hipError_t launch_prefill_bf16(const uint16_t* q, const uint16_t* kp, const uint16_t* vt,
                                const float* kmax, const int* kexp, const float2* cs, void* o,
                                int out_bf16,

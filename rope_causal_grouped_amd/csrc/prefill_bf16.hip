@@ -83,6 +83,8 @@ constexpr int NW = 8;                       // waves per workgroup
 constexpr int RW = 32;                      // rows per wave
 constexpr int PF = 4;                       // LDS operand reads kept ahead of the MFMAs
 constexpr int kXcds = 8;                    // XCDs (each with its own L2) per MI355X
+constexpr int kPoolStride = kPrefillPoolStride;   // ints between the per-XCD tail counters
+static_assert(kPrefillPoolXcds == kXcds, "one shared-tail counter per XCD");
 constexpr float kRescaleThreshold = 8.0f;   // log2 units, max-first path
 constexpr float kBoundHeadroom = 64.0f;     // log2 units, bound-first path
 constexpr float kSumCap = 4294967296.0f;    // 2^32
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t ks0[TK * D], ks1[TK * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs0[TK * D], vs1[TK * D];
   __shared__ float wred[NW];
-  __shared__ int wexp[NW + 1];               // [NW]: the shared-tail ticket
+  __shared__ int wexp[NW + 2];               // [NW], [NW + 1]: the shared-tail pick
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,13 +156,18 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // most keys) first.  Ids past an XCD's items exit at once.
   //
   // Shared tail (pool_t > 0): the last pool_t items of every XCD's list
-  // (its lightest) form one pool of 8 * pool_t items, taken in order
-  // through a device-scope ticket by the workgroups with ids from an XCD's
-  // own item count - pool_t on (each XCD also has pool_t extra ids, which
-  // exit once the pool is empty).  The XCDs do not all run at the same
-  // speed, so with a fixed split the faster ones would idle at the end;
-  // this way they take more of the pool.  The counter is zeroed by the
-  // preparation kernel that runs before this one.
+  // (its lightest) become that XCD's pool, handed out through a
+  // device-scope ticket counter per XCD to the workgroups with ids from the
+  // XCD's own item count - pool_t on (each XCD also has pool_t extra ids).
+  // Such a workgroup takes the next item of its own XCD's pool; once that
+  // is empty it takes one from the pool with the most items left (read all
+  // counters, then a ticket there; a few bounded retries if another
+  // workgroup got there first), and it exits when every pool is empty.  The
+  // XCDs do not all run at the same speed, so with a fixed split the faster
+  // ones would idle at the end; this way they take over part of the slower
+  // ones' tails, and most items still run where their K/V sit in L2.  The
+  // counters (kPoolStride ints apart) are zeroed by the preparation kernel
+  // that runs before this one.
   int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
   const int low = n_bu & -n_bu;               // largest power of two dividing n_bu
   const int s_parts = low >= kXcds ? 1 : kXcds / low;
@@ -171,13 +178,43 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     return c;
   };
   if (pool_t > 0 && j >= xcd_items(xcd) - pool_t) {
-    if (tid == 0)
-      wexp[NW] = __hip_atomic_fetch_add(pool_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      int sel = -1, tk = 0;
+      int t = __hip_atomic_fetch_add(pool_ctr + xcd * kPoolStride, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+      if (t < pool_t) {
+        sel = xcd;
+        tk = t;
+      }
+      for (int tries = 0; sel < 0 && tries < kXcds; ++tries) {
+        int best = -1, left = 0;
+        int cnt[kXcds];
+#pragma unroll
+        for (int y = 0; y < kXcds; ++y)
+          cnt[y] = __hip_atomic_load(pool_ctr + y * kPoolStride, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int y = 0; y < kXcds; ++y)
+          if (pool_t - cnt[y] > left) {
+            left = pool_t - cnt[y];
+            best = y;
+          }
+        if (best < 0) break;                    // every pool is empty
+        t = __hip_atomic_fetch_add(pool_ctr + best * kPoolStride, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (t < pool_t) {
+          sel = best;
+          tk = t;
+        }
+      }
+      wexp[NW] = sel;
+      wexp[NW + 1] = tk;
+    }
     __syncthreads();
-    const int t = wexp[NW];
-    if (t >= kXcds * pool_t) return;          // pool empty
-    xcd = t % kXcds;
-    j = xcd_items(xcd) - pool_t + t / kXcds;
+    const int sel = wexp[NW];
+    if (sel < 0) return;                        // no item left
+    xcd = sel;
+    j = xcd_items(sel) - pool_t + wexp[NW + 1];
   }
   int part = xcd * ppx, jj = j;
   for (int t = 0; t < ppx; ++t) {

@@ -145,9 +145,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     if (tid < HALF) om[tid] = rope_omega(tid, D, rp);
     __syncthreads();
   }
-  // the attention kernel's ticket counter for its shared tail starts at 0
-  if (pool_ctr && tile == 0 && u == 0 && b == 0 && tid == 0)
-    __hip_atomic_store(pool_ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the attention kernel's ticket counters for its shared tail start at 0
+  if (pool_ctr && tile == 0 && u == 0 && b == 0 && tid < kPrefillPoolXcds)
+    __hip_atomic_store(pool_ctr + tid * kPrefillPoolStride, 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   if (kstart) {   // keys of sequence b: rows 0 .. kstart[b] + klen[b] - 1 of the source
     const int64_t s0 = kstart[b], n = klen ? klen[b] : L;
     L = (s0 >= 0 && n >= 0 && n <= L && s0 + n <= kend) ? s0 + n : 0;

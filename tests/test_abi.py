@@ -116,10 +116,10 @@ def test_rope_rejects(lib):
 
 def test_workspace_sizes(lib):
     # bf16 prefill: cos/sin table + rotated K + transposed V (64-key padded)
-    # + the largest K row norm and the fp16 exponent per 64-key tile + 256
-    # bytes for the attention kernel's work-ticket counter
+    # + the largest K row norm and the fp16 exponent per 64-key tile + 512
+    # bytes for the attention kernel's work-ticket counters (8, 64 bytes apart)
     n = lib.gqa_prefill_workspace_size(1, 4, 4096, 4, 128)
-    assert n == 4096 * 64 * 8 + 2 * 4 * 4 * 4096 * 128 * 2 + 2 * 4 * 4 * 64 * 4 + 256
+    assert n == 4096 * 64 * 8 + 2 * 4 * 4 * 4096 * 128 * 2 + 2 * 4 * 4 * 64 * 4 + 512
     assert lib.gqa_prefill_workspace_size(1, 0, 10, 4, 128) == 0
     # decode: (m, l, o[d]) per (b, group, 1024-key chunk, head) and the
     # rotated queries of an appending step (fp32-sized)
