@@ -58,11 +58,11 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
 # device copy: FETCH x 2.00, WRITE x 1.00).  Each figure is valid only for the
 # kernel source it was measured on (sha256 prefix); otherwise it reports null.
 TRAFFIC = {
-    "prefill": ("prefill_bf16.hip", "e9da43b9798be525", (102977.3 * 2.0 + 229406.9) * 1024),
-    "prefill_c4": ("prefill_bf16.hip", "e9da43b9798be525", (302314.0 * 2.0 + 524338.1) * 1024),
-    "prefill_c5": ("prefill_bf16.hip", "e9da43b9798be525", (691369.8 * 2.0 + 458790.5) * 1024),
+    "prefill": ("prefill_bf16.hip", "d2bffe1f423a3633", (102977.3 * 2.0 + 229406.9) * 1024),
+    "prefill_c4": ("prefill_bf16.hip", "d2bffe1f423a3633", (302314.0 * 2.0 + 524338.1) * 1024),
+    "prefill_c5": ("prefill_bf16.hip", "d2bffe1f423a3633", (691369.8 * 2.0 + 458790.5) * 1024),
     "decode": ("decode.hip", "5d5c44530499b2f8", (1049670.9 * 2.0 + 7392.1) * 1024),
-    "prefill_chunk": ("prefill_bf16.hip", "e9da43b9798be525", (41377.9 * 2.0 + 57344.0) * 1024),
+    "prefill_chunk": ("prefill_bf16.hip", "d2bffe1f423a3633", (41377.9 * 2.0 + 57344.0) * 1024),
     "decode_append": ("decode.hip", "5d5c44530499b2f8", (922583.2 * 2.0 + 7392.0) * 1024),
     "decode_paged": ("decode.hip", "5d5c44530499b2f8", (1049802.1 * 2.0 + 7392.0) * 1024),
     "qkv_epilogue": ("rope.hip", "b4d77aead74c0c45", (73825.9 * 2.0 + 147472.8) * 1024),

@@ -14,7 +14,10 @@
 // workgroup owns 256 consecutive stacked rows (about 256/g positions, all g
 // heads) and streams the K/V tiles of group u through LDS once for all of
 // them: the g-fold K/V reuse GQA offers (same page, closing note of §4.1.3).
-// Eight waves own 32 rows each, two waves per SIMD.
+// Eight waves own 32 rows each, two waves per SIMD.  Which row block a
+// workgroup takes follows an XCD-aware order (each XCD works through a few
+// groups, heaviest row blocks first) whose lightest items form per-XCD
+// pools that faster XCDs may take over (see the work-item comment below).
 //
 // Per 64-key tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_f16
 // (K from LDS as the A operand, the wave's rotated Q rows resident in VGPRs
