@@ -24,7 +24,11 @@
  * Ownership: every pointer is device memory owned by the caller (16-byte
  * aligned).  The library never allocates, frees or synchronises; it only
  * enqueues kernels on `stream` (a hipStream_t, or NULL for the default
- * stream).  Scratch space is the caller's `workspace`.
+ * stream).  Scratch space is the caller's `workspace`.  A workspace serves
+ * one call at a time: the call overwrites it (rotated K, transposed V,
+ * per-tile norms, work counters, chunk states), so calls that can run at the
+ * same time (on different streams) need workspaces of their own; calls
+ * ordered on one stream may share one.
  *
  * Errors: arguments are validated on the host before anything is enqueued;
  * on failure nothing is launched, a negative status is returned and
