@@ -99,3 +99,37 @@ def test_noalloc_rejects_a_step_past_the_scratch():
         gqa.decode_noalloc(q, kc, kc, kv_len=cap, q_pos=cap, out=out)
     torch.cuda.synchronize()
     assert int(out.count_nonzero()) == 0
+
+
+def test_noalloc_decode_replays_from_a_captured_graph():
+    """The allocation-free decode inside a captured HIP graph, the kind of
+    caller it is for.  One eager call first (it looks up the static scratch's
+    device address, which is not done under capture); then the call is
+    captured once and replayed three times, with new query values written
+    eagerly and a synchronisation between replays.  Every replay must equal
+    the eager gqa_decode (caller's workspace) on the same inputs, bit for
+    bit."""
+    B, cap, h_q, h_kv, d = 4, 4096, 28, 4, 128
+    kv_len, q_pos = 3000, 3100                # two 2048-key chunks, the second partial
+    note(f"noalloc decode under graph capture: B{B} kv {kv_len} {h_q}/{h_kv} d{d} bf16")
+    gen = torch.Generator(device="cuda").manual_seed(29)
+    q = torch.randn((B, h_q, d), device="cuda", generator=gen).to(torch.bfloat16)
+    kc = torch.randn((B, cap, h_kv, d), device="cuda", generator=gen).to(torch.bfloat16)
+    vc = torch.randn((B, cap, h_kv, d), device="cuda", generator=gen).to(torch.bfloat16)
+    out = torch.empty((B, h_q, d), dtype=torch.float32, device="cuda")
+    gqa.decode_noalloc(q, kc, vc, kv_len=kv_len, q_pos=q_pos, out=out)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gqa.decode_noalloc(q, kc, vc, kv_len=kv_len, q_pos=q_pos, out=out)
+    torch.cuda.synchronize()
+    for r in range(3):
+        q.copy_(torch.randn((B, h_q, d), device="cuda", generator=gen).to(torch.bfloat16))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = gqa.decode(q, kc, vc, kv_len=kv_len, q_pos=q_pos)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), f"replay {r}"
+        assert torch.equal(out, want), f"replay {r}"
