@@ -137,7 +137,10 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
  * nothing.  All calls on one GPU share its scratch: two calls whose work
  * overlaps on the device (on different streams, or from several threads on
  * one device without ordering) race and give wrong results; calls ordered
- * on one stream are safe.  Outputs equal gqa_decode's bit for bit.
+ * on one stream are safe.  Outputs equal gqa_decode's bit for bit.  The
+ * call only launches kernels, so it can be captured into a HIP graph; its
+ * first call on a device looks up the scratch's device address, so make
+ * that call before any capture on that device.
  */
 #define GQA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
 int gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
